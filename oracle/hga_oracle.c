@@ -1,0 +1,376 @@
+/*
+ * hga_oracle.c -- plain CPU oracle for the hot path of Hierarchical Global
+ * Attention (HGA): chunk summaries -> per-block top-k chunk routing -> exact
+ * softmax attention over the routed chunks plus the causal local block, and
+ * the gradient of that attention for the active segment.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, obviously correct
+ * definition that the GPU library is checked against. Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg load it; the product path
+ * never does, and this file shares no code with it.
+ *
+ * Source: arXiv 2607.15105, "Long-Context Fine-Tuning with Limited VRAM"
+ * (gist.science technical summary, section 2.1 "Hierarchical Global
+ * Attention", section 2.2 "segment-wise backward"; author abstract).
+ *
+ * Precision: inputs are float32 arrays (bf16 workloads pass the widened bf16
+ * values); every sum, dot product and exponential is taken in double, in
+ * plain ascending index order. Outputs are double.
+ *
+ * Readings of points the pages leave open (each is listed with its reason in
+ * the design notes of this repository):
+ *   - summary of a chunk = arithmetic mean of its C key vectors (keys only);
+ *   - the query block scores with the mean of its queries over all query
+ *     heads that share one key/value head (routing per block and kv head);
+ *   - score = plain dot product, ranking by (score desc, chunk id asc);
+ *   - candidates = every closed chunk that ends at or before the block's
+ *     first query position; fewer than k candidates -> take all, pad with -1;
+ *   - local window = the query block itself under the causal mask;
+ *   - no sink tokens and no 8-token group level (whole chunks are attended);
+ *   - softmax scale = 1/sqrt(D) unless given; lse is the natural log;
+ *   - gradients flow only into the active segment's keys/values (history is
+ *     detached) and never through the routing decision.
+ *
+ * Parallelism: OpenMP over independent output rows only; the arithmetic of
+ * each output element is the same sequential loop whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ threads */
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- summarize
+ * Chunk summary (technical summary 2.1, chunk selection: one compact summary
+ * vector per closed fixed-size chunk, kept resident):
+ *     S[g][c][d] = (1/C) * sum_{t = cC}^{cC + C - 1} K[g][t][d]
+ * K is [Hkv][T][D]; S is [Hkv][n_cap][D]; rows c_begin .. c_end-1 are written.
+ */
+void oracle_summarize(const float *K, int64_t Hkv, int64_t T, int64_t D,
+                      int64_t C, int64_t c_begin, int64_t c_end,
+                      double *S, int64_t n_cap)
+{
+    (void)T;
+    int64_t n_rows = Hkv * (c_end - c_begin);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t g = r / (c_end - c_begin);
+        int64_t c = c_begin + r % (c_end - c_begin);
+        for (int64_t d = 0; d < D; ++d) {
+            double sum = 0.0;
+            for (int64_t t = c * C; t < c * C + C; ++t)
+                sum += (double)K[(g * T + t) * D + d];
+            S[(g * n_cap + c) * D + d] = sum / (double)C;
+        }
+    }
+}
+
+/* -------------------------------------------------------------------- route
+ * Chunk routing (technical summary 2.1: the current query block scores the
+ * resident summaries and keeps the most relevant historical chunks; the
+ * selection carries no gradient).
+ *
+ * For kv head g and query block b (first query at absolute position
+ * P = p0 + b*Bq):
+ *     qbar[d]  = mean over the G query heads h of group g and the Bq queries i
+ *                of block b of Q[h][i][d]
+ *     E        = { c : (c + 1) * C <= P }           closed, causally earlier
+ *     sigma_c  = sum_d qbar[d] * S[g][c][d]
+ *     keep the first min(k, |E|) chunks of E ordered by (sigma desc, c asc),
+ *     write them in ascending id order, pad with -1.
+ * ids is [Hkv][n_blocks][k]. If sigma_out is not NULL it receives
+ * sigma_c for every c < n_cap as [Hkv][n_blocks][n_cap] (NaN for c not in E).
+ */
+typedef struct { double sigma; int64_t c; } scored_chunk;
+
+static int by_score_desc_then_id(const void *pa, const void *pb)
+{
+    const scored_chunk *a = (const scored_chunk *)pa;
+    const scored_chunk *b = (const scored_chunk *)pb;
+    if (a->sigma > b->sigma) return -1;
+    if (a->sigma < b->sigma) return 1;
+    return (a->c < b->c) ? -1 : (a->c > b->c);
+}
+
+static int by_id_asc(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
+                  int64_t D, int64_t p0, int64_t C, int64_t Bq,
+                  const double *S, int64_t n_cap, int64_t k,
+                  int32_t *ids, double *sigma_out)
+{
+    int64_t G = Hq / Hkv;
+    int64_t n_blocks = n_q / Bq;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t u = 0; u < Hkv * n_blocks; ++u) {
+        int64_t g = u / n_blocks, b = u % n_blocks;
+        int64_t P = p0 + b * Bq;
+        int64_t nE = P / C;                 /* chunks c with (c+1)*C <= P */
+        if (nE > n_cap) nE = n_cap;
+
+        double *qbar = (double *)malloc((size_t)D * sizeof(double));
+        for (int64_t d = 0; d < D; ++d) {
+            double sum = 0.0;
+            for (int64_t h = g * G; h < g * G + G; ++h)
+                for (int64_t i = b * Bq; i < b * Bq + Bq; ++i)
+                    sum += (double)Q[(h * n_q + i) * D + d];
+            qbar[d] = sum / (double)(G * Bq);
+        }
+
+        scored_chunk *cand = (scored_chunk *)malloc((size_t)(nE > 0 ? nE : 1) * sizeof(scored_chunk));
+        for (int64_t c = 0; c < nE; ++c) {
+            double sigma = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                sigma += qbar[d] * S[(g * n_cap + c) * D + d];
+            cand[c].sigma = sigma;
+            cand[c].c = c;
+        }
+        if (sigma_out) {
+            double *row = sigma_out + (g * n_blocks + b) * n_cap;
+            for (int64_t c = 0; c < n_cap; ++c) row[c] = NAN;
+            for (int64_t c = 0; c < nE; ++c) row[c] = cand[c].sigma;
+        }
+
+        qsort(cand, (size_t)nE, sizeof(scored_chunk), by_score_desc_then_id);
+        int64_t take = nE < k ? nE : k;
+        int32_t *out = ids + (g * n_blocks + b) * k;
+        for (int64_t r = 0; r < take; ++r) out[r] = (int32_t)cand[r].c;
+        qsort(out, (size_t)take, sizeof(int32_t), by_id_asc);
+        for (int64_t r = take; r < k; ++r) out[r] = -1;
+
+        free(cand);
+        free(qbar);
+    }
+}
+
+/* ---------------------------------------------------------- attended set A(i)
+ * Exact-token attention (technical summary 2.1: only the exact K/V of the
+ * selected units enter attention; summaries are never attention values).
+ * For active query i (absolute position p = p0 + i) in block b = i / Bq with
+ * first position P = p0 + b*Bq and kv head g:
+ *     A(i) = union over listed chunks c with 0 <= c < P/C of [cC, cC + C)
+ *            united with the causal local block [P, p].
+ * The listed chunk set is taken as a set (a repeated id adds nothing).
+ * Returns the number of positions written to pos (ascending within each part).
+ */
+static int64_t attended_positions(const int32_t *ids_gb, int64_t k, int64_t C,
+                                  int64_t P, int64_t p, int64_t *pos,
+                                  unsigned char *seen, int64_t n_seen)
+{
+    int64_t n = 0;
+    memset(seen, 0, (size_t)n_seen);
+    for (int64_t r = 0; r < k; ++r) {
+        int64_t c = ids_gb[r];
+        if (c < 0 || c >= P / C || c >= n_seen || seen[c]) continue;
+        seen[c] = 1;
+    }
+    for (int64_t c = 0; c < n_seen; ++c)
+        if (seen[c])
+            for (int64_t t = c * C; t < c * C + C; ++t) pos[n++] = t;
+    for (int64_t t = P; t <= p; ++t) pos[n++] = t;
+    return n;
+}
+
+static int is_attended(const int32_t *ids_gb, int64_t k, int64_t C,
+                       int64_t P, int64_t p, int64_t j)
+{
+    if (j >= P) return j <= p;
+    int64_t c = j / C;
+    if (c >= P / C) return 0;
+    for (int64_t r = 0; r < k; ++r)
+        if (ids_gb[r] == c) return 1;
+    return 0;
+}
+
+static double dot_fd(const float *a, const float *b, int64_t D)
+{
+    double s = 0.0;
+    for (int64_t d = 0; d < D; ++d) s += (double)a[d] * (double)b[d];
+    return s;
+}
+
+/* --------------------------------------------------------------- attend fwd
+ * For every active query i of query head h (kv head g = h / G):
+ *     z_j   = scale * Q[h][i] . K[g][j]           j in A(i)
+ *     m     = max_j z_j
+ *     l     = sum_j exp(z_j - m)
+ *     O[h][i] = (sum_j exp(z_j - m) V[g][j]) / l
+ *     lse[h][i] = m + ln l
+ * unit_mask ([Hq][n_blocks], may be NULL) limits the work to chosen
+ * (head, block) units; other rows of O/lse are left untouched.
+ */
+void oracle_attend_fwd(const float *Q, const float *K, const float *V,
+                       int64_t Hq, int64_t Hkv, int64_t D, int64_t T,
+                       int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
+                       const int32_t *ids, int64_t k, double scale,
+                       const uint8_t *unit_mask, double *O, double *lse)
+{
+    int64_t G = Hq / Hkv;
+    int64_t n_blocks = n_q / Bq;
+    int64_t n_chunks = T / C;
+#pragma omp parallel
+    {
+        int64_t *pos = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
+        double *z = (double *)malloc((size_t)(T + 1) * sizeof(double));
+        double *acc = (double *)malloc((size_t)D * sizeof(double));
+        unsigned char *seen = (unsigned char *)malloc((size_t)n_chunks + 1);
+#pragma omp for schedule(dynamic)
+        for (int64_t row = 0; row < Hq * n_q; ++row) {
+            int64_t h = row / n_q, i = row % n_q;
+            int64_t b = i / Bq, g = h / G;
+            if (unit_mask && !unit_mask[h * n_blocks + b]) continue;
+            int64_t P = p0 + b * Bq, p = p0 + i;
+            const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
+            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks);
+            const float *q = Q + (h * n_q + i) * D;
+
+            double m = -INFINITY;
+            for (int64_t a = 0; a < n; ++a) {
+                z[a] = scale * dot_fd(q, K + (g * T + pos[a]) * D, D);
+                if (z[a] > m) m = z[a];
+            }
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                double e = exp(z[a] - m);
+                l += e;
+                const float *v = V + (g * T + pos[a]) * D;
+                for (int64_t d = 0; d < D; ++d) acc[d] += e * (double)v[d];
+            }
+            for (int64_t d = 0; d < D; ++d) O[(h * n_q + i) * D + d] = acc[d] / l;
+            lse[h * n_q + i] = m + log(l);
+        }
+        free(seen); free(acc); free(z); free(pos);
+    }
+}
+
+/* --------------------------------------------------------------- attend bwd
+ * Gradient of the attention above for an upstream gradient dO, with the
+ * routed ids held constant (no gradient through routing) and every key/value
+ * before p0 detached (segment-wise backward, technical summary 2.2):
+ *     P_ij   = exp(z_j - lse_i)
+ *     Delta_i = sum_j P_ij dO_i . V_j  ( = dO_i . O_i )
+ *     dS_ij  = P_ij (dO_i . V_j - Delta_i)
+ *     dQ_i   = scale * sum_{j in A(i)} dS_ij K_j
+ *     dK_j   = scale * sum_{(h,i) : j in A(i)} dS_ij Q_i      p0 <= j < p0+n_q
+ *     dV_j   =         sum_{(h,i) : j in A(i)} P_ij dO_i      p0 <= j < p0+n_q
+ * dQ is [Hq][n_q][D]; dK, dV are [Hkv][n_q][D] indexed by j - p0.
+ * dq_mask ([Hq][n_blocks]) and dkv_mask ([Hkv][n_q/C]) may be NULL; masked-out
+ * rows are left untouched. lse and O are recomputed here from Q, K, V.
+ */
+void oracle_attend_bwd(const float *Q, const float *K, const float *V,
+                       const float *dO,
+                       int64_t Hq, int64_t Hkv, int64_t D, int64_t T,
+                       int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
+                       const int32_t *ids, int64_t k, double scale,
+                       const uint8_t *dq_mask, const uint8_t *dkv_mask,
+                       double *dQ, double *dK, double *dV)
+{
+    int64_t G = Hq / Hkv;
+    int64_t n_blocks = n_q / Bq;
+    int64_t n_chunks = T / C;
+    double *lse = (double *)malloc((size_t)(Hq * n_q) * sizeof(double));
+    double *Obuf = (double *)malloc((size_t)(Hq * n_q * D) * sizeof(double));
+    double *Delta = (double *)malloc((size_t)(Hq * n_q) * sizeof(double));
+
+    /* pass 1: lse, O and Delta for every active query */
+    oracle_attend_fwd(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k, scale,
+                      NULL, Obuf, lse);
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < Hq * n_q; ++row) {
+        double s = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            s += (double)dO[row * D + d] * Obuf[row * D + d];
+        Delta[row] = s;
+    }
+
+    /* pass 2: dQ, query by query over its attended set */
+#pragma omp parallel
+    {
+        int64_t *pos = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
+        double *acc = (double *)malloc((size_t)D * sizeof(double));
+        unsigned char *seen = (unsigned char *)malloc((size_t)n_chunks + 1);
+#pragma omp for schedule(dynamic)
+        for (int64_t row = 0; row < Hq * n_q; ++row) {
+            int64_t h = row / n_q, i = row % n_q;
+            int64_t b = i / Bq, g = h / G;
+            if (dq_mask && !dq_mask[h * n_blocks + b]) continue;
+            int64_t P = p0 + b * Bq, p = p0 + i;
+            const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
+            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks);
+            const float *q = Q + row * D;
+            const float *go = dO + row * D;
+            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                const float *kj = K + (g * T + pos[a]) * D;
+                const float *vj = V + (g * T + pos[a]) * D;
+                double Pij = exp(scale * dot_fd(q, kj, D) - lse[row]);
+                double dS = Pij * (dot_fd(go, vj, D) - Delta[row]);
+                for (int64_t d = 0; d < D; ++d) acc[d] += dS * (double)kj[d];
+            }
+            for (int64_t d = 0; d < D; ++d) dQ[row * D + d] = scale * acc[d];
+        }
+        free(seen); free(acc); free(pos);
+    }
+
+    /* pass 3: dK, dV, key by key over every (head, query) that attends it */
+#pragma omp parallel
+    {
+        double *ak = (double *)malloc((size_t)D * sizeof(double));
+        double *av = (double *)malloc((size_t)D * sizeof(double));
+#pragma omp for schedule(dynamic)
+        for (int64_t kr = 0; kr < Hkv * n_q; ++kr) {
+            int64_t g = kr / n_q, jj = kr % n_q, j = p0 + jj;
+            if (dkv_mask && !dkv_mask[g * (n_q / C) + jj / C]) continue;
+            const float *kj = K + (g * T + j) * D;
+            const float *vj = V + (g * T + j) * D;
+            for (int64_t d = 0; d < D; ++d) { ak[d] = 0.0; av[d] = 0.0; }
+            for (int64_t h = g * G; h < g * G + G; ++h) {
+                for (int64_t i = 0; i < n_q; ++i) {
+                    int64_t b = i / Bq, P = p0 + b * Bq, p = p0 + i;
+                    if (!is_attended(ids + (g * n_blocks + b) * k, k, C, P, p, j))
+                        continue;
+                    int64_t row = h * n_q + i;
+                    const float *q = Q + row * D;
+                    const float *go = dO + row * D;
+                    double Pij = exp(scale * dot_fd(q, kj, D) - lse[row]);
+                    double dS = Pij * (dot_fd(go, vj, D) - Delta[row]);
+                    for (int64_t d = 0; d < D; ++d) {
+                        ak[d] += dS * (double)q[d];
+                        av[d] += Pij * (double)go[d];
+                    }
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                dK[kr * D + d] = scale * ak[d];
+                dV[kr * D + d] = av[d];
+            }
+        }
+        free(av); free(ak);
+    }
+    free(Delta); free(Obuf); free(lse);
+}
