@@ -1,0 +1,172 @@
+/*
+ * hga.h -- C ABI of libhga, the gfx950 (MI355X) hot path of Hierarchical
+ * Global Attention (HGA): chunk summaries -> per-block top-k chunk routing ->
+ * exact attention over the routed chunks plus the causal local block, and its
+ * segment-wise backward.
+ *
+ * Method: arXiv 2607.15105, "Long-Context Fine-Tuning with Limited VRAM"
+ * (gist.science technical summary, section 2.1 "Hierarchical Global
+ * Attention" and section 2.2 "segment-wise backward and tiered storage";
+ * author abstract on franklineh.com and fugumt.com).
+ *
+ * Conventions shared by every call
+ *   - Notation: Hq query heads, Hkv key/value heads, G = Hq / Hkv, head dim
+ *     D = 128, chunk C = 64, query block Bq = C, top-k k. Query head h uses
+ *     key/value head h / G.
+ *   - All buffers are caller-owned, contiguous device memory. The library
+ *     never allocates or frees device memory and keeps no global mutable
+ *     state apart from a thread-local error string; it is reentrant.
+ *   - Layouts (row-major, innermost last):
+ *       Q, O, dO        bf16  [Hq][n_q][D]      active queries p0 .. p0+n_q-1
+ *       K, V            bf16  [Hkv][T_cap][D]   every position 0 .. T_cap-1
+ *       summaries       f32   [Hkv][n_chunk_cap][D]
+ *       ids             int32 [Hkv][n_q/Bq][k]
+ *       lse             f32   [Hq][n_q]
+ *       dQ              f32   [Hq][n_q][D]
+ *       dK, dV          f32   [Hkv][n_q][D]     active keys p0 .. p0+n_q-1
+ *     bf16 buffers hold raw bfloat16 bit patterns (uint16_t storage).
+ *   - Every call only enqueues work on `stream` (NULL = the null stream) and
+ *     returns; results are visible once the caller synchronises. Device-side
+ *     faults surface at that synchronisation, not in the return code.
+ *   - Argument checks are synchronous and complete before anything is
+ *     launched: a call that returns an error has enqueued nothing.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type, declared as HIP itself declares it. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum hga_status {
+    HGA_OK = 0,
+    HGA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned position  */
+    HGA_ERR_UNSUPPORTED = 2,   /* a shape this build has no kernel for         */
+    HGA_ERR_CAPACITY = 3,      /* a buffer too small for the requested work    */
+    HGA_ERR_HIP = 4            /* the HIP runtime refused a launch             */
+} hga_status;
+
+typedef enum hga_dtype { HGA_BF16 = 0 } hga_dtype;
+
+typedef struct hga_config {
+    int32_t n_q_heads;      /* Hq; a multiple of n_kv_heads                    */
+    int32_t n_kv_heads;     /* Hkv; G = Hq / Hkv must be 1, 2, 4 or 8          */
+    int32_t head_dim;       /* D; must be 128                                  */
+    int32_t chunk;          /* C; must be 64 (the pages' example chunk length) */
+    int32_t q_block;        /* Bq; must equal chunk                            */
+    int32_t top_k;          /* k; 0 .. 256 routed chunks per query block       */
+    float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                   */
+    int32_t dtype;          /* HGA_BF16                                        */
+} hga_config;
+
+/*
+ * hga_summarize -- append chunk summaries (technical summary 2.1, chunk
+ * selection: a compact summary vector per closed fixed-size chunk stays
+ * resident). For every kv head g and every chunk c with
+ * tok_begin <= cC < tok_begin + n_tok:
+ *     summaries[g][c][:] = (1/C) * sum_{t=cC}^{cC+C-1} K[g][t][:]
+ * accumulated in fp32. Rows outside that range are not touched.
+ *   K            device bf16 [Hkv][T_cap][D]
+ *   tok_begin    multiple of C; n_tok >= 0, multiple of C;
+ *                tok_begin + n_tok <= T_cap
+ *   summaries    device f32 [Hkv][n_chunk_cap][D]; needs
+ *                (tok_begin + n_tok)/C <= n_chunk_cap, else HGA_ERR_CAPACITY
+ */
+hga_status hga_summarize(const hga_config *cfg, const void *K, int64_t T_cap,
+                         int64_t tok_begin, int64_t n_tok,
+                         float *summaries, int64_t n_chunk_cap,
+                         hipStream_t stream);
+
+/*
+ * hga_route -- per query block top-k chunk ids (technical summary 2.1: the
+ * current query block scores the resident summaries and keeps the most
+ * relevant earlier chunks; the selection carries no gradient). For kv head g
+ * and block b, first query position P = p0 + b*Bq:
+ *     qbar    = mean of Q[h][i] over the G heads of group g and the Bq
+ *               queries of block b (fp32)
+ *     score_c = qbar . summaries[g][c]     for every chunk c < P/C (fp32)
+ *     ids[g][b][:] = the min(k, P/C) chunks of highest score, ties to the
+ *               lower chunk id, written in ascending id order, then -1.
+ *   Q              device bf16 [Hq][n_q][D]
+ *   summaries      device f32 [Hkv][n_chunk_cap][D]; rows 0 .. n_chunks_valid-1
+ *                  must hold summaries. Needs (p0 + n_q - Bq)/C <= n_chunks_valid
+ *                  <= n_chunk_cap, else HGA_ERR_CAPACITY. Only rows c < P/C are
+ *                  read for block b.
+ *   ids            device int32 [Hkv][n_q/Bq][k]
+ *   scores_or_null device f32 [Hkv][n_q/Bq][k] or NULL: the fp32 score of each
+ *                  written id, -INFINITY beside a -1.
+ */
+hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                     const float *summaries, int64_t n_chunk_cap,
+                     int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                     hipStream_t stream);
+
+/*
+ * hga_attend_fwd -- exact-token attention over the routed chunks and the
+ * causal local block (technical summary 2.1: only the exact K/V of the
+ * selected units enter attention; summaries never act as values). For query
+ * i (position p = p0 + i, block b, head h, kv head g = h/G):
+ *     A(i) = union_{c in ids[g][b], 0 <= c < P/C} [cC, cC+C)  U  [P, p]
+ *     z_j  = scale * Q[h][i] . K[g][j]
+ *     O[h][i]   = sum_{j in A(i)} softmax(z)_j V[g][j]      (bf16, RNE)
+ *     lse[h][i] = ln sum_{j in A(i)} exp(z_j)                (f32)
+ * bf16 operands, fp32 accumulation, the probabilities rounded to bf16 for the
+ * P.V product. ids entries outside [0, P/C) are skipped; non-negative entries
+ * must be ascending and unique, as hga_route writes them.
+ *   Q, O   device bf16 [Hq][n_q][D];   K, V device bf16 [Hkv][T_cap][D]
+ *   ids    device int32 [Hkv][n_q/Bq][k];   lse device f32 [Hq][n_q]
+ *   p0     multiple of C; n_q multiple of Bq; p0 + n_q <= T_cap
+ */
+hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
+                          const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                          const int32_t *ids, void *O, float *lse,
+                          hipStream_t stream);
+
+/*
+ * hga_attend_bwd_workspace_bytes -- size of the device workspace that
+ * hga_attend_bwd needs for n_q active queries (0 on invalid arguments).
+ */
+size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
+
+/*
+ * hga_attend_bwd -- gradient of the attention above for the active segment
+ * only (technical summary 2.2: segment-wise backward; the key/value history
+ * before the segment is detached; routing runs without gradient, so ids are
+ * constants). With P_ij = exp(z_j - lse_i), Delta_i = dO_i . O_i and
+ * dS_ij = P_ij (dO_i . V_j - Delta_i):
+ *     dQ_i = scale * sum_{j in A(i)} dS_ij K_j
+ *     dK_j = scale * sum_{(h,i): j in A(i)} dS_ij Q_i     p0 <= j < p0+n_q
+ *     dV_j =         sum_{(h,i): j in A(i)} P_ij dO_i     p0 <= j < p0+n_q
+ * (sums over the G query heads that share kv head g). O and lse are the
+ * outputs of hga_attend_fwd for the same arguments. Every element of dQ, dK
+ * and dV is written; the caller does not clear them. Deterministic: no atomics.
+ *   workspace  device memory of at least hga_attend_bwd_workspace_bytes bytes,
+ *              else HGA_ERR_CAPACITY; contents on entry are ignored.
+ */
+hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K,
+                          const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                          const int32_t *ids, const void *O, const float *lse,
+                          const void *dO, float *dQ, float *dK_active,
+                          float *dV_active, void *workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *hga_status_string(hga_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *hga_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t hga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

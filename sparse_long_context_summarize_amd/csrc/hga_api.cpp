@@ -1,0 +1,215 @@
+// hga_api.cpp -- the C ABI of libhga: argument checks, status codes and
+// kernel dispatch on the caller's stream. See include/hga.h for the contract
+// of each call. No call allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "hga_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hga_status fail(hga_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+hga_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return HGA_OK;
+    return fail(HGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Largest number of eligible chunks one route workgroup can rank (its keys sit
+// in LDS next to ~22 KiB of fixed state).
+constexpr int64_t kMaxEligible = 24576;
+
+hga_status check_config(const hga_config *cfg)
+{
+    if (!cfg) return fail(HGA_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0)
+        return fail(HGA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
+                    cfg->n_q_heads, cfg->n_kv_heads);
+    if (cfg->n_q_heads % cfg->n_kv_heads != 0)
+        return fail(HGA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                    cfg->n_q_heads, cfg->n_kv_heads);
+    const int G = cfg->n_q_heads / cfg->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(HGA_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", G);
+    if (cfg->head_dim != hga::kD)
+        return fail(HGA_ERR_UNSUPPORTED, "head_dim must be %d (got %d)", hga::kD, cfg->head_dim);
+    if (cfg->chunk != hga::kC)
+        return fail(HGA_ERR_UNSUPPORTED, "chunk must be %d (got %d)", hga::kC, cfg->chunk);
+    if (cfg->q_block != cfg->chunk)
+        return fail(HGA_ERR_UNSUPPORTED, "q_block (%d) must equal chunk (%d)", cfg->q_block,
+                    cfg->chunk);
+    if (cfg->top_k < 0 || cfg->top_k > hga::kMaxTopK)
+        return fail(HGA_ERR_INVALID_ARG, "top_k must be in [0, %d] (got %d)", hga::kMaxTopK,
+                    cfg->top_k);
+    if (cfg->dtype != HGA_BF16)
+        return fail(HGA_ERR_UNSUPPORTED, "dtype must be HGA_BF16 (got %d)", cfg->dtype);
+    if (isnan(cfg->softmax_scale) || isinf(cfg->softmax_scale))
+        return fail(HGA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    return HGA_OK;
+}
+
+float effective_scale(const hga_config *cfg)
+{
+    return cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf((float)cfg->head_dim);
+}
+
+// p0 / n_q / T_cap checks shared by route, fwd and bwd.
+hga_status check_segment(int64_t p0, int64_t n_q, int64_t T_cap, bool need_T)
+{
+    if (p0 < 0 || n_q < 0) return fail(HGA_ERR_INVALID_ARG, "p0 (%lld) and n_q (%lld) must be >= 0",
+                                       (long long)p0, (long long)n_q);
+    if (p0 % hga::kC != 0)
+        return fail(HGA_ERR_INVALID_ARG, "p0 (%lld) is not a multiple of the chunk length %d",
+                    (long long)p0, hga::kC);
+    if (n_q % hga::kC != 0)
+        return fail(HGA_ERR_INVALID_ARG, "n_q (%lld) is not a multiple of the query block %d",
+                    (long long)n_q, hga::kC);
+    if (need_T && p0 + n_q > T_cap)
+        return fail(HGA_ERR_INVALID_ARG, "p0 + n_q (%lld) exceeds T_cap (%lld)",
+                    (long long)(p0 + n_q), (long long)T_cap);
+    if (n_q / hga::kC > (int64_t)INT32_MAX / 64)
+        return fail(HGA_ERR_UNSUPPORTED, "n_q too large");
+    return HGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hga_status_string(hga_status s)
+{
+    switch (s) {
+    case HGA_OK: return "HGA_OK";
+    case HGA_ERR_INVALID_ARG: return "HGA_ERR_INVALID_ARG";
+    case HGA_ERR_UNSUPPORTED: return "HGA_ERR_UNSUPPORTED";
+    case HGA_ERR_CAPACITY: return "HGA_ERR_CAPACITY";
+    case HGA_ERR_HIP: return "HGA_ERR_HIP";
+    }
+    return "HGA_ERR_UNKNOWN";
+}
+
+const char *hga_last_error(void) { return g_last_error; }
+
+int32_t hga_version(void) { return 10000; }   // 1.0.0
+
+hga_status hga_summarize(const hga_config *cfg, const void *K, int64_t T_cap,
+                         int64_t tok_begin, int64_t n_tok, float *summaries,
+                         int64_t n_chunk_cap, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    if (tok_begin < 0 || n_tok < 0 || T_cap < 0 || n_chunk_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative size or position");
+    if (tok_begin % hga::kC != 0 || n_tok % hga::kC != 0)
+        return fail(HGA_ERR_INVALID_ARG, "tok_begin (%lld) and n_tok (%lld) must be multiples of %d",
+                    (long long)tok_begin, (long long)n_tok, hga::kC);
+    if (tok_begin + n_tok > T_cap)
+        return fail(HGA_ERR_INVALID_ARG, "tok_begin + n_tok (%lld) exceeds T_cap (%lld)",
+                    (long long)(tok_begin + n_tok), (long long)T_cap);
+    const int64_t c_begin = tok_begin / hga::kC, c_end = (tok_begin + n_tok) / hga::kC;
+    if (c_end > n_chunk_cap)
+        return fail(HGA_ERR_CAPACITY, "summary buffer holds %lld chunks, %lld needed",
+                    (long long)n_chunk_cap, (long long)c_end);
+    if (n_tok == 0) return HGA_OK;
+    if (!K || !summaries) return fail(HGA_ERR_INVALID_ARG, "K or summaries is NULL");
+    return hip_status(hga::launch_summarize((const uint16_t *)K, cfg->n_kv_heads, T_cap, c_begin,
+                                            c_end, summaries, n_chunk_cap, stream),
+                      "hga_summarize launch");
+}
+
+hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                     const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
+                     int32_t *ids, float *scores_or_null, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, 0, false);
+    if (st != HGA_OK) return st;
+    if (n_chunks_valid < 0 || n_chunk_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative chunk count");
+    if (n_chunks_valid > n_chunk_cap)
+        return fail(HGA_ERR_CAPACITY, "n_chunks_valid (%lld) exceeds n_chunk_cap (%lld)",
+                    (long long)n_chunks_valid, (long long)n_chunk_cap);
+    if (n_q == 0 || cfg->top_k == 0) return HGA_OK;
+    const int64_t need = (p0 + n_q - hga::kC) / hga::kC;   // eligible chunks of the last block
+    if (need > n_chunks_valid)
+        return fail(HGA_ERR_CAPACITY, "the last query block needs %lld summaries, %lld valid",
+                    (long long)need, (long long)n_chunks_valid);
+    if (need > kMaxEligible)
+        return fail(HGA_ERR_UNSUPPORTED, "more than %lld candidate chunks per block",
+                    (long long)kMaxEligible);
+    if (!Q || !ids || (need > 0 && !summaries))
+        return fail(HGA_ERR_INVALID_ARG, "Q, summaries or ids is NULL");
+    return hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads, p0,
+                                        n_q, summaries, n_chunk_cap, cfg->top_k, ids,
+                                        scores_or_null, stream),
+                      "hga_route launch");
+}
+
+hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, const void *V,
+                          int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids, void *O,
+                          float *lse, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (n_q == 0) return HGA_OK;
+    if (!Q || !K || !V || !O || !lse || (cfg->top_k > 0 && !ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
+                                             (const uint16_t *)V, cfg->n_q_heads,
+                                             cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
+                                             effective_scale(cfg), (uint16_t *)O, lse, stream),
+                      "hga_attend_fwd launch");
+}
+
+size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)
+{
+    if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;
+    return hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+}
+
+hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, const void *V,
+                          int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids,
+                          const void *O, const float *lse, const void *dO, float *dQ,
+                          float *dK_active, float *dV_active, void *workspace, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (n_q == 0) return HGA_OK;
+    if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK_active || !dV_active ||
+        (cfg->top_k > 0 && !ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+    if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    return hip_status(hga::launch_attend_bwd((const uint16_t *)Q, (const uint16_t *)K,
+                                             (const uint16_t *)V, cfg->n_q_heads,
+                                             cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
+                                             effective_scale(cfg), (const uint16_t *)O, lse,
+                                             (const uint16_t *)dO, dQ, dK_active, dV_active,
+                                             workspace, stream),
+                      "hga_attend_bwd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// hga_internal.h -- shared device helpers and launcher declarations of libhga
+// (gfx950 only: wave64, bf16 MFMA with 16-deep k per instruction).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hga.h"
+
+namespace hga {
+
+constexpr int kD = 128;      // head dim
+constexpr int kC = 64;       // chunk length == query block length
+constexpr int kMaxTopK = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bit pattern -> f32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Value of lane l ^ 32 (swap of the two half-waves).
+__device__ __forceinline__ float partner32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    // r[0] holds lanes 0..31 of x in both halves, r[1] lanes 32..63 of x.
+    return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger
+// key); -0 is folded onto +0 so equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Launchers (argument checks are done by the caller in hga_api.cpp).
+hipError_t launch_summarize(const uint16_t *K, int64_t Hkv, int64_t T_cap,
+                            int64_t c_begin, int64_t c_end, float *S,
+                            int64_t n_cap, hipStream_t stream);
+
+hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
+                        int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                        int32_t *ids, float *scores, hipStream_t stream);
+
+hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
+                             const uint16_t *V, int64_t Hq, int64_t Hkv,
+                             int64_t T_cap, int64_t p0, int64_t n_q,
+                             const int32_t *ids, int32_t k, float scale,
+                             uint16_t *O, float *lse, hipStream_t stream);
+
+size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
+
+hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K,
+                             const uint16_t *V, int64_t Hq, int64_t Hkv,
+                             int64_t T_cap, int64_t p0, int64_t n_q,
+                             const int32_t *ids, int32_t k, float scale,
+                             const uint16_t *O, const float *lse,
+                             const uint16_t *dO, float *dQ, float *dK,
+                             float *dV, void *workspace, hipStream_t stream);
+
+}  // namespace hga

@@ -1,0 +1,178 @@
+"""Thin ctypes binding of libhga (include/hga.h), one Python function per C
+entry point and with the same name. Argument marshalling only: torch tensors
+provide device memory and the current HIP stream; every step of the hot path
+runs in the library's HIP kernels. There is no fallback: without a built
+``libhga.so`` every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhga.so")
+
+HGA_OK = 0
+HGA_ERR_INVALID_ARG = 1
+HGA_ERR_UNSUPPORTED = 2
+HGA_ERR_CAPACITY = 3
+HGA_ERR_HIP = 4
+HGA_BF16 = 0
+
+EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd",
+            "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
+            "hga_status_string", "hga_last_error", "hga_version")
+
+
+class hga_config(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("q_block", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+def make_config(n_q_heads: int, n_kv_heads: int, top_k: int, *, head_dim: int = 128,
+                chunk: int = 64, q_block: int = 64, softmax_scale: float = 0.0,
+                dtype: int = HGA_BF16) -> hga_config:
+    return hga_config(n_q_heads, n_kv_heads, head_dim, chunk, q_block, top_k,
+                      softmax_scale, dtype)
+
+
+class HGAError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{fn}: {_status_name(status)}: {detail}")
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_cfgp = ctypes.POINTER(hga_config)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhga (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libhga.so not found at {LIB_PATH}; build it with "
+            "`python -m sparse_long_context_summarize_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.hga_summarize.argtypes = [_cfgp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
+    L.hga_route.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp]
+    L.hga_attend_fwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
+    L.hga_attend_bwd_workspace_bytes.argtypes = [_cfgp, _i64]
+    L.hga_attend_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.hga_attend_bwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.hga_status_string.argtypes = [ctypes.c_int]
+    L.hga_status_string.restype = ctypes.c_char_p
+    L.hga_last_error.restype = ctypes.c_char_p
+    L.hga_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    return lib().hga_status_string(status).decode()
+
+
+def hga_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def hga_last_error() -> str:
+    return lib().hga_last_error().decode()
+
+
+def hga_version() -> int:
+    return int(lib().hga_version())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != HGA_OK:
+        raise HGAError(fn, status, hga_last_error())
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype: torch.dtype):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
+                  summaries: torch.Tensor, stream=None) -> None:
+    """K bf16 [Hkv][T_cap][D]; summaries f32 [Hkv][n_chunk_cap][D]."""
+    kp = _dev(K, "K", torch.bfloat16)
+    sp = _dev(summaries, "summaries", torch.float32)
+    _check("hga_summarize", lib().hga_summarize(
+        ctypes.byref(cfg), kp, K.shape[1], tok_begin, n_tok, sp, summaries.shape[1],
+        _stream(stream)))
+
+
+def hga_route(cfg: hga_config, Q: torch.Tensor, p0: int, summaries: torch.Tensor,
+              n_chunks_valid: int, ids: torch.Tensor, scores: torch.Tensor | None = None,
+              stream=None) -> None:
+    """Q bf16 [Hq][n_q][D]; ids int32 [Hkv][n_q/64][k]; scores f32 like ids or None."""
+    qp = _dev(Q, "Q", torch.bfloat16)
+    sp = _dev(summaries, "summaries", torch.float32)
+    ip = _dev(ids, "ids", torch.int32)
+    scp = _dev(scores, "scores", torch.float32)
+    _check("hga_route", lib().hga_route(
+        ctypes.byref(cfg), qp, p0, Q.shape[1], sp, summaries.shape[1], n_chunks_valid, ip,
+        scp, _stream(stream)))
+
+
+def hga_attend_fwd(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                   p0: int, ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
+                   stream=None) -> None:
+    """O bf16 [Hq][n_q][D], lse f32 [Hq][n_q] are written."""
+    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16))
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    _check("hga_attend_fwd", lib().hga_attend_fwd(
+        ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1], _dev(ids, "ids", torch.int32),
+        _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream)))
+
+
+def hga_attend_bwd_workspace_bytes(cfg: hga_config, n_q: int) -> int:
+    return int(lib().hga_attend_bwd_workspace_bytes(ctypes.byref(cfg), n_q))
+
+
+def hga_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV,
+                   workspace: torch.Tensor, stream=None) -> None:
+    """dQ f32 [Hq][n_q][D]; dK, dV f32 [Hkv][n_q][D] (active keys) are written."""
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("hga_attend_bwd", lib().hga_attend_bwd(
+        ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+        _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+        _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
+        _dev(lse, "lse", torch.float32), _dev(dO, "dO", torch.bfloat16),
+        _dev(dQ, "dQ", torch.float32), _dev(dK, "dK", torch.float32),
+        _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream)))

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and each argument check returns its status code before any
+HIP call (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_context_summarize_amd import hga
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "hga.h")
+FAKE = ctypes.c_void_p(0x1000)    # a non-NULL pointer; argument checks fail first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hga_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    L = hga.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(hga.EXPORTED), declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert hga.hga_version() == 10000
+    assert hga.hga_status_string(hga.HGA_OK) == "HGA_OK"
+    assert hga.hga_status_string(hga.HGA_ERR_CAPACITY) == "HGA_ERR_CAPACITY"
+    assert hga.hga_status_string(99) == "HGA_ERR_UNKNOWN"
+
+
+def _cfg(**kw):
+    base = dict(n_q_heads=32, n_kv_heads=8, top_k=16)
+    base.update(kw)
+    return hga.make_config(base.pop("n_q_heads"), base.pop("n_kv_heads"), base.pop("top_k"),
+                           **base)
+
+
+def _fwd(cfg, p0=14336, n_q=2048, T=16384, ids=FAKE, O=FAKE):
+    return hga.lib().hga_attend_fwd(ctypes.byref(cfg), FAKE, FAKE, FAKE, T, p0, n_q, ids, O,
+                                    FAKE, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(n_q_heads=30, n_kv_heads=8), hga.HGA_ERR_INVALID_ARG, "multiple"),
+    (dict(n_q_heads=48, n_kv_heads=8), hga.HGA_ERR_UNSUPPORTED, "1, 2, 4 or 8"),
+    (dict(n_kv_heads=0), hga.HGA_ERR_INVALID_ARG, "positive"),
+    (dict(head_dim=64), hga.HGA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(chunk=32, q_block=32), hga.HGA_ERR_UNSUPPORTED, "chunk"),
+    (dict(q_block=128), hga.HGA_ERR_UNSUPPORTED, "q_block"),
+    (dict(top_k=257), hga.HGA_ERR_INVALID_ARG, "top_k"),
+    (dict(top_k=-1), hga.HGA_ERR_INVALID_ARG, "top_k"),
+    (dict(dtype=1), hga.HGA_ERR_UNSUPPORTED, "dtype"),
+    (dict(softmax_scale=float("nan")), hga.HGA_ERR_INVALID_ARG, "finite"),
+])
+def test_config_checks(kw, status, needle):
+    cfg = _cfg(**kw)
+    assert _fwd(cfg) == status
+    assert needle in hga.hga_last_error()
+
+
+def test_null_config():
+    assert hga.lib().hga_attend_fwd(None, FAKE, FAKE, FAKE, 16384, 0, 64, FAKE, FAKE, FAKE,
+                                    None) == hga.HGA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("p0,n_q,T,needle", [
+    (14335, 2048, 16384, "p0"),
+    (14336, 2047, 16384, "n_q"),
+    (14336, 2048, 16383, "T_cap"),
+    (-64, 64, 16384, ">= 0"),
+])
+def test_segment_checks(p0, n_q, T, needle):
+    assert _fwd(_cfg(), p0=p0, n_q=n_q, T=T) == hga.HGA_ERR_INVALID_ARG
+    assert needle in hga.hga_last_error()
+
+
+def test_null_pointers():
+    assert _fwd(_cfg(), O=None) == hga.HGA_ERR_INVALID_ARG
+    assert _fwd(_cfg(), ids=None) == hga.HGA_ERR_INVALID_ARG
+    # k = 0 needs no ids; n_q = 0 is a no-op that launches nothing
+    assert _fwd(_cfg(top_k=0), n_q=0, ids=None) == hga.HGA_OK
+
+
+def test_summarize_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    s = L.hga_summarize
+    assert s(ctypes.byref(cfg), FAKE, 16384, 32, 64, FAKE, 256, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(ctypes.byref(cfg), FAKE, 16384, 0, 100, FAKE, 256, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(ctypes.byref(cfg), FAKE, 16384, 16320, 128, FAKE, 512, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(ctypes.byref(cfg), FAKE, 16384, 0, 16384, FAKE, 255, None) == hga.HGA_ERR_CAPACITY
+    assert "255" in hga.hga_last_error()
+    assert s(ctypes.byref(cfg), None, 16384, 0, 64, FAKE, 256, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(ctypes.byref(cfg), FAKE, 16384, 64, 0, FAKE, 256, None) == hga.HGA_OK
+
+
+def test_route_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    r = L.hga_route
+    # the last block of 14336 + 2048 needs 255 summaries
+    assert r(ctypes.byref(cfg), FAKE, 14336, 2048, FAKE, 256, 254, FAKE, None,
+             None) == hga.HGA_ERR_CAPACITY
+    assert r(ctypes.byref(cfg), FAKE, 14336, 2048, FAKE, 256, 257, FAKE, None,
+             None) == hga.HGA_ERR_CAPACITY
+    assert r(ctypes.byref(cfg), FAKE, 14300, 2048, FAKE, 256, 255, FAKE, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert r(ctypes.byref(cfg), FAKE, 14336, 2048, FAKE, 256, 255, None, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    big = 64 * 30000
+    assert r(ctypes.byref(cfg), FAKE, big, 64, FAKE, 30000, 30000, FAKE, None,
+             None) == hga.HGA_ERR_UNSUPPORTED
+    assert r(ctypes.byref(_cfg(top_k=0)), FAKE, 14336, 2048, FAKE, 256, 255, None, None,
+             None) == hga.HGA_OK
+
+
+def test_bwd_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    need = hga.hga_attend_bwd_workspace_bytes(cfg, 2048)
+    assert need > 0
+    assert hga.hga_attend_bwd_workspace_bytes(cfg, 2047) == 0
+    assert hga.hga_attend_bwd_workspace_bytes(_cfg(head_dim=64), 2048) == 0
+    b = L.hga_attend_bwd
+    args = [ctypes.byref(cfg), FAKE, FAKE, FAKE, 16384, 14336, 2048, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE]
+    assert b(*args, FAKE, need - 1, None) == hga.HGA_ERR_CAPACITY
+    assert b(*args, None, need, None) == hga.HGA_ERR_INVALID_ARG
+    bad = list(args)
+    bad[13] = None                      # dV
+    assert b(*bad, FAKE, need, None) == hga.HGA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    cfg = _cfg()
+    K = torch.zeros(8, 64, 128, dtype=torch.bfloat16)
+    S = torch.zeros(8, 1, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        hga.hga_summarize(cfg, K, 0, 64, S)
