@@ -137,17 +137,24 @@ size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
 /*
  * hga_attend_bwd -- gradient of the attention above for the active segment
  * only (technical summary 2.2: segment-wise backward; the key/value history
- * before the segment is detached; routing runs without gradient, so ids are
- * constants). With P_ij = exp(z_j - lse_i), Delta_i = dO_i . O_i and
- * dS_ij = P_ij (dO_i . V_j - Delta_i):
+ * before the segment is detached; technical summary 2.1: routing runs without
+ * gradient, so ids are constants). With P_ij = exp(z_j - lse_i),
+ * Delta_i = sum_j P_ij (dO_i . V_j) and dS_ij = P_ij (dO_i . V_j - Delta_i):
  *     dQ_i = scale * sum_{j in A(i)} dS_ij K_j
  *     dK_j = scale * sum_{(h,i): j in A(i)} dS_ij Q_i     p0 <= j < p0+n_q
  *     dV_j =         sum_{(h,i): j in A(i)} P_ij dO_i     p0 <= j < p0+n_q
- * (sums over the G query heads that share kv head g). O and lse are the
- * outputs of hga_attend_fwd for the same arguments. Every element of dQ, dK
- * and dV is written; the caller does not clear them. Deterministic: no atomics.
+ * (sums over the G query heads that share kv head g). lse is the output of
+ * hga_attend_fwd for the same arguments. Delta is recomputed in fp32 from P
+ * and dP rather than taken as dO . O, because the bf16 rounding of O would
+ * reach dS undamped wherever attention concentrates on a few keys; O is
+ * therefore accepted for interface symmetry but not read (it may be NULL).
+ * Every element of dQ, dK and dV is written; the caller does not clear them.
+ * Deterministic: no output is accumulated with atomics, every sum has a fixed
+ * order (a per-chunk counter in the workspace only decides which workgroup
+ * adds the partial sums). At most 65536 active queries (HGA_ERR_UNSUPPORTED).
  *   workspace  device memory of at least hga_attend_bwd_workspace_bytes bytes,
- *              else HGA_ERR_CAPACITY; contents on entry are ignored.
+ *              else HGA_ERR_CAPACITY; contents on entry are ignored; calls that
+ *              share one workspace must not overlap in time.
  */
 hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K,
                           const void *V, int64_t T_cap, int64_t p0, int64_t n_q,

@@ -196,7 +196,10 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, c
     st = check_segment(p0, n_q, T_cap, true);
     if (st != HGA_OK) return st;
     if (n_q == 0) return HGA_OK;
-    if (!Q || !K || !V || !O || !lse || !dO || !dQ || !dK_active || !dV_active ||
+    if (n_q > hga::bwd_max_queries())
+        return fail(HGA_ERR_UNSUPPORTED, "backward supports at most %lld active queries",
+                    (long long)hga::bwd_max_queries());
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
         (cfg->top_k > 0 && !ids))
         return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
     const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);

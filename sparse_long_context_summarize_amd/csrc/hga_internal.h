@@ -62,6 +62,9 @@ hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
 
+// Largest active segment (queries) the backward's key-major pass can list.
+int64_t bwd_max_queries();
+
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
