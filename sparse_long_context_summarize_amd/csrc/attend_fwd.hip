@@ -5,28 +5,34 @@
 //
 // Work unit: one query block b (64 queries) of one kv head g, i.e. the G query
 // heads that share g -- one gather of each routed chunk serves all of them.
-// A workgroup has 4 waves and serves up to 4 query heads (wave w -> head
-// g*G + 4*hg + w); G = 8 takes two workgroups per unit, G < 4 leaves the spare
-// waves to help with the loads.
+// A workgroup has 8 waves (two per SIMD, so one wave's softmax arithmetic
+// overlaps the other's matrix work) and serves up to 4 query heads: wave w
+// takes head g*G + 4*hg + w/2, queries 32*(w%2) .. +32 of the block. G = 8
+// takes two workgroups per unit; G < 4 leaves spare waves that only load.
 //
-// Per chunk tile (64 keys), per wave (64 queries = 2 tiles of 32):
-//   S^T[key][q] = K Q^T          A = K rows from LDS, B = Q^T from registers
-//   online softmax on S^T        each lane owns one query (lane & 31) and 16
-//                                of its 32 keys per 32-key tile; the other 16
-//                                sit in lane ^ 32, one swap joins them
-//   O^T[d][q] += V^T P^T         A = V^T rows from LDS, B = P^T straight from
-//                                the S^T accumulators (bf16)
-// using v_mfma_f32_32x32x16_bf16 (fp32 accumulate). The accumulator row order
-// of a 32x32 tile (8*(j/4) + 4*(lane/32) + j%4) makes the P^T operand's k
-// index a permutation of the keys; V^T is stored in LDS under the same
-// permutation (bits 2 and 3 of the key index swapped), so each operand is one
-// 16-byte LDS read.
+// Per chunk tile (64 keys), per wave (32 queries), v_mfma_f32_32x32x16_bf16
+// with fp32 accumulation:
+//   S^T[key][q] = K Q^T      A = K rows from LDS, B = Q^T held in registers
+//   online softmax on S^T    each lane owns one query (lane & 31) and 16 of the
+//                            32 keys of each 32-key half; lane ^ 32 holds the
+//                            other 16, one lane swap joins them
+//   O^T[d][q] += V^T P^T     B = P^T straight from the S^T accumulators (bf16);
+//                            A = V^T read from the row-major V tile with the
+//                            gfx950 transposing LDS read ds_read_b64_tr_b16
+//                            (each 16-lane group turns four 4-element row
+//                            pieces into four 4-key columns), two per operand.
+// The S^T accumulator's row order (8*(j/4) + 4*(lane/32) + j%4) fixes which
+// keys each lane's P^T operand holds; the transposing reads fetch V rows in
+// exactly that order, so no data is permuted anywhere.
+// The running max is rescaled lazily: O^T and the row sum are only rescaled
+// when some row's max grows by more than 8 (log2 units), otherwise the stale
+// max stays and probabilities up to 2^8 enter the bf16 operand unchanged.
 //
-// Chunk tiles are double buffered in LDS: the 32 KiB of K and V for tile t+1
-// are loaded to registers (16-byte coalesced loads, a 256-byte key row per 16
-// lanes) while tile t is computed, then written to the other buffer, one
-// barrier per tile. Rows are padded (K: 272 B, V^T: 144 B) so the 16-byte
-// operand reads hit distinct banks.
+// Chunk tiles (32 KiB of K and V) are loaded two tiles ahead into registers
+// (16-byte coalesced loads, a 256-byte key row per 16 lanes) and written to a
+// double-buffered LDS tile one barrier before use. LDS rows are padded: K to
+// 272 B (conflict-free 16-byte operand reads), V to 320 B (the four rows a
+// transposing read touches start 64 B apart in the banks).
 //
 // Workgroup w serves kv head w % Hkv: with 8 kv heads every block of one head
 // runs on the same XCD, where neighbouring blocks' overlapping chunk choices
@@ -36,66 +42,70 @@
 namespace hga {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kKStride = kD + 8;            // bf16 elements per K row in LDS (272 B)
-constexpr int kVtStride = kC + 8;           // bf16 elements per V^T row in LDS (144 B)
+constexpr int kThreads = 512;
+constexpr int kKStride = kD + 8;            // bf16 per K row in LDS (272 B)
+constexpr int kVStride = kD + 32;           // bf16 per V row in LDS (320 B)
 constexpr int kKTile = kC * kKStride;       // elements
-constexpr int kVtTile = kD * kVtStride;     // elements
-constexpr int kLoadsPerThread = kC * kD * 2 / 16 / kThreads;   // 16-byte loads of K (and of V)
+constexpr int kVTile = kC * kVStride;       // elements
+constexpr int kRowsPerThread = kC * kD * 2 / 16 / kThreads;   // 16-byte pieces per tensor
+constexpr float kLazy = 8.0f;               // log2 growth that forces a rescale
+// s_waitcnt immediate (gfx9 encoding): vector memory count 0, others no wait.
+constexpr int kWaitVm0 = 0x0F70;
 
-static_assert(kLoadsPerThread == 4, "tile loader assumes 4 rows per thread");
+static_assert(kRowsPerThread == 2, "tile loader assumes 2 pieces per tensor per thread");
 
-// Position of key kk (0..63) inside a V^T row: swap bits 2 and 3.
-__device__ __forceinline__ int vt_pos(int kk) {
-    return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct TileRegs {
-    u32x4 k[kLoadsPerThread];
-    u32x4 v[kLoadsPerThread];
+    u32x4 k[kRowsPerThread];
+    u32x4 v[kRowsPerThread];
 };
 
-// Thread t loads keys 4*(t/16) + r, r = 0..3, d = 8*(t%16) .. +8.
+// Thread t loads row 32*r + t/16, d = 8*(t%16) .. +8, r = 0, 1.
 __device__ __forceinline__ void load_tile(TileRegs &tr, const uint16_t *Kg,
                                           const uint16_t *Vg, int64_t tok0)
 {
     const int t = threadIdx.x;
-    const int key0 = 4 * (t >> 4);
-    const int dseg = t & 15;
+    const int row0 = t >> 4, dseg = t & 15;
 #pragma unroll
-    for (int r = 0; r < kLoadsPerThread; ++r) {
-        const int64_t off = (tok0 + key0 + r) * kD + dseg * 8;
+    for (int r = 0; r < kRowsPerThread; ++r) {
+        const int64_t off = (tok0 + 32 * r + row0) * kD + dseg * 8;
         tr.k[r] = *(const u32x4 *)(Kg + off);
         tr.v[r] = *(const u32x4 *)(Vg + off);
     }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs &tr, uint16_t *Ks, uint16_t *Vts)
+__device__ __forceinline__ void store_tile(const TileRegs &tr, uint16_t *Ks, uint16_t *Vs)
 {
     const int t = threadIdx.x;
-    const int key0 = 4 * (t >> 4);
-    const int dseg = t & 15;
+    const int row0 = t >> 4, dseg = t & 15;
 #pragma unroll
-    for (int r = 0; r < kLoadsPerThread; ++r)
-        *(u32x4 *)(Ks + (key0 + r) * kKStride + dseg * 8) = tr.k[r];
-    // V^T: for each d of this thread's slice, the 4 keys key0..key0+3 are
-    // adjacent in the permuted order -> one 8-byte write.
-    const int pos = vt_pos(key0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t a = tr.v[0][q], b = tr.v[1][q], c = tr.v[2][q], d = tr.v[3][q];
-        u32x2 even, odd;    // d = 8*dseg + 2q and 8*dseg + 2q + 1
-        even[0] = (a & 0xFFFFu) | (b << 16);
-        even[1] = (c & 0xFFFFu) | (d << 16);
-        odd[0] = (a >> 16) | (b & 0xFFFF0000u);
-        odd[1] = (c >> 16) | (d & 0xFFFF0000u);
-        *(u32x2 *)(Vts + (dseg * 8 + 2 * q) * kVtStride + pos) = even;
-        *(u32x2 *)(Vts + (dseg * 8 + 2 * q + 1) * kVtStride + pos) = odd;
+    for (int r = 0; r < kRowsPerThread; ++r) {
+        *(u32x4 *)(Ks + (32 * r + row0) * kKStride + dseg * 8) = tr.k[r];
+        *(u32x4 *)(Vs + (32 * r + row0) * kVStride + dseg * 8) = tr.v[r];
     }
 }
 
+// A operand V^T[d][key] for d-tile dt, k-step ks: lane gets d = 32*dt + lane%32
+// and keys 16*ks + 8*u + 4*(lane/32) + m (element 4u + m), matching the key
+// order of the P^T operand taken from the S^T accumulators.
+__device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vs, int dt, int ks, int lane)
+{
+    const int grp = lane >> 4, i = lane & 15;
+    const int half = grp >> 1, dsub = grp & 1;
+    const int row = 16 * ks + 4 * half + (i >> 2);
+    const int col = 32 * dt + 16 * dsub + 4 * (i & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + row * kVStride + col));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + (row + 8) * kVStride + col));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int G>
-__global__ __launch_bounds__(kThreads, 1) void attend_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int64_t T_cap,
     int64_t p0, const int32_t *__restrict__ ids, int k, float scale_log2,
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void attend_fwd_kernel(
     constexpr int HW = G < 4 ? G : 4;            // query heads per workgroup
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
-    __shared__ __attribute__((aligned(16))) uint16_t Vts[2][kVtTile];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVTile];
     __shared__ int list[kMaxTopK + 1];
     __shared__ int list_n;
 
@@ -138,140 +148,147 @@ __global__ __launch_bounds__(kThreads, 1) void attend_fwd_kernel(
     __syncthreads();
     const int n_tiles = list_n;
 
-    TileRegs tr;
-    load_tile(tr, Kg, Vg, (int64_t)list[0] * kC);
+    TileRegs tr[2];
+    load_tile(tr[0], Kg, Vg, (int64_t)list[0] * kC);
+    load_tile(tr[1], Kg, Vg, (int64_t)list[min(1, n_tiles - 1)] * kC);
 
-    // Q^T operands: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
-    const bool computes = wave < HW;
-    const int64_t h = g * G + hg * HW + wave;
+    // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
+    const int hw = wave >> 1, qt = wave & 1;
+    const bool computes = hw < HW;
+    const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
     const int half = lane >> 5;
-    bf16x8 qf[2][8];
+    bf16x8 qf[8];
     if (computes) {
+        const uint16_t *qrow = Q + (h * n_q + b * kC + 32 * qt + col) * kD + 8 * half;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                qf[qt][ks] = *(const bf16x8 *)(Q + (h * n_q + b * kC + 32 * qt + col) * kD +
-                                               16 * ks + 8 * half);
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
     }
-    store_tile(tr, Ks[0], Vts[0]);
+    store_tile(tr[0], Ks[0], Vs[0]);
+    // Let the one-time Q loads land here, so no wait for them is left inside
+    // the tile loop (where it would also wait for the prefetch in flight).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
 
-    f32x16 o[2][4];
+    f32x16 o[4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[qt][dt][j] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+        for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
 
-    for (int it = 0; it < n_tiles; ++it) {
+    // One tile step. `pre` receives tile it+2, `nxt` (holding tile it+1) is
+    // written to the other LDS buffer; the caller alternates the two register
+    // sets so both stay statically named.
+    auto tile_step = [&](int it, TileRegs &pre, const TileRegs &nxt) {
         const int buf = it & 1;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_tile(tr, Kg, Vg, (int64_t)list[it + 1] * kC);
+        // Always issue the prefetch (the last tile again near the end) so the
+        // wait before storing `nxt` can leave these newer loads in flight.
+        load_tile(pre, Kg, Vg, (int64_t)list[min(it + 2, n_tiles - 1)] * kC);
 
         if (computes) {
             const uint16_t *Kb = Ks[buf];
-            const uint16_t *Vb = Vts[buf];
-            // S^T = K Q^T for key tiles kt (32 keys) x query tiles qt.
-            f32x16 s[2][2];
+            const uint16_t *Vb = Vs[buf];
+            // S^T = K Q^T for the two 32-key halves kt: all 16 operand reads are
+            // issued first (LDS answers in order, so each MFMA waits only for
+            // its own operand), then the two accumulation chains interleave.
+            f32x16 s[2];
+            {
+                bf16x8 a[2][8];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+                for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                    for (int kt = 0; kt < 2; ++kt)
+                        a[kt][ks] = *(const bf16x8 *)(Kb + (32 * kt + col) * kKStride + 16 * ks + 8 * half);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) s[kt][qt][j] = 0.f;
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 a = *(const bf16x8 *)(Kb + (32 * kt + col) * kKStride +
-                                                       16 * ks + 8 * half);
+                    for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-                        s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ks],
-                                                                            s[kt][qt], 0, 0, 0);
-                }
+                for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kt][ks], qf[ks], s[kt], 0, 0, 0);
             }
             // Causal mask on the local block (the last tile): key > query.
             if (it == n_tiles - 1) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
-                            if (key > 32 * qt + col) s[kt][qt][j] = -INFINITY;
-                        }
-            }
-            // Online softmax in the log2 domain.
-            bf16x8 pb[2][4];
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][qt][j]);
-                mx = fmaxf(mx, partner32(mx));
-                const float m_new = fmaxf(m_run[qt], mx * scale_log2);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-                m_run[qt] = m_new;
-                float psum = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -m_new));
-                        psum += p;
-                        pb[qt][2 * kt + (j >> 3)][j & 7] = (__bf16)p;
+                        const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
+                        if (key > 32 * qt + col) s[kt][j] = -INFINITY;
                     }
-                l_run[qt] = l_run[qt] * alpha + psum;
+            }
+            // Online softmax in the log2 domain, lazily rescaled.
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
+            mx = fmaxf(mx, partner32(mx)) * scale_log2;
+            if (__ballot(mx > m_run + kLazy) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) o[qt][dt][j] *= alpha;
+                    for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
             }
-            // O^T += V^T P^T
+            // Per 32-key half: probabilities -> bf16 P^T operands, the half's
+            // 8 V^T operands (16 transposing reads), then its 8 MFMAs.
+            float psum = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
+            for (int kt = 0; kt < 2; ++kt) {
+                bf16x8 pb[2];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 a = *(const bf16x8 *)(Vb + (32 * dt + col) * kVtStride +
-                                                       16 * ks + 8 * half);
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-                        o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qt][ks],
-                                                                            o[qt][dt], 0, 0, 0);
+                for (int j = 0; j < 16; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j], scale_log2, -m_run));
+                    psum += p;
+                    pb[j >> 3][j & 7] = (__bf16)p;
                 }
+                bf16x8 va[2][4];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) va[kk][dt] = vt_operand(Vb, dt, 2 * kt + kk, lane);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][dt], pb[kk], o[dt], 0, 0, 0);
             }
+            l_run += psum;
         }
-        if (more) store_tile(tr, Ks[buf ^ 1], Vts[buf ^ 1]);
+        if (it + 1 < n_tiles) store_tile(nxt, Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile_step(it, tr[0], tr[1]);
+        if (it + 1 < n_tiles) tile_step(it + 1, tr[1], tr[0]);
     }
 
     if (!computes) return;
     // Normalise and store: lane holds query 32*qt + col, d = 32*dt + 8*u + 4*half + 0..3.
+    const float l_tot = l_run + partner32(l_run);
+    const float inv = 1.0f / l_tot;
+    const int64_t row = h * n_q + b * kC + 32 * qt + col;
+    uint16_t *orow = O + row * kD;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const float l_tot = l_run[qt] + partner32(l_run[qt]);
-        const float inv = 1.0f / l_tot;
-        const int64_t row = h * n_q + b * kC + 32 * qt + col;
-        uint16_t *orow = O + row * kD;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 4; ++u) {
+            bf16x4 v;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bf16x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[qt][dt][4 * u + e] * inv);
-                *(bf16x4 *)(orow + 32 * dt + 8 * u + 4 * half) = v;
-            }
-        if (half == 0)
-            lse[row] = (m_run[qt] + __log2f(l_tot)) * 0.69314718055994530942f;
-    }
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][4 * u + e] * inv);
+            *(bf16x4 *)(orow + 32 * dt + 8 * u + 4 * half) = v;
+        }
+    if (half == 0)
+        lse[row] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 template <int G>

@@ -145,33 +145,45 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
 
-    // 2. scores -> keys.
+    // 2. scores -> keys. Each wave scores 4 chunks per step (16 lanes per
+    // chunk); the loads of kBatch steps are issued before any is used so their
+    // latencies overlap.
     {
+        constexpr int kBatch = 16;
         const int dseg = lane & 15, sub = lane >> 4;
         float qv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[e] = qbar[dseg * 8 + e];
         const float *Sg = S + g * n_cap * kD + dseg * 8;
-        for (int base = wave * 4; base < nE; base += kRouteWaves * 4) {
-            const int c = base + sub;
-            float s = 0.f;
-            if (c < nE) {
-                const f32x4 a = *(const f32x4 *)(Sg + (int64_t)c * kD);
-                const f32x4 bb = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
-                s = qv[0] * a[0];
-                s = fmaf(qv[1], a[1], s);
-                s = fmaf(qv[2], a[2], s);
-                s = fmaf(qv[3], a[3], s);
-                s = fmaf(qv[4], bb[0], s);
-                s = fmaf(qv[5], bb[1], s);
-                s = fmaf(qv[6], bb[2], s);
-                s = fmaf(qv[7], bb[3], s);
+        for (int base = wave * 4; base < nE; base += kRouteWaves * 4 * kBatch) {
+            f32x4 lo[kBatch], hi[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = base + u * kRouteWaves * 4 + sub;
+                if (c < nE) {
+                    lo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
+                    hi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
+                } else {
+                    lo[u] = hi[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            s += __shfl_xor(s, 4);
-            s += __shfl_xor(s, 8);
-            if (dseg == 0 && c < nE) keys[c] = score_key(s);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                float s = qv[0] * lo[u][0];
+                s = fmaf(qv[1], lo[u][1], s);
+                s = fmaf(qv[2], lo[u][2], s);
+                s = fmaf(qv[3], lo[u][3], s);
+                s = fmaf(qv[4], hi[u][0], s);
+                s = fmaf(qv[5], hi[u][1], s);
+                s = fmaf(qv[6], hi[u][2], s);
+                s = fmaf(qv[7], hi[u][3], s);
+                s += __shfl_xor(s, 1);
+                s += __shfl_xor(s, 2);
+                s += __shfl_xor(s, 4);
+                s += __shfl_xor(s, 8);
+                const int c = base + u * kRouteWaves * 4 + sub;
+                if (dseg == 0 && c < nE) keys[c] = score_key(s);
+            }
         }
     }
     __syncthreads();
