@@ -6,13 +6,18 @@
 // One 256-thread workgroup per (query block b, kv head g):
 //   1. qbar = mean of the block's G*64 query rows (fp32, LDS reduction);
 //   2. score_c = qbar . S[g][c] for every chunk c < P/C: 16 lanes per chunk
-//      read one 512-byte summary row with coalesced 16-byte loads, each lane
-//      holding its 8-wide slice of qbar in registers; the 16 partial sums are
-//      folded across lanes. Scores become order-preserving uint32 keys in LDS;
-//   3. top-k by (score desc, id asc): every wave selects its own contiguous
-//      id range with a ballot/popcount threshold search, then wave 0 selects
-//      among the survivors. Selected ids come out in ascending order from a
-//      ballot + mbcnt compaction, so no sort is needed.
+//      read one 512-byte summary row with coalesced 16-byte loads (16 chunks
+//      per wave in flight), each lane holding its 8-wide slice of qbar in
+//      registers; the 16 partial sums are folded with four DPP row adds.
+//      Scores become order-preserving uint32 keys in LDS;
+//   3. top-k by (score desc, id asc), for up to 2048 candidates: one wave
+//      holds every key in registers (NI per lane, candidate it*64 + lane); the
+//      k-th largest key is found one bit at a time from ballot/popcount counts
+//      -- no barrier, no memory traffic per bit -- ties at that key go to the
+//      lowest ids, and the chosen ids come out ascending from a ballot + mbcnt
+//      compaction, so no sort is needed. Larger candidate sets take a
+//      two-stage selection over the keys in LDS (every wave over its id range,
+//      then wave 0 over the survivors).
 // Workgroup w serves kv head w % Hkv: with 8 kv heads the blocks of one head
 // land on one XCD and share its L2 copy of that head's summaries.
 #include "hga_internal.h"
@@ -22,15 +27,44 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kMaxRegKeys = 32;             // keys per lane of the register selection (2048)
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Max / min over the wave: within each 16-lane row by DPP (quad swaps, then
+// mirrors within 8 and 16 lanes), then across row pairs and half-waves with
+// the gfx950 lane-swap instructions. Every lane receives the result.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, s));
-    return x;
+    x = max(x, dpp_u32<0xB1>(x));
+    x = max(x, dpp_u32<0x4E>(x));
+    x = max(x, dpp_u32<0x141>(x));
+    x = max(x, dpp_u32<0x140>(x));
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)r[0], (uint32_t)r[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, s));
+    x = min(x, dpp_u32<0xB1>(x));
+    x = min(x, dpp_u32<0x4E>(x));
+    x = min(x, dpp_u32<0x141>(x));
+    x = min(x, dpp_u32<0x140>(x));
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = min((uint32_t)r[0], (uint32_t)r[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return min((uint32_t)q[0], (uint32_t)q[1]);
+}
+
+// Sum over each 16-lane row, result in every lane of the row: quad swaps
+// (lane ^ 1, lane ^ 2), then mirrors within 8 and within 16 lanes (DPP).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
     return x;
 }
 
@@ -91,7 +125,7 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-template <int G>
+template <int G, int NI>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
     const float *__restrict__ S, int64_t n_cap, int k,
@@ -115,23 +149,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int64_t P = p0 + b * kC;
     const int nE = (int)(P / kC);
 
-    // 1. qbar over the G heads x 64 queries of this block.
+    // 1. qbar over the G heads x 64 queries of this block (8 loads in flight
+    // per thread before any is summed).
     {
         const int dseg = tid & 15, r0 = tid >> 4;
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int m = 0; m < G * 4; ++m) {
-            const int row = r0 + 16 * m;               // 0 .. G*64-1
-            const int64_t h = g * G + row / kC;
-            const int64_t i = b * kC + row % kC;
-            const u32x4 w = *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+        for (int m0 = 0; m0 < G * 4; m0 += 8) {
+            u32x4 w[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] += bf16_lo(w[q]);
-                acc[2 * q + 1] += bf16_hi(w[q]);
+            for (int m = 0; m < 8 && m0 + m < G * 4; ++m) {
+                const int row = r0 + 16 * (m0 + m);        // 0 .. G*64-1
+                const int64_t h = g * G + row / kC;
+                const int64_t i = b * kC + row % kC;
+                w[m] = *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m = 0; m < 8 && m0 + m < G * 4; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += bf16_lo(w[m][q]);
+                    acc[2 * q + 1] += bf16_hi(w[m][q]);
+                }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[r0][dseg * 8 + e] = acc[e];
@@ -159,14 +201,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             f32x4 lo[kBatch], hi[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int c = base + u * kRouteWaves * 4 + sub;
-                if (c < nE) {
-                    lo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
-                    hi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
-                } else {
-                    lo[u] = hi[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                // past the end: re-read the last row (in bounds, result unused)
+                const int c = min(base + u * kRouteWaves * 4 + sub, nE - 1);
+                lo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
+                hi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 float s = qv[0] * lo[u][0];
@@ -177,10 +217,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
                 s = fmaf(qv[5], hi[u][1], s);
                 s = fmaf(qv[6], hi[u][2], s);
                 s = fmaf(qv[7], hi[u][3], s);
-                s += __shfl_xor(s, 1);
-                s += __shfl_xor(s, 2);
-                s += __shfl_xor(s, 4);
-                s += __shfl_xor(s, 8);
+                s = row16_sum(s);
                 const int c = base + u * kRouteWaves * 4 + sub;
                 if (dseg == 0 && c < nE) keys[c] = score_key(s);
             }
@@ -188,7 +225,82 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
 
-    // 3. top-k: each wave over its contiguous id range, then wave 0 merges.
+    int32_t *out = ids + (g * n_blocks + b) * k;
+    float *sout = scores ? scores + (g * n_blocks + b) * k : nullptr;
+
+    if (NI * 64 >= nE) {
+        // 3. one wave, keys in registers: candidate c = it*64 + lane. Empty
+        // slots hold key 0, below every finite score's key (>= 0x00800000) and
+        // below every threshold tried (>= 1), so no test needs a bounds check.
+        if (wave != 0) return;
+        uint32_t key[NI];
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const int c = it * 64 + lane;
+            key[it] = (c < nE) ? keys[c] : 0u;
+        }
+        int n_sel;
+        if (nE <= k) {
+            n_sel = nE;
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const int c = it * 64 + lane;
+                if (c < nE) {
+                    out[c] = c;
+                    if (sout) sout[c] = key_to_score(key[it]);
+                }
+            }
+        } else {
+            uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                mx = max(mx, key[it]);
+                mn = min(mn, key[it] ? key[it] : 0xFFFFFFFFu);
+            }
+            mx = wave_max_u32(mx);
+            mn = wave_min_u32(mn);
+            // Bits above the highest bit in which the keys differ are shared.
+            const uint32_t diff = mx ^ mn;
+            const int top = diff ? 31 - __builtin_clz(diff) : -1;
+            uint32_t T = (top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)));
+            // Largest T with #{key >= T} >= k, one bit at a time.
+            for (int bit = top; bit >= 0; --bit) {
+                const uint32_t cand = T | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
+                if (cnt >= k) T = cand;
+            }
+            int n_gt = 0;
+#pragma unroll
+            for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));
+            const int need = k - n_gt;          // equal keys to take, lowest ids first
+            int eq_seen = 0, pos = 0;
+#pragma unroll
+            for (int it = 0; it < NI; ++it) {
+                const bool eq = key[it] == T;
+                const uint64_t em = __ballot(eq);
+                const bool take = key[it] > T || (eq && eq_seen + lanes_below(em) < need);
+                eq_seen += __popcll(em);
+                const uint64_t sm = __ballot(take);
+                if (take) {
+                    const int r = pos + lanes_below(sm);
+                    out[r] = it * 64 + lane;
+                    if (sout) sout[r] = key_to_score(key[it]);
+                }
+                pos += __popcll(sm);
+            }
+            n_sel = pos;
+        }
+        for (int r = n_sel + lane; r < k; r += 64) {
+            out[r] = -1;
+            if (sout) sout[r] = -INFINITY;
+        }
+        return;
+    }
+
+    // 3'. more than 2048 candidates: each wave selects over its contiguous id
+    // range (keys in LDS), then wave 0 selects among the survivors.
     const int per = (nE + kRouteWaves - 1) / kRouteWaves;
     const int lo = min(nE, wave * per);
     const int hi = min(nE, lo + per);
@@ -209,12 +321,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         }
         // cand_pos is ascending: wave ranges are in order, each list ascending.
         const int n_sel = wave_select(cand_key, m, k, chosen);
-        int32_t *out = ids + (g * n_blocks + b) * k;
-        float *sout = scores ? scores + (g * n_blocks + b) * k : nullptr;
         for (int r = lane; r < k; r += 64) {
             if (r < n_sel) {
-                const int pos = cand_pos[chosen[r]];
-                out[r] = pos;
+                out[r] = cand_pos[chosen[r]];
                 if (sout) sout[r] = key_to_score(cand_key[chosen[r]]);
             } else {
                 out[r] = -1;
@@ -224,17 +333,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
+template <int G, int NI>
+hipError_t launch_route_gn(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
+                           const float *S, int64_t n_cap, int32_t k, int32_t *ids,
+                           float *scores, size_t shmem, hipStream_t stream)
+{
+    const int64_t n_blocks = n_q / kC;
+    hipLaunchKernelGGL((route_kernel<G, NI>), dim3((unsigned)(n_blocks * Hkv)),
+                       dim3(kRouteThreads), shmem, stream, Q, n_q, Hkv, p0, S, n_cap, k,
+                       ids, scores);
+    return hipGetLastError();
+}
+
+// Keys per lane of the register selection: the smallest class that holds the
+// last (largest) block's candidates; beyond 2048 the LDS path takes over.
 template <int G>
 hipError_t launch_route_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
                           const float *S, int64_t n_cap, int32_t k, int32_t *ids,
                           float *scores, hipStream_t stream)
 {
-    const int64_t n_blocks = n_q / kC;
     const int64_t max_eligible = (p0 + n_q - kC) / kC;
     const size_t shmem = (size_t)(max_eligible > 0 ? max_eligible : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(route_kernel<G>, dim3((unsigned)(n_blocks * Hkv)), dim3(kRouteThreads),
-                       shmem, stream, Q, n_q, Hkv, p0, S, n_cap, k, ids, scores);
-    return hipGetLastError();
+    if (max_eligible <= 4 * 64)
+        return launch_route_gn<G, 4>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
+    if (max_eligible <= 8 * 64)
+        return launch_route_gn<G, 8>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
+    if (max_eligible <= 16 * 64)
+        return launch_route_gn<G, 16>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
+    return launch_route_gn<G, kMaxRegKeys>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem,
+                                           stream);
 }
 
 }  // namespace

@@ -275,3 +275,11 @@ def test_ids_outside_the_causal_range_are_skipped():
     O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0)
     check_close("skip O", res["O"], O_ref)
     check_close("skip lse", res["lse"], lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+
+
+def test_route_beyond_2048_candidates():
+    # 2198 / 2199 eligible chunks per block: the wave-level two-stage selection
+    T, n_q = 64 * 2200, 128
+    x = inputs.small_random(12, 4, 1, 128, T, n_q, bf16=True)
+    res = gpu_forward(x, T - n_q, 32)
+    full_check(x, T - n_q, 32, res, where="2200 candidates")
