@@ -5,9 +5,8 @@
 //
 // Work unit: one query block b (64 queries) of one kv head g, i.e. the G query
 // heads that share g -- one gather of each routed chunk serves all of them.
-// A workgroup has 8 waves (two per SIMD, so one wave's softmax arithmetic
-// overlaps the other's matrix work) and serves up to 4 query heads: wave w
-// takes head g*G + 4*hg + w/2, queries 32*(w%2) .. +32 of the block. G = 8
+// A workgroup has 8 waves (two per SIMD) and serves up to 4 query heads: wave
+// w takes head g*G + 4*hg + w%4, queries 32*(w/4) .. +32 of the block. G = 8
 // takes two workgroups per unit; G < 4 leaves spare waves that only load.
 //
 // Per chunk tile (64 keys), per wave (32 queries), v_mfma_f32_32x32x16_bf16
@@ -153,7 +152,7 @@ void attend_fwd_kernel(
     load_tile(tr[1], Kg, Vg, (int64_t)list[min(1, n_tiles - 1)] * kC);
 
     // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
-    const int hw = wave >> 1, qt = wave & 1;
+    const int hw = wave & 3, qt = wave >> 2;
     const bool computes = hw < HW;
     const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
@@ -222,11 +221,13 @@ void attend_fwd_kernel(
                     }
             }
             // Online softmax in the log2 domain, lazily rescaled.
-            float mx = -INFINITY;
+            // (four independent max / sum chains keep the VALU pipeline full)
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kt][j]);
+                for (int j = 0; j < 16; ++j) m4[j & 3] = fmaxf(m4[j & 3], s[kt][j]);
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
             mx = fmaxf(mx, partner32(mx)) * scale_log2;
             if (__ballot(mx > m_run + kLazy) != 0) {
                 const float m_new = fmaxf(m_run, mx);
@@ -240,14 +241,14 @@ void attend_fwd_kernel(
             }
             // Per 32-key half: probabilities -> bf16 P^T operands, the half's
             // 8 V^T operands (16 transposing reads), then its 8 MFMAs.
-            float psum = 0.f;
+            float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 bf16x8 pb[2];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j], scale_log2, -m_run));
-                    psum += p;
+                    ps4[j & 3] += p;
                     pb[j >> 3][j & 7] = (__bf16)p;
                 }
                 bf16x8 va[2][4];
@@ -262,7 +263,7 @@ void attend_fwd_kernel(
                     for (int dt = 0; dt < 4; ++dt)
                         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][dt], pb[kk], o[dt], 0, 0, 0);
             }
-            l_run += psum;
+            l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
         }
         if (it + 1 < n_tiles) store_tile(nxt, Ks[buf ^ 1], Vs[buf ^ 1]);
         __syncthreads();

@@ -121,40 +121,69 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _m_summarize(cfg: hga_config, K, tok_begin: int, n_tok: int, summaries, stream=None):
+    return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), K.shape[1], tok_begin, n_tok,
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], _stream(stream))
+
+
+def _m_route(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids, scores=None,
+             stream=None):
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _stream(stream))
+
+
+def _m_attend_fwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, stream=None):
+    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16))
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1], _dev(ids, "ids", torch.int32),
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
+
+
+def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV, workspace,
+                  stream=None):
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+            _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
+            _dev(lse, "lse", torch.float32), _dev(dO, "dO", torch.bfloat16),
+            _dev(dQ, "dQ", torch.float32), _dev(dK, "dK", torch.float32),
+            _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream))
+
+
+_MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
+            "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd}
+
+
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
                   summaries: torch.Tensor, stream=None) -> None:
     """K bf16 [Hkv][T_cap][D]; summaries f32 [Hkv][n_chunk_cap][D]."""
-    kp = _dev(K, "K", torch.bfloat16)
-    sp = _dev(summaries, "summaries", torch.float32)
     _check("hga_summarize", lib().hga_summarize(
-        ctypes.byref(cfg), kp, K.shape[1], tok_begin, n_tok, sp, summaries.shape[1],
-        _stream(stream)))
+        *_m_summarize(cfg, K, tok_begin, n_tok, summaries, stream)))
 
 
 def hga_route(cfg: hga_config, Q: torch.Tensor, p0: int, summaries: torch.Tensor,
               n_chunks_valid: int, ids: torch.Tensor, scores: torch.Tensor | None = None,
               stream=None) -> None:
     """Q bf16 [Hq][n_q][D]; ids int32 [Hkv][n_q/64][k]; scores f32 like ids or None."""
-    qp = _dev(Q, "Q", torch.bfloat16)
-    sp = _dev(summaries, "summaries", torch.float32)
-    ip = _dev(ids, "ids", torch.int32)
-    scp = _dev(scores, "scores", torch.float32)
     _check("hga_route", lib().hga_route(
-        ctypes.byref(cfg), qp, p0, Q.shape[1], sp, summaries.shape[1], n_chunks_valid, ip,
-        scp, _stream(stream)))
+        *_m_route(cfg, Q, p0, summaries, n_chunks_valid, ids, scores, stream)))
 
 
 def hga_attend_fwd(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                    p0: int, ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
                    stream=None) -> None:
     """O bf16 [Hq][n_q][D], lse f32 [Hq][n_q] are written."""
-    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
-            _dev(V, "V", torch.bfloat16))
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
     _check("hga_attend_fwd", lib().hga_attend_fwd(
-        ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1], _dev(ids, "ids", torch.int32),
-        _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream)))
+        *_m_attend_fwd(cfg, Q, K, V, p0, ids, O, lse, stream)))
 
 
 def hga_attend_bwd_workspace_bytes(cfg: hga_config, n_q: int) -> int:
@@ -164,15 +193,22 @@ def hga_attend_bwd_workspace_bytes(cfg: hga_config, n_q: int) -> int:
 def hga_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV,
                    workspace: torch.Tensor, stream=None) -> None:
     """dQ f32 [Hq][n_q][D]; dK, dV f32 [Hkv][n_q][D] (active keys) are written."""
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
-    if workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous GPU memory")
-    ws_bytes = workspace.numel() * workspace.element_size()
     _check("hga_attend_bwd", lib().hga_attend_bwd(
-        ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
-        _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
-        _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
-        _dev(lse, "lse", torch.float32), _dev(dO, "dO", torch.bfloat16),
-        _dev(dQ, "dQ", torch.float32), _dev(dK, "dK", torch.float32),
-        _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream)))
+        *_m_attend_bwd(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, workspace, stream)))
+
+
+def prepare(name: str, *args, **kwargs):
+    """Marshal the arguments of entry point `name` once and return a
+    zero-argument callable that repeats that exact C call (same pointers,
+    sizes and stream) and raises HGAError on a non-OK status. The tensors
+    passed must stay alive, unmoved, for as long as the callable is used.
+    For launch loops where per-call argument checks would dominate."""
+    fn = getattr(lib(), name)
+    cfg = args[0]
+    c_args = _MARSHAL[name](*args, **kwargs)
+
+    def run(_fn=fn, _a=c_args, _keep=cfg):
+        st = _fn(*_a)
+        if st:
+            raise HGAError(name, st, hga_last_error())
+    return run
