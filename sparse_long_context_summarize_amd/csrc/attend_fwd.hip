@@ -38,68 +38,90 @@
 // hit that XCD's L2.
 #include "hga_internal.h"
 
+#include <type_traits>
+
 namespace hga {
 namespace {
 
 constexpr int kThreads = 512;
 constexpr int kKStride = kD + 8;            // bf16 per K row in LDS (272 B)
-constexpr int kVStride = kD + 32;           // bf16 per V row in LDS (320 B)
+constexpr int kVtStride = kC + 8;           // bf16 per V^T row (one d) in LDS (144 B)
 constexpr int kKTile = kC * kKStride;       // elements
-constexpr int kVTile = kC * kVStride;       // elements
-constexpr int kRowsPerThread = kC * kD * 2 / 16 / kThreads;   // 16-byte pieces per tensor
+constexpr int kVtTile = kD * kVtStride;     // elements
+constexpr int kPieces = kC * kD * 2 * 2 / 16 / kThreads;      // 16-byte pieces per thread
 constexpr float kLazy = 8.0f;               // log2 growth that forces a rescale
-// s_waitcnt immediate (gfx9 encoding): vector memory count 0, others no wait.
-constexpr int kWaitVm0 = 0x0F70;
+// s_waitcnt immediates (gfx9 encoding).
+constexpr int kWaitVm8 = 0x0F78;       // vector memory count 8, others no wait
+constexpr int kLook = 6;                // MFMA operands read this many MFMAs ahead
 
-static_assert(kRowsPerThread == 2, "tile loader assumes 2 pieces per tensor per thread");
+static_assert(kPieces == 4, "tile loader assumes 4 pieces per thread");
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
+// Tile loaders. Waves 4-7 ("K group") move K tiles, waves 0-3 ("V group")
+// move V tiles; each thread holds four 16-byte pieces of one tile.
 struct TileRegs {
-    u32x4 k[kRowsPerThread];
-    u32x4 v[kRowsPerThread];
+    u32x4 p[kPieces];
 };
 
-// Thread t loads row 32*r + t/16, d = 8*(t%16) .. +8, r = 0, 1.
-__device__ __forceinline__ void load_tile(TileRegs &tr, const uint16_t *Kg,
-                                          const uint16_t *Vg, int64_t tok0)
+// K group, u = thread - 256: piece j is key row 16*j + u/16, d = 8*(u%16) .. +8
+// (each load instruction reads four whole 256-B rows).
+__device__ __forceinline__ void load_k(TileRegs &tr, const uint16_t *Kg, int64_t tok0)
 {
-    const int t = threadIdx.x;
-    const int row0 = t >> 4, dseg = t & 15;
+    const int u = threadIdx.x - kThreads / 2;
+    const uint16_t *src = Kg + (tok0 + (u >> 4)) * kD + (u & 15) * 8;
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-        const int64_t off = (tok0 + 32 * r + row0) * kD + dseg * 8;
-        tr.k[r] = *(const u32x4 *)(Kg + off);
-        tr.v[r] = *(const u32x4 *)(Vg + off);
-    }
+    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + 16 * j * kD);
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs &tr, uint16_t *Ks, uint16_t *Vs)
+__device__ __forceinline__ void store_k(const TileRegs &tr, uint16_t *Ks)
 {
-    const int t = threadIdx.x;
-    const int row0 = t >> 4, dseg = t & 15;
+    const int u = threadIdx.x - kThreads / 2;
+    uint16_t *dst = Ks + (u >> 4) * kKStride + (u & 15) * 8;
 #pragma unroll
-    for (int r = 0; r < kRowsPerThread; ++r) {
-        *(u32x4 *)(Ks + (32 * r + row0) * kKStride + dseg * 8) = tr.k[r];
-        *(u32x4 *)(Vs + (32 * r + row0) * kVStride + dseg * 8) = tr.v[r];
+    for (int j = 0; j < kPieces; ++j) *(u32x4 *)(dst + 16 * j * kKStride) = tr.p[j];
+}
+
+// V group, u = thread: lane takes keys 4*kg .. 4*kg+3 of the 8-wide d slice
+// dp, kg = lane%16, dp = 4*(u/64) + lane/16; piece j is key 4*kg + j.
+__device__ __forceinline__ void load_v(TileRegs &tr, const uint16_t *Vg, int64_t tok0)
+{
+    const int u = threadIdx.x, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+    const uint16_t *src = Vg + (tok0 + 4 * kg) * kD + dp * 8;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + j * kD);
+}
+
+// V goes to LDS transposed, V^T[d][pos], where within each 16-key group
+// position 8*h + 4*u + m holds key 8*u + 4*h + m: then the 8 keys that lane l
+// needs for one P^T operand (keys 16*ks + 8*u + 4*(l/32) + m, the S^T
+// accumulator's row order) sit at 8 consecutive positions, one 16-byte read.
+// The 4 keys x 8 d block a lane holds is transposed in registers (byte
+// permutes) and written as 8 rows of 4 keys; with kg = lane%16 the 64 lanes'
+// 8-byte writes fall on distinct banks.
+__device__ __forceinline__ void store_v(const TileRegs &tr, uint16_t *Vt)
+{
+    const int u = threadIdx.x, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+    const int pos = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+    uint16_t *dst = Vt + (8 * dp) * kVtStride + pos;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // element e of each key's 8-wide slice is the low (e even) or high
+        // half of dword e/2; keys (0,1) and (2,3) pack into two dwords.
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 w;
+        w[0] = __builtin_amdgcn_perm(tr.p[1][e >> 1], tr.p[0][e >> 1], sel);
+        w[1] = __builtin_amdgcn_perm(tr.p[3][e >> 1], tr.p[2][e >> 1], sel);
+        *(u32x2 *)(dst + e * kVtStride) = w;
     }
 }
 
 // A operand V^T[d][key] for d-tile dt, k-step ks: lane gets d = 32*dt + lane%32
 // and keys 16*ks + 8*u + 4*(lane/32) + m (element 4u + m), matching the key
 // order of the P^T operand taken from the S^T accumulators.
-__device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vs, int dt, int ks, int lane)
+__device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vt, int dt, int ks, int lane)
 {
-    const int grp = lane >> 4, i = lane & 15;
-    const int half = grp >> 1, dsub = grp & 1;
-    const int row = 16 * ks + 4 * half + (i >> 2);
-    const int col = 32 * dt + 16 * dsub + 4 * (i & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + row * kVStride + col));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(Vs + (row + 8) * kVStride + col));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
+    return *(const bf16x8 *)(Vt + (32 * dt + (lane & 31)) * kVtStride + 16 * ks + 8 * (lane >> 5));
 }
 
 template <int G>
@@ -113,7 +135,7 @@ void attend_fwd_kernel(
     constexpr int HW = G < 4 ? G : 4;            // query heads per workgroup
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVTile];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVtTile];
     __shared__ int list[kMaxTopK + 1];
     __shared__ int list_n;
 
@@ -147,26 +169,36 @@ void attend_fwd_kernel(
     __syncthreads();
     const int n_tiles = list_n;
 
-    TileRegs tr[2];
-    load_tile(tr[0], Kg, Vg, (int64_t)list[0] * kC);
-    load_tile(tr[1], Kg, Vg, (int64_t)list[min(1, n_tiles - 1)] * kC);
-
-    // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
-    const int hw = wave & 3, qt = wave >> 2;
+    // Group A = waves 0-3, group B = waves 4-7: wave w computes head
+    // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
+    const int grp = wave >> 2;
+    const int hw = wave & 3, qt = grp;
     const bool computes = hw < HW;
     const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
     const int half = lane >> 5;
+
+    // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
     bf16x8 qf[8];
     if (computes) {
         const uint16_t *qrow = Q + (h * n_q + b * kC + 32 * qt + col) * kD + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
     }
-    store_tile(tr[0], Ks[0], Vs[0]);
-    // Let the one-time Q loads land here, so no wait for them is left inside
-    // the tile loop (where it would also wait for the prefetch in flight).
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    auto tile_tok = [&](int t) __attribute__((always_inline)) { return (int64_t)list[min(t, n_tiles - 1)] * kC; };
+    TileRegs r0, r1;
+    if (grp == 0) {
+        load_v(r0, Vg, tile_tok(0));
+        load_v(r1, Vg, tile_tok(1));
+    } else {
+        load_k(r0, Kg, tile_tok(0));
+        load_k(r1, Kg, tile_tok(1));
+        store_k(r0, Ks[0]);
+        load_k(r0, Kg, tile_tok(2));
+    }
+    // The Q loads were issued first: let them land here (the eight newer tile
+    // loads may stay in flight), so no wait for them is left in the loop.
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
     __syncthreads();
 
     f32x16 o[4];
@@ -175,102 +207,167 @@ void attend_fwd_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    f32x16 s[2];        // S^T of a tile, from its MFMA half-step to its softmax
+    bf16x8 pb[4];       // P^T of a tile, from its softmax to the next MFMA half-step
 
-    // One tile step. `pre` receives tile it+2, `nxt` (holding tile it+1) is
-    // written to the other LDS buffer; the caller alternates the two register
-    // sets so both stay statically named.
-    auto tile_step = [&](int it, TileRegs &pre, const TileRegs &nxt) {
-        const int buf = it & 1;
-        // Always issue the prefetch (the last tile again near the end) so the
-        // wait before storing `nxt` can leave these newer loads in flight.
-        load_tile(pre, Kg, Vg, (int64_t)list[min(it + 2, n_tiles - 1)] * kC);
-
-        if (computes) {
-            const uint16_t *Kb = Ks[buf];
-            const uint16_t *Vb = Vs[buf];
-            // S^T = K Q^T for the two 32-key halves kt: all 16 operand reads are
-            // issued first (LDS answers in order, so each MFMA waits only for
-            // its own operand), then the two accumulation chains interleave.
-            f32x16 s[2];
-            {
-                bf16x8 a[2][8];
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        a[kt][ks] = *(const bf16x8 *)(Kb + (32 * kt + col) * kKStride + 16 * ks + 8 * half);
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kt][ks], qf[ks], s[kt], 0, 0, 0);
-            }
-            // Causal mask on the local block (the last tile): key > query.
-            if (it == n_tiles - 1) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
-                        if (key > 32 * qt + col) s[kt][j] = -INFINITY;
-                    }
-            }
-            // Online softmax in the log2 domain, lazily rescaled.
-            // (four independent max / sum chains keep the VALU pipeline full)
-            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // MFMA half-step of tile t: PV of tile t-1 (if PV) and S^T of tile t (if
+    // SC), interleaved one MFMA each, operands streamed from LDS kLook MFMAs
+    // ahead of use.
+    auto mf = [&](int t, auto PV, auto SC) __attribute__((always_inline)) {
+        if (!computes) return;
+        constexpr bool kPV = decltype(PV)::value, kSC = decltype(SC)::value;
+        constexpr int NS = (kPV ? 16 : 0) + (kSC ? 16 : 0);
+        const uint16_t *Kb = Ks[t & 1];
+        const uint16_t *Vb = Vs[(t + 1) & 1];
+        // step i -> (is_s, index within its kind)
+        auto is_s = [&](int i) __attribute__((always_inline)) { return kPV && kSC ? (i & 1) == 0 : kSC; };
+        auto idx = [&](int i) __attribute__((always_inline)) { return kPV && kSC ? i >> 1 : i; };
+        auto read = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+            const int j = idx(i);
+            if (is_s(i))     // j = 2*ks + kt
+                return *(const bf16x8 *)(Kb + (32 * (j & 1) + col) * kKStride + 16 * (j >> 1) + 8 * half);
+            return vt_operand(Vb, j & 3, j >> 2, lane);     // j = 4*kk + dt
+        };
+        if (kSC) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) m4[j & 3] = fmaxf(m4[j & 3], s[kt][j]);
-            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-            mx = fmaxf(mx, partner32(mx)) * scale_log2;
-            if (__ballot(mx > m_run + kLazy) != 0) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
+                for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
+        }
+        bf16x8 op[NS];
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
+        for (int i = 0; i < kLook; ++i) op[i] = read(i);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-            }
-            // Per 32-key half: probabilities -> bf16 P^T operands, the half's
-            // 8 V^T operands (16 transposing reads), then its 8 MFMAs.
-            float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NS; ++i) {
+            if (i + kLook < NS) op[i + kLook] = read(i + kLook);
+            const int j = idx(i);
+            if (is_s(i))
+                s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[j >> 1], s[j & 1], 0, 0, 0);
+            else
+                o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], pb[j >> 2], o[j & 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Softmax half-step of tile t: causal mask on the local block (the last
+    // tile), online softmax in the log2 domain with a lazy rescale, P^T to bf16.
+    auto va = [&](int t) __attribute__((always_inline)) {
+        if (!computes) return;
+        if (t == n_tiles - 1) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                bf16x8 pb[2];
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j], scale_log2, -m_run));
-                    ps4[j & 3] += p;
-                    pb[j >> 3][j & 7] = (__bf16)p;
+                    const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
+                    if (key > 32 * qt + col) s[kt][j] = -INFINITY;
                 }
-                bf16x8 va[2][4];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) va[kk][dt] = vt_operand(Vb, dt, 2 * kt + kk, lane);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][dt], pb[kk], o[dt], 0, 0, 0);
-            }
-            l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
         }
-        if (it + 1 < n_tiles) store_tile(nxt, Ks[buf ^ 1], Vs[buf ^ 1]);
+        // (four independent max / sum chains keep the VALU pipeline full)
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m4[j & 3] = fmaxf(m4[j & 3], s[kt][j]);
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        mx = fmaxf(mx, partner32(mx)) * scale_log2;
+        if (__ballot(mx > m_run + kLazy) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+        }
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j], scale_log2, -m_run));
+                ps4[j & 3] += p;
+                pb[2 * kt + (j >> 3)][j & 7] = (__bf16)p;
+            }
+        l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+    };
+
+    // Loader duties, in the group's softmax half-steps. V group, tile t: V(t)
+    // to LDS, prefetch V(t+2). K group, tile t: K(t+2) to LDS, prefetch K(t+4).
+    auto duty_v = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
+        store_v(rr, Vs[t & 1]);
+        load_v(rr, Vg, tile_tok(t + 2));
+    };
+    auto duty_k = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
+        if (t + 2 < n_tiles) store_k(rr, Ks[t & 1]);
+        load_k(rr, Kg, tile_tok(t + 4));
+    };
+    const std::true_type Y{};
+    const std::false_type N{};
+
+    // Half-step schedule (each ends at a workgroup barrier), tile t:
+    //   slot 2t:   A: PV(t-1) + S(t)     B: softmax(t-1), K(t+1) to LDS
+    //   slot 2t+1: A: softmax(t), V(t)   B: PV(t-1) + S(t)
+    // so on every SIMD one wave's MFMAs overlap the other wave's softmax.
+    // Buffers: K(t) is read in slots 2t, 2t+1 and rewritten with K(t+2) in
+    // slot 2t+2; V(t) is written in slot 2t+1 and read in slots 2t+2, 2t+3.
+    // Both groups pass 2*n_tiles barriers.
+    // The loops below run whole pairs of tiles (register sets r0, r1 in a
+    // fixed order) and leave an odd tile to a copy after the loop, so the
+    // compiler sees one order of outstanding loads at the loop head and can
+    // wait for the older prefetch set only.
+    auto step_a = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
+        mf(t, Y, Y);
+        __syncthreads();
+        va(t);
+        duty_v(t, rr);
         __syncthreads();
     };
-    for (int it = 0; it < n_tiles; it += 2) {
-        tile_step(it, tr[0], tr[1]);
-        if (it + 1 < n_tiles) tile_step(it + 1, tr[1], tr[0]);
+    auto step_b = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
+        mf(t, Y, Y);
+        __syncthreads();
+        va(t);
+        duty_k(t, rr);
+        __syncthreads();
+    };
+    if (grp == 0) {
+        mf(0, N, Y);
+        __syncthreads();
+        va(0);
+        duty_v(0, r0);
+        __syncthreads();
+        int t = 1;
+        for (; t + 1 < n_tiles; t += 2) {
+            step_a(t, r1);
+            step_a(t + 1, r0);
+        }
+        if (t < n_tiles) step_a(t, r1);
+        mf(n_tiles, Y, N);
+    } else {
+        duty_k(-1, r1);
+        __syncthreads();
+        mf(0, N, Y);
+        __syncthreads();
+        int t = 0;
+        if (n_tiles > 1) {
+            va(0);
+            duty_k(0, r0);
+            __syncthreads();
+            t = 1;
+            for (; t + 2 < n_tiles; t += 2) {
+                step_b(t, r1);
+                step_b(t + 1, r0);
+            }
+            if (t + 1 < n_tiles) {
+                step_b(t, r1);
+                ++t;
+            }
+            // tile n_tiles-1: its softmax and the final PV need no barrier after them
+            mf(t, Y, Y);
+            __syncthreads();
+        }
+        va(t);
+        mf(n_tiles, Y, N);
     }
 
     if (!computes) return;
