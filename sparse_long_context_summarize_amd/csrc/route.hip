@@ -4,7 +4,8 @@
 // gradient flows through the choice).
 //
 // One 256-thread workgroup per (query block b, kv head g):
-//   1. qbar = mean of the block's G*64 query rows (fp32, LDS reduction);
+//   1. qbar = mean of the block's G*64 query rows (fp32, LDS reduction); the
+//      first batch of summary rows is loaded together with the query rows;
 //   2. score_c = qbar . S[g][c] for every chunk c < P/C: 16 lanes per chunk
 //      read one 512-byte summary row with coalesced 16-byte loads (16 chunks
 //      per wave in flight), each lane holding its 8-wide slice of qbar in
@@ -13,7 +14,8 @@
 //   3. top-k by (score desc, id asc), for up to 2048 candidates: one wave
 //      holds every key in registers (NI per lane, candidate it*64 + lane); the
 //      k-th largest key is found one bit at a time from ballot/popcount counts
-//      -- no barrier, no memory traffic per bit -- ties at that key go to the
+//      -- no barrier, no memory traffic per bit, and done as soon as exactly k
+//      keys reach the threshold being built -- ties at that key go to the
 //      lowest ids, and the chosen ids come out ascending from a ballot + mbcnt
 //      compaction, so no sort is needed. Larger candidate sets take a
 //      two-stage selection over the keys in LDS (every wave over its id range,
@@ -90,7 +92,9 @@ __device__ int wave_select(const uint32_t *keys, int n, int k, int *out_pos)
     const uint32_t diff = mx ^ mn;
     int top = diff ? 31 - __builtin_clz(diff) : -1;
     uint32_t T = (top >= 31) ? 0u : (mx & ~((2u << top) - 1u));
-    // Largest T with #{key >= T} >= k, one bit at a time.
+    // Largest T with #{key >= T} >= k, one bit at a time; once exactly k keys
+    // reach a candidate threshold they are the k largest, and no lower bit
+    // can change which keys are taken.
     for (int bit = top; bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
         int cnt = 0;
@@ -99,6 +103,7 @@ __device__ int wave_select(const uint32_t *keys, int n, int k, int *out_pos)
             cnt += __popcll(__ballot(p < n && keys[p] >= cand));
         }
         if (cnt >= k) T = cand;
+        if (cnt == k) break;
     }
     int n_gt = 0;
     for (int base = 0; base < n; base += 64) {
@@ -149,32 +154,47 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int64_t P = p0 + b * kC;
     const int nE = (int)(P / kC);
 
-    // 1. qbar over the G heads x 64 queries of this block (8 loads in flight
-    // per thread before any is summed).
+    // Every load that does not depend on qbar is issued first: all of this
+    // thread's query rows and the first batch of summary rows, so the two
+    // memory round trips overlap.
+    constexpr int kBatch = 16;                  // chunk steps per wave per batch
+    constexpr int kStride = kRouteWaves * 4 * kBatch;     // chunks per batch
+    const int sdseg = lane & 15, sub = lane >> 4;
+    const float *Sg = S + g * n_cap * kD + sdseg * 8;
+    f32x4 slo[kBatch], shi[kBatch];
+    auto load_batch = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            // past the end: re-read the last row (in bounds, result unused)
+            const int c = min(base + u * kRouteWaves * 4 + sub, nE - 1);
+            slo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
+            shi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
+        }
+    };
+
+    // 1. qbar over the G heads x 64 queries of this block: thread (r0, dseg)
+    // sums rows r0, r0 + 16, ... at d = 8*dseg .. +8.
     {
         const int dseg = tid & 15, r0 = tid >> 4;
+        u32x4 w[G * 4];
+#pragma unroll
+        for (int m = 0; m < G * 4; ++m) {
+            const int row = r0 + 16 * m;                   // 0 .. G*64-1
+            const int64_t h = g * G + row / kC;
+            const int64_t i = b * kC + row % kC;
+            w[m] = *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+        }
+        if (wave * 4 < nE) load_batch(wave * 4);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int m0 = 0; m0 < G * 4; m0 += 8) {
-            u32x4 w[8];
+        for (int m = 0; m < G * 4; ++m)
 #pragma unroll
-            for (int m = 0; m < 8 && m0 + m < G * 4; ++m) {
-                const int row = r0 + 16 * (m0 + m);        // 0 .. G*64-1
-                const int64_t h = g * G + row / kC;
-                const int64_t i = b * kC + row % kC;
-                w[m] = *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += bf16_lo(w[m][q]);
+                acc[2 * q + 1] += bf16_hi(w[m][q]);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < 8 && m0 + m < G * 4; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] += bf16_lo(w[m][q]);
-                    acc[2 * q + 1] += bf16_hi(w[m][q]);
-                }
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) part[r0][dseg * 8 + e] = acc[e];
     }
@@ -188,38 +208,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     __syncthreads();
 
     // 2. scores -> keys. Each wave scores 4 chunks per step (16 lanes per
-    // chunk); the loads of kBatch steps are issued before any is used so their
-    // latencies overlap.
+    // chunk, each holding its 8-wide slice of qbar), kBatch steps per batch.
     {
-        constexpr int kBatch = 16;
-        const int dseg = lane & 15, sub = lane >> 4;
         float qv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = qbar[dseg * 8 + e];
-        const float *Sg = S + g * n_cap * kD + dseg * 8;
-        for (int base = wave * 4; base < nE; base += kRouteWaves * 4 * kBatch) {
-            f32x4 lo[kBatch], hi[kBatch];
+        for (int e = 0; e < 8; ++e) qv[e] = qbar[sdseg * 8 + e];
+        for (int base = wave * 4; base < nE; base += kStride) {
+            if (base != wave * 4) load_batch(base);
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                // past the end: re-read the last row (in bounds, result unused)
-                const int c = min(base + u * kRouteWaves * 4 + sub, nE - 1);
-                lo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
-                hi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                float s = qv[0] * lo[u][0];
-                s = fmaf(qv[1], lo[u][1], s);
-                s = fmaf(qv[2], lo[u][2], s);
-                s = fmaf(qv[3], lo[u][3], s);
-                s = fmaf(qv[4], hi[u][0], s);
-                s = fmaf(qv[5], hi[u][1], s);
-                s = fmaf(qv[6], hi[u][2], s);
-                s = fmaf(qv[7], hi[u][3], s);
+                float s = qv[0] * slo[u][0];
+                s = fmaf(qv[1], slo[u][1], s);
+                s = fmaf(qv[2], slo[u][2], s);
+                s = fmaf(qv[3], slo[u][3], s);
+                s = fmaf(qv[4], shi[u][0], s);
+                s = fmaf(qv[5], shi[u][1], s);
+                s = fmaf(qv[6], shi[u][2], s);
+                s = fmaf(qv[7], shi[u][3], s);
                 s = row16_sum(s);
                 const int c = base + u * kRouteWaves * 4 + sub;
-                if (dseg == 0 && c < nE) keys[c] = score_key(s);
+                if (sdseg == 0 && c < nE) keys[c] = score_key(s);
             }
         }
     }
@@ -263,13 +271,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             const uint32_t diff = mx ^ mn;
             const int top = diff ? 31 - __builtin_clz(diff) : -1;
             uint32_t T = (top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)));
-            // Largest T with #{key >= T} >= k, one bit at a time.
+            // Largest T with #{key >= T} >= k, one bit at a time (stopping
+            // early once exactly k keys reach the candidate, as above).
             for (int bit = top; bit >= 0; --bit) {
                 const uint32_t cand = T | (1u << bit);
                 int cnt = 0;
 #pragma unroll
                 for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
                 if (cnt >= k) T = cand;
+                if (cnt == k) break;
             }
             int n_gt = 0;
 #pragma unroll

@@ -283,3 +283,29 @@ def test_route_beyond_2048_candidates():
     x = inputs.small_random(12, 4, 1, 128, T, n_q, bf16=True)
     res = gpu_forward(x, T - n_q, 32)
     full_check(x, T - n_q, 32, res, where="2200 candidates")
+
+
+@pytest.mark.parametrize("n_chunks", [32, 2200])
+def test_route_exact_ties_take_lowest_ids(n_chunks):
+    """Chunks repeated bit for bit give equal scores on both sides, so the
+    tie rule alone (higher score, then lower chunk id) fixes every id: the
+    GPU must reproduce the oracle's ids exactly (register selection for 32
+    chunks, the two-stage selection for 2200)."""
+    rng = np.random.default_rng(n_chunks)
+    Hq, Hkv, D, n_q, k = 4, 2, 128, 256, 7
+    T = n_chunks * C
+    p0 = T - n_q
+    x = inputs.small_random(13, Hq, Hkv, D, T, n_q, bf16=True)
+    # five key patterns with well separated offsets; chunk c repeats pattern c % 5
+    pats = rng.standard_normal((Hkv, 5, C, D)).astype(np.float32)
+    pats += (0.4 * np.arange(5, dtype=np.float32))[None, :, None, None]
+    pats = inputs.round_bf16(pats)
+    K = np.empty((Hkv, T, D), np.float32)
+    for c in range(n_chunks):
+        K[:, c * C:(c + 1) * C] = pats[:, c % 5]
+    x["K"] = K
+    res = gpu_forward(x, p0, k)
+    S_ref = check_summaries(x, res, p0, n_q, "ties")
+    ids_ref = oracle.route(x["Q"], S_ref, p0, k, Hkv)
+    np.testing.assert_array_equal(res["ids"], ids_ref)
+    check_attend(x, res, p0, where="ties")
