@@ -5,8 +5,9 @@
 //
 // Two kernels; no output element is accumulated with atomics and every sum
 // runs in a fixed order, so results are bitwise reproducible:
-//   dq     query-major, the forward's work unit (query block x kv head), two
-//          passes over the routed chunks and the causal local block:
+//   dq     query-major, the forward's work unit (query block x kv head) and
+//          wave layout (8 waves, two per SIMD, 32 queries of one head each),
+//          two passes over the routed chunks and the causal local block:
 //          pass 1: S^T = K Q^T, dP^T = V dO^T, P = exp(S - lse),
 //                  Delta_i = sum_j P_ij dP_ij (fp32; written for dkdv)
 //          pass 2: dS = P (dP - Delta), dQ^T += K^T dS^T.
@@ -26,6 +27,10 @@
 //          adds the partials in workgroup order and writes the result. This
 //          spreads the chunks that many blocks chose (routing concentrates on
 //          high-scoring chunks) over several CUs.
+// Both kernels load their tiles two steps ahead into registers (two sets
+// used in a fixed order, steps run in pairs) and write them to double-buffered
+// LDS one barrier before use; transposed copies are written with byte
+// permutes in a lane order whose 8-byte writes fall on distinct banks.
 #include "hga_internal.h"
 
 namespace hga {
@@ -46,42 +51,6 @@ __device__ __forceinline__ int t_pos(int kk) {   // swap bits 2 and 3
     return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
 }
 
-// 64 rows x 128 bf16 of a row-major source, thread t holds rows 4*(t/16)+r
-// and d = 8*(t%16) .. +8.
-struct Rows4 { u32x4 r[4]; };
-
-__device__ __forceinline__ void load_rows(Rows4 &x, const uint16_t *src) {
-    const int t = threadIdx.x;
-    const uint16_t *p = src + (int64_t)(4 * (t >> 4)) * kD + (t & 15) * 8;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x.r[r] = *(const u32x4 *)(p + (int64_t)r * kD);
-}
-
-__device__ __forceinline__ void store_rows(const Rows4 &x, uint16_t *dst) {
-    const int t = threadIdx.x;
-    const int row0 = 4 * (t >> 4), dseg = t & 15;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *(u32x4 *)(dst + (row0 + r) * kRowStride + dseg * 8) = x.r[r];
-}
-
-// Transposed store: dst[d][t_pos(row)] for the thread's 4 rows and 8 d's.
-__device__ __forceinline__ void store_rows_t(const Rows4 &x, uint16_t *dst) {
-    const int t = threadIdx.x;
-    const int row0 = 4 * (t >> 4), dseg = t & 15;
-    const int pos = t_pos(row0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t a = x.r[0][q], b = x.r[1][q], c = x.r[2][q], d = x.r[3][q];
-        u32x2 even, odd;
-        even[0] = (a & 0xFFFFu) | (b << 16);
-        even[1] = (c & 0xFFFFu) | (d << 16);
-        odd[0] = (a >> 16) | (b & 0xFFFF0000u);
-        odd[1] = (c >> 16) | (d & 0xFFFF0000u);
-        *(u32x2 *)(dst + (dseg * 8 + 2 * q) * kTStride + pos) = even;
-        *(u32x2 *)(dst + (dseg * 8 + 2 * q + 1) * kTStride + pos) = odd;
-    }
-}
-
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -91,8 +60,73 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // --------------------------------------------------------------------- dq
 
+constexpr int kDqThreads = 512;
+constexpr int kDqPieces = 4;       // 16-byte pieces of one tile per loader thread
+
+// Tile loaders of the dq kernel. Waves 4-7 ("K group") move K tiles, waves
+// 0-3 ("V group") V tiles; each thread holds four 16-byte pieces.
+struct DqRegs { u32x4 p[kDqPieces]; };
+
+// K group, u = thread - 256: lane takes keys 4*kg .. 4*kg+3 of the 8-wide d
+// slice dp, kg = lane%16, dp = 4*(u/64) + lane/16; piece j is key 4*kg + j.
+__device__ __forceinline__ void dq_load_k(DqRegs &r, const uint16_t *Kg, int64_t tok0)
+{
+    const int u = threadIdx.x - kDqThreads / 2, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+    const uint16_t *src = Kg + (tok0 + 4 * kg) * kD + dp * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) r.p[j] = *(const u32x4 *)(src + j * kD);
+}
+
+// K to LDS twice: row-major (272-B rows) for the S^T operand, and transposed,
+// K^T[d][t_pos(key)], for the dQ^T operand (the 4 keys x 8 d a lane holds are
+// transposed with byte permutes; with kg = lane%16 the 64 lanes' 8-byte
+// writes fall on distinct banks).
+__device__ __forceinline__ void dq_store_k(const DqRegs &r, uint16_t *Ks, uint16_t *Kts)
+{
+    const int u = threadIdx.x - kDqThreads / 2, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j)
+        *(u32x4 *)(Ks + (4 * kg + j) * kRowStride + dp * 8) = r.p[j];
+    uint16_t *dst = Kts + (8 * dp) * kTStride + t_pos(4 * kg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 w;
+        w[0] = __builtin_amdgcn_perm(r.p[1][e >> 1], r.p[0][e >> 1], sel);
+        w[1] = __builtin_amdgcn_perm(r.p[3][e >> 1], r.p[2][e >> 1], sel);
+        *(u32x2 *)(dst + e * kTStride) = w;
+    }
+}
+
+// V group, u = thread: piece j is key row 16*j + u/16, d = 8*(u%16) .. +8.
+__device__ __forceinline__ void dq_load_v(DqRegs &r, const uint16_t *Vg, int64_t tok0)
+{
+    const int u = threadIdx.x;
+    const uint16_t *src = Vg + (tok0 + (u >> 4)) * kD + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) r.p[j] = *(const u32x4 *)(src + 16 * j * kD);
+}
+
+__device__ __forceinline__ void dq_store_v(const DqRegs &r, uint16_t *Vs)
+{
+    const int u = threadIdx.x;
+    uint16_t *dst = Vs + (u >> 4) * kRowStride + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) *(u32x4 *)(dst + 16 * j * kRowStride) = r.p[j];
+}
+
+// Work unit: query block b of kv head g, as in the forward. 8 waves, two per
+// SIMD: wave w computes head g*G + hg*HW + w%4 for queries 32*(w/4) .. +32,
+// with Q^T and dO^T in registers as MFMA B operands, in the transposed form
+// S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (each query's state in one
+// lane pair). Steps walk the tile list twice (pass 1, then pass 2); tiles are
+// loaded two steps ahead into registers and written to double-buffered LDS
+// one barrier before use. Each 64-key tile is processed as two 32-key halves.
 template <int G>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDqThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
@@ -137,166 +171,166 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
     __syncthreads();
     const int n_tiles = list_n;
+    // Each pass walks the tile list once, padded to an even number of steps
+    // (a padding step moves data but computes nothing), so both pass loops
+    // run whole pairs with the register sets in one fixed order.
+    const int n_pass = n_tiles + (n_tiles & 1);
+    const int n_steps = 2 * n_pass;
+    const bool kgrp = tid >= kDqThreads / 2;
 
-    Rows4 kr, vr;
-    load_rows(kr, Kg + (int64_t)list[0] * kC * kD);
-    load_rows(vr, Vg + (int64_t)list[0] * kC * kD);
-
-    const bool computes = wave < HW;
-    const int64_t h = g * G + hg * HW + wave;
+    const int hw = wave & 3, qt = wave >> 2;
+    const bool computes = hw < HW;
+    const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
     const int half = lane >> 5;
-    bf16x8 qf[2][8], df[2][8];
-    float lse2[2], dl[2];
+    const int64_t qrow = h * n_q + b * kC + 32 * qt + col;
+    bf16x8 qf[8], df[8];
+    float lse2 = 0.f, dl = 0.f;
     if (computes) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const int64_t row = h * n_q + b * kC + 32 * qt + col;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                qf[qt][ks] = *(const bf16x8 *)(Q + row * kD + 16 * ks + 8 * half);
-                df[qt][ks] = *(const bf16x8 *)(dO + row * kD + 16 * ks + 8 * half);
-            }
-            lse2[qt] = lse[row] * 1.44269504088896340736f;
-            dl[qt] = 0.f;
+        for (int ks = 0; ks < 8; ++ks) {
+            qf[ks] = *(const bf16x8 *)(Q + qrow * kD + 16 * ks + 8 * half);
+            df[ks] = *(const bf16x8 *)(dO + qrow * kD + 16 * ks + 8 * half);
         }
+        lse2 = lse[qrow] * 1.44269504088896340736f;
     }
-    store_rows(kr, Ks[0]);
-    store_rows_t(kr, Kts[0]);
-    store_rows(vr, Vs[0]);
+    auto step_tok = [&](int st) __attribute__((always_inline)) {
+        const int i = min(st % n_pass, n_tiles - 1);
+        return (int64_t)list[i] * kC;
+    };
+    auto load = [&](DqRegs &r, int st) __attribute__((always_inline)) {
+        if (kgrp) dq_load_k(r, Kg, step_tok(min(st, n_steps - 1)));
+        else dq_load_v(r, Vg, step_tok(min(st, n_steps - 1)));
+    };
+    auto store = [&](const DqRegs &r, int buf) __attribute__((always_inline)) {
+        if (kgrp) dq_store_k(r, Ks[buf], Kts[buf]);
+        else dq_store_v(r, Vs[buf]);
+    };
+    DqRegs r0, r1;
+    load(r0, 0);
+    load(r1, 1);
+    store(r0, 0);
+    // Q, dO and lse have landed once the first tile has (issued before it).
     __syncthreads();
 
-    // One pipeline step: prefetch the next tile (tile order: the list twice),
-    // compute S^T and dP^T of the current tile, hand them to `body`.
-    const int n_steps = 2 * n_tiles;
-    auto step_tile = [&](int step, auto &&body) {
-        const int buf = step & 1;
-        const bool more = step + 1 < n_steps;
-        if (more) {
-            const int nxt = list[(step + 1) % n_tiles];
-            load_rows(kr, Kg + (int64_t)nxt * kC * kD);
-            load_rows(vr, Vg + (int64_t)nxt * kC * kD);
+    // S^T and dP^T of one 32-key half kt of the tile in buffer buf, P in place
+    // of S^T (causal mask on the local block: key 32*kt + 8*(j/4) + 4*half +
+    // j%4 is masked above query 32*qt + col, i.e. when 8*(j/4) + j%4 > thr).
+    auto sdp = [&](int buf, int kt, bool diag, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+        const uint16_t *Kb = Ks[buf];
+        const uint16_t *Vb = Vs[buf];
+        s = zero16();
+        dp = zero16();
+        bf16x8 ka[8], va[8];
+        auto rd = [&](int ks) __attribute__((always_inline)) {
+            const int off = (32 * kt + col) * kRowStride + 16 * ks + 8 * half;
+            ka[ks] = *(const bf16x8 *)(Kb + off);
+            va[ks] = *(const bf16x8 *)(Vb + off);
+        };
+        rd(0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (ks + 1 < 8) rd(ks + 1);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (computes) {
-            const uint16_t *Kb = Ks[buf];
-            const uint16_t *Vb = Vs[buf];
-            f32x16 s[2][2], dp[2][2];
+        const int thr = diag ? 32 * (qt - kt) + col - 4 * half : 1 << 20;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) { s[kt][qt] = zero16(); dp[kt][qt] = zero16(); }
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const int off = (32 * kt + col) * kRowStride + 16 * ks + 8 * half;
-                    const bf16x8 a = *(const bf16x8 *)(Kb + off);
-                    const bf16x8 v = *(const bf16x8 *)(Vb + off);
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) {
-                        s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qt][ks], s[kt][qt], 0, 0, 0);
-                        dp[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, df[qt][ks], dp[kt][qt], 0, 0, 0);
-                    }
-                }
-            }
-            const int it = step < n_tiles ? step : step - n_tiles;
-            const bool diag = it == n_tiles - 1;
-            // P, with the causal mask on the local block (the last tile)
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        float p = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], scale_log2, -lse2[qt]));
-                        if (diag) {
-                            const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
-                            if (key > 32 * qt + col) p = 0.f;
-                        }
-                        s[kt][qt][j] = p;
-                    }
-            body(s, dp, Ks[buf], Kts[buf]);
+        for (int j = 0; j < 16; ++j) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -lse2));
+            s[j] = (8 * (j >> 2) + (j & 3) > thr) ? 0.f : p;
         }
-        if (more) {
-            store_rows(kr, Ks[buf ^ 1]);
-            store_rows_t(kr, Kts[buf ^ 1]);
-            store_rows(vr, Vs[buf ^ 1]);
-        }
+    };
+
+    // One step: prefetch step st+2 into `pre`, compute step st from LDS
+    // buffer st&1 (pass 1 or pass 2 by `body`), write step st+1 (held in
+    // `nxt`) to the other buffer.
+    auto step = [&](int st, DqRegs &pre, const DqRegs &nxt, auto &&body) __attribute__((always_inline)) {
+        const int buf = st & 1;
+        load(pre, st + 2);
+        const int it = st % n_pass;
+        if (computes && it < n_tiles) body(buf, it == n_tiles - 1);
+        if (st + 1 < n_steps) store(nxt, buf ^ 1);
         __syncthreads();
     };
 
     // pass 1: Delta_i = sum_j P_ij dP_ij
-    for (int step = 0; step < n_tiles; ++step)
-        step_tile(step, [&](f32x16 (&p)[2][2], f32x16 (&dp)[2][2], const uint16_t *, const uint16_t *) {
+    auto pass1 = [&](int buf, bool diag) __attribute__((always_inline)) {
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16 s, dp;
+            sdp(buf, kt, diag, s, dp);
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) dl[qt] = fmaf(p[kt][qt][j], dp[kt][qt][j], dl[qt]);
-        });
-    if (computes) {
-        // join the two half-waves' key subsets and publish Delta for dkdv
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            dl[qt] += partner32(dl[qt]);
-            if (half == 0) delta[h * n_q + b * kC + 32 * qt + col] = dl[qt];
+            for (int j = 0; j < 16; ++j) dl = fmaf(s[j], dp[j], dl);
         }
+    };
+    for (int st = 0; st < n_pass; st += 2) {
+        step(st, r0, r1, pass1);
+        step(st + 1, r1, r0, pass1);
     }
+    // Delta complete: join the two half-waves' key subsets, publish for dkdv
+    dl += partner32(dl);
+    if (computes && half == 0) delta[qrow] = dl;
 
-    // pass 2: dS = P (dP - Delta); dQ^T += K^T dS^T
-    f32x16 acc[2][4];
+    // pass 2: dS = P (dP - Delta); dQ^T += K^T dS^T. dS enters the MFMAs as
+    // bf16 hi; halves holding a probability above kPairAbove add the rounding
+    // remainder lo = bf16(dS - hi) in a second round (wave-uniform branch).
+    f32x16 acc[4];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+    auto pass2 = [&](int buf, bool diag) __attribute__((always_inline)) {
+        const uint16_t *Ktb = Kts[buf];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[qt][dt] = zero16();
-    for (int step = n_tiles; step < n_steps; ++step)
-        step_tile(step, [&](f32x16 (&p)[2][2], f32x16 (&dp)[2][2], const uint16_t *, const uint16_t *Ktb) {
-            // dS as a bf16 pair: hi always enters the MFMA, lo only in tiles
-            // holding a probability above kPairAbove (wave-uniform branch)
-            bf16x8 dsh[2][4], dsl[2][4];
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16 s, dp;
+            sdp(buf, kt, diag, s, dp);
+            bf16x8 dsh[2];
             bool big = false;
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+            for (int j = 0; j < 16; ++j) {
+                big |= s[j] > kPairAbove;
+                dp[j] = s[j] * (dp[j] - dl);
+                dsh[j >> 3][j & 7] = (__bf16)dp[j];
+            }
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        big |= p[kt][qt][j] > kPairAbove;
-                        const float ds = p[kt][qt][j] * (dp[kt][qt][j] - dl[qt]);
-                        const __bf16 hi = (__bf16)ds;
-                        dsh[qt][2 * kt + (j >> 3)][j & 7] = hi;
-                        dsl[qt][2 * kt + (j >> 3)][j & 7] = (__bf16)(ds - (float)hi);
-                    }
-            const bool pair = __ballot(big) != 0;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 a = *(const bf16x8 *)(Ktb + (32 * dt + col) * kTStride + 16 * ks + 8 * half);
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-                        acc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsh[qt][ks], acc[qt][dt], 0, 0, 0);
-                    if (pair) {
-#pragma unroll
-                        for (int qt = 0; qt < 2; ++qt)
-                            acc[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsl[qt][ks], acc[qt][dt], 0, 0, 0);
-                    }
+                for (int dt = 0; dt < 4; ++dt) {
+                    const bf16x8 a = *(const bf16x8 *)(Ktb + (32 * dt + col) * kTStride + 16 * (2 * kt + kk) + 8 * half);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsh[kk], acc[dt], 0, 0, 0);
                 }
-        });
+            if (__ballot(big) != 0) {
+                bf16x8 dsl[2];
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    dsl[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsh[j >> 3][j & 7]);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const bf16x8 a = *(const bf16x8 *)(Ktb + (32 * dt + col) * kTStride + 16 * (2 * kt + kk) + 8 * half);
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsl[kk], acc[dt], 0, 0, 0);
+                    }
+            }
+        }
+    };
+    for (int st = n_pass; st < n_steps; st += 2) {
+        step(st, r0, r1, pass2);
+        step(st + 1, r1, r0, pass2);
+    }
 
     if (!computes) return;
+    float *drow = dQ + qrow * kD;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        float *drow = dQ + (h * n_q + b * kC + 32 * qt + col) * kD;
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int u = 0; u < 4; ++u) {
+            f32x4 v;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[qt][dt][4 * u + e] * scale;
-                *(f32x4 *)(drow + 32 * dt + 8 * u + 4 * half) = v;
-            }
-    }
+            for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * u + e] * scale;
+            *(f32x4 *)(drow + 32 * dt + 8 * u + 4 * half) = v;
+        }
 }
 
 // ------------------------------------------------------------------- dkdv
@@ -312,7 +346,7 @@ constexpr int kBufBytes = kDlOff + kC * 4;
 static_assert(kBufBytes % 16 == 0, "buffer alignment");
 static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits");
 
-constexpr int kSplit = 4;                  // workgroups that share one chunk's block list
+constexpr int kSplit = 2;                  // workgroups that share one chunk's block list
 
 template <int G>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
@@ -376,47 +410,76 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         vb[ks] = *(const bf16x8 *)(V + (g * T_cap + key_row) * kD + 16 * ks + 8 * half);
     }
 
-    auto tile_src = [&](int t, int64_t &row0) {
+    auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
+        t = min(t, n_tiles - 1);
         const int64_t bb = blist[split + kSplit * (t / G)];
-        const int64_t h = g * G + t % G;
-        row0 = h * n_q + bb * kC;
+        const int64_t hh = g * G + t % G;
+        return hh * n_q + bb * kC;
     };
-
-    Rows4 qr, dr;
-    float lsev = 0.f, dlv = 0.f;
-    int64_t row0;
-    tile_src(0, row0);
-    load_rows(qr, Q + row0 * kD);
-    load_rows(dr, dO + row0 * kD);
-    if (tid < kC) { lsev = lse[row0 + tid]; dlv = delta[row0 + tid]; }
-
-    auto store_buf = [&](int buf) {
+    // Tile loader (all 256 threads): lane takes rows 4*kg .. 4*kg+3 of the
+    // 8-wide d slice dp of the Q and dO tiles (kg = lane%16, dp = 4*wave +
+    // lane/16), lse and Delta of the tile's queries on threads 0..63.
+    struct TileIn { u32x4 q[4], d[4]; float l, dl; };
+    const int lkg = lane & 15, ldp = 4 * wave + (lane >> 4);
+    auto load = [&](TileIn &r, int t) __attribute__((always_inline)) {
+        const int64_t row0 = tile_row0(t);
+        const uint16_t *qs = Q + (row0 + 4 * lkg) * kD + ldp * 8;
+        const uint16_t *ds = dO + (row0 + 4 * lkg) * kD + ldp * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r.q[j] = *(const u32x4 *)(qs + j * kD);
+            r.d[j] = *(const u32x4 *)(ds + j * kD);
+        }
+        const int qi = tid & (kC - 1);
+        r.l = lse[row0 + qi];
+        r.dl = delta[row0 + qi];
+    };
+    // Q and dO to LDS row-major (S and dP operands) and transposed under the
+    // accumulator's query permutation (dK and dV operands); with kg = lane%16
+    // the 8-byte transposed writes of the 64 lanes fall on distinct banks.
+    auto store = [&](const TileIn &r, int buf) __attribute__((always_inline)) {
         uint8_t *B = smem + buf * kBufBytes;
-        store_rows(qr, (uint16_t *)(B + kQOff));
-        store_rows(dr, (uint16_t *)(B + kDOOff));
-        store_rows_t(qr, (uint16_t *)(B + kQtOff));
-        store_rows_t(dr, (uint16_t *)(B + kDOtOff));
+        uint16_t *Qs = (uint16_t *)(B + kQOff), *dOs = (uint16_t *)(B + kDOOff);
+        uint16_t *Qts = (uint16_t *)(B + kQtOff), *dOts = (uint16_t *)(B + kDOtOff);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *(u32x4 *)(Qs + (4 * lkg + j) * kRowStride + ldp * 8) = r.q[j];
+            *(u32x4 *)(dOs + (4 * lkg + j) * kRowStride + ldp * 8) = r.d[j];
+        }
+        const int pos = t_pos(4 * lkg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            u32x2 wq, wd;
+            wq[0] = __builtin_amdgcn_perm(r.q[1][e >> 1], r.q[0][e >> 1], sel);
+            wq[1] = __builtin_amdgcn_perm(r.q[3][e >> 1], r.q[2][e >> 1], sel);
+            wd[0] = __builtin_amdgcn_perm(r.d[1][e >> 1], r.d[0][e >> 1], sel);
+            wd[1] = __builtin_amdgcn_perm(r.d[3][e >> 1], r.d[2][e >> 1], sel);
+            *(u32x2 *)(Qts + (8 * ldp + e) * kTStride + pos) = wq;
+            *(u32x2 *)(dOts + (8 * ldp + e) * kTStride + pos) = wd;
+        }
         if (tid < kC) {
-            ((float *)(B + kLseOff))[tid] = lsev * 1.44269504088896340736f;
-            ((float *)(B + kDlOff))[tid] = dlv;
+            ((float *)(B + kLseOff))[tid] = r.l * 1.44269504088896340736f;
+            ((float *)(B + kDlOff))[tid] = r.dl;
         }
     };
-    store_buf(0);
+    // Tiles run in pairs (register sets r0, r1 in a fixed order, loaded two
+    // tiles ahead); an odd count gets one padding step that computes nothing.
+    const int n_steps = n_tiles + (n_tiles & 1);
+    TileIn r0, r1;
+    load(r0, 0);
+    load(r1, 1);
+    store(r0, 0);
     __syncthreads();
 
     f32x16 dk[4], dv[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
 
-    for (int it = 0; it < n_tiles; ++it) {
+    auto step = [&](int it, TileIn &pre, const TileIn &nxt) __attribute__((always_inline)) {
         const int buf = it & 1;
-        const bool more = it + 1 < n_tiles;
-        if (more) {
-            tile_src(it + 1, row0);
-            load_rows(qr, Q + row0 * kD);
-            load_rows(dr, dO + row0 * kD);
-            if (tid < kC) { lsev = lse[row0 + tid]; dlv = delta[row0 + tid]; }
-        }
+        load(pre, it + 2);
+        if (it < n_tiles) {
         const uint8_t *B = smem + buf * kBufBytes;
         const uint16_t *Qb = (const uint16_t *)(B + kQOff);
         const uint16_t *dOb = (const uint16_t *)(B + kDOOff);
@@ -433,10 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(Qb + off), kb[ks], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(dOb + off), vb[ks], dp, 0, 0, 0);
         }
-        // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e)
+        // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
+        // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
         const bool diag = split == 0 && (it / G) == 0;   // list entry 0 is the own block
         bf16x8 pb[2], dsb[2];
-        float pf[16], dsf[16];
         bool big = false;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -449,10 +512,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -l4[e]));
                 if (diag && 32 * kh + col > q0 + e) p = 0.f;
                 big |= p > kPairAbove;
-                pf[j] = p;
-                dsf[j] = p * (dp[j] - d4[e]);
-                pb[j >> 3][j & 7] = (__bf16)pf[j];
-                dsb[j >> 3][j & 7] = (__bf16)dsf[j];
+                s[j] = p;
+                dp[j] = p * (dp[j] - d4[e]);
+                pb[j >> 3][j & 7] = (__bf16)s[j];
+                dsb[j >> 3][j & 7] = (__bf16)dp[j];
             }
         }
         // dV^T += dO^T P, dK^T += Q^T dS (k runs over this wave's 32 queries)
@@ -467,8 +530,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         if (__ballot(big) != 0) {              // wave-uniform: add the low halves
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                pb[j >> 3][j & 7] = (__bf16)(pf[j] - (float)pb[j >> 3][j & 7]);
-                dsb[j >> 3][j & 7] = (__bf16)(dsf[j] - (float)dsb[j >> 3][j & 7]);
+                pb[j >> 3][j & 7] = (__bf16)(s[j] - (float)pb[j >> 3][j & 7]);
+                dsb[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsb[j >> 3][j & 7]);
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
@@ -479,8 +542,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(Qtb + off), dsb[ks], dk[dt], 0, 0, 0);
                 }
         }
-        if (more) store_buf(buf ^ 1);
+        }
+        if (it + 1 < n_steps) store(nxt, buf ^ 1);
         __syncthreads();
+    };
+    for (int it = 0; it < n_steps; it += 2) {
+        step(it, r0, r1);
+        step(it + 1, r1, r0);
     }
 
     // Sum the two query halves: waves 2, 3 hand their partials to waves 0, 1.
@@ -581,7 +649,7 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(bwd_dq_kernel<G>, dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kThreads),
+    hipLaunchKernelGGL(bwd_dq_kernel<G>, dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kDqThreads),
                        0, stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, T_cap, p0, ids,
                        k, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
