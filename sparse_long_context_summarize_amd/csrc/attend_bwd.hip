@@ -488,13 +488,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const float *lse2s = (const float *)(B + kLseOff);
         const float *dls = (const float *)(B + kDlOff);
 
-        // S[q][key] = Q K^T, dP[q][key] = dO V^T for this wave's 32 x 32 block.
+        // S[q][key] = Q K^T, dP[q][key] = dO V^T for this wave's 32 x 32 block
+        // (A operands read from LDS two k-steps ahead of their MFMAs).
         f32x16 s = zero16(), dp = zero16();
+        {
+            bf16x8 qa[8], da[8];
+            auto rd = [&](int ks) __attribute__((always_inline)) {
+                const int off = (32 * qh + col) * kRowStride + 16 * ks + 8 * half;
+                qa[ks] = *(const bf16x8 *)(Qb + off);
+                da[ks] = *(const bf16x8 *)(dOb + off);
+            };
+            rd(0);
+            rd(1);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int off = (32 * qh + col) * kRowStride + 16 * ks + 8 * half;
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(Qb + off), kb[ks], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(dOb + off), vb[ks], dp, 0, 0, 0);
+            for (int ks = 0; ks < 8; ++ks) {
+                if (ks + 2 < 8) rd(ks + 2);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vb[ks], dp, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
         // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
@@ -518,14 +530,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 dsb[j >> 3][j & 7] = (__bf16)dp[j];
             }
         }
-        // dV^T += dO^T P, dK^T += Q^T dS (k runs over this wave's 32 queries)
+        // dV^T += dO^T P, dK^T += Q^T dS (k runs over this wave's 32 queries);
+        // the 16 transposed operands are read before the MFMAs that use them
+        // and serve the low-half round too.
+        bf16x8 ta[8], tq[8];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int off = (32 * dt + col) * kTStride + 32 * qh + 16 * ks + 8 * half;
-                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(dOtb + off), pb[ks], dv[dt], 0, 0, 0);
-                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(Qtb + off), dsb[ks], dk[dt], 0, 0, 0);
+                ta[2 * dt + ks] = *(const bf16x8 *)(dOtb + off);
+                tq[2 * dt + ks] = *(const bf16x8 *)(Qtb + off);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
+                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
             }
         if (__ballot(big) != 0) {              // wave-uniform: add the low halves
 #pragma unroll
@@ -537,9 +560,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const int off = (32 * dt + col) * kTStride + 32 * qh + 16 * ks + 8 * half;
-                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(dOtb + off), pb[ks], dv[dt], 0, 0, 0);
-                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8 *)(Qtb + off), dsb[ks], dk[dt], 0, 0, 0);
+                    dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
+                    dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
                 }
         }
         }
