@@ -91,6 +91,24 @@ def attend_bytes(ids: np.ndarray, n_q: int, Hq: int, D: int, p0: int) -> float:
     return float(gathered + Hq * n_q * D * 2 * 2 + Hq * n_q * 4)
 
 
+def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int) -> float:
+    """Algorithmic flops of hga_attend_bwd: per attended (query, key) pair
+    2*D each for S, dP and dQ, plus 2*D each for dK and dV where the key is
+    in the active segment (history is detached)."""
+    Hkv, nb, k = ids.shape
+    P = p0 + np.arange(nb) * C
+    hist = act = 0
+    for b in range(nb):
+        for g in range(Hkv):
+            row = ids[g, b]
+            ok = row[(row >= 0) & (row < P[b] // C)]
+            a = int((ok * C >= p0).sum())
+            act += a * C * C
+            hist += (len(ok) - a) * C * C
+        act += Hkv * (C * (C + 1) // 2)
+    return float(G * (6 * D * hist + 10 * D * act))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +274,9 @@ def extra_timings(torch, hga, inputs, dev):
         torch.cuda.synchronize()
         t = sorted(a.elapsed_time(b) for a, b in times[5:])
         res["bwd16k_ms"] = t[len(t) // 2]
+        fl = bwd_flops(ids.cpu().numpy(), w.n_q, w.G, w.D, w.p0)
+        res["bwd16k_algorithmic_gflop"] = fl / 1e9
+        res["bwd16k_tflops"] = fl / (res["bwd16k_ms"] * 1e-3) / 1e12
     except hga.HGAError as e:
         res["bwd16k_ms"] = None
         res["bwd16k_error"] = str(e)
