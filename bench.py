@@ -263,6 +263,7 @@ def extra_timings(torch, hga, inputs, dev):
     ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg, w.n_q), dtype=torch.uint8,
                      device=dev)
     res.update(segloop_timing(torch, hga, inputs, dev))
+    res.update(attend_timings(torch, hga, inputs, dev))
     try:
         times = []
         for i in range(25):
@@ -280,6 +281,60 @@ def extra_timings(torch, hga, inputs, dev):
     except hga.HGAError as e:
         res["bwd16k_ms"] = None
         res["bwd16k_error"] = str(e)
+    return res
+
+
+def attend_timings(torch, hga, inputs, dev):
+    """hga_attend_fwd alone, HIP-event timed (median of 10 after 3 warm-up
+    launches): at the 128K-history workload (k = 32), and at the 16K layer
+    with L2 and the Infinity Cache flushed before every launch (a 512 MiB
+    write) beside the same launches warm."""
+    res = {}
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    def med(fn, pre=None, n=10):
+        ts = []
+        for i in range(n + 3):
+            if pre is not None:
+                pre()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ts[3:])
+        return t[len(t) // 2]
+
+    for w, tag in ((inputs.LAYER128K, "layer128k"), (inputs.LAYER16K, "layer16k")):
+        x = inputs.generate(w)
+        Q, K, V = up(x["Q"]), up(x["K"]), up(x["V"])
+        cfg = hga.make_config(w.Hq, w.Hkv, w.k)
+        S = torch.zeros((w.Hkv, w.T // C, w.D), device=dev)
+        ids = torch.empty((w.Hkv, w.n_q // C, w.k), dtype=torch.int32, device=dev)
+        O = torch.empty((w.Hq, w.n_q, w.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.Hq, w.n_q), device=dev)
+        hga.hga_summarize(cfg, K, 0, w.T, S)
+        hga.hga_route(cfg, Q, w.p0, S, w.T // C, ids)
+        run = hga.prepare("hga_attend_fwd", cfg, Q, K, V, w.p0, ids, O, lse)
+        flops = attend_flops(ids.cpu().numpy(), w.n_q, w.G, w.D, w.p0)
+        abytes = attend_bytes(ids.cpu().numpy(), w.n_q, w.Hq, w.D, w.p0)
+        if tag == "layer128k":
+            ms = med(run)
+            res["layer128k_attend_us"] = ms * 1e3
+            res["layer128k_attend_tflops"] = flops / (ms * 1e-3) / 1e12
+            res["layer128k_attend_gathered_GBps"] = abytes / (ms * 1e-3) / 1e9
+        else:
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+            ms_cold = med(run, pre=lambda: flush.fill_(1))
+            ms_warm = med(run, pre=lambda: flush[:1].fill_(1))
+            res["layer16k_attend_cold_us"] = ms_cold * 1e3
+            res["layer16k_attend_warm_us"] = ms_warm * 1e3
+            res["layer16k_attend_cold_gathered_GBps"] = abytes / (ms_cold * 1e-3) / 1e9
+            del flush
+        del Q, K, V, S, ids, O, lse
     return res
 
 
