@@ -117,8 +117,10 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
  *     O[h][i]   = sum_{j in A(i)} softmax(z)_j V[g][j]      (bf16, RNE)
  *     lse[h][i] = ln sum_{j in A(i)} exp(z_j)                (f32)
  * bf16 operands, fp32 accumulation, the probabilities rounded to bf16 for the
- * P.V product. ids entries outside [0, P/C) are skipped; non-negative entries
- * must be ascending and unique, as hga_route writes them.
+ * P.V product. ids entries outside [0, P/C) are skipped, and the entries of
+ * a row form a set: their order does not matter and a repeated id is attended
+ * once (rows as hga_route writes them, ascending and distinct, need no
+ * de-duplication work).
  *   Q, O   device bf16 [Hq][n_q][D];   K, V device bf16 [Hkv][T_cap][D]
  *   ids    device int32 [Hkv][n_q/Bq][k];   lse device f32 [Hq][n_q]
  *   p0     multiple of C; n_q multiple of Bq; p0 + n_q <= T_cap
@@ -143,7 +145,8 @@ size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
  *     dQ_i = scale * sum_{j in A(i)} dS_ij K_j
  *     dK_j = scale * sum_{(h,i): j in A(i)} dS_ij Q_i     p0 <= j < p0+n_q
  *     dV_j =         sum_{(h,i): j in A(i)} P_ij dO_i     p0 <= j < p0+n_q
- * (sums over the G query heads that share kv head g). lse is the output of
+ * (sums over the G query heads that share kv head g; A(i) and the ids rule as
+ * for hga_attend_fwd, a set per row). lse is the output of
  * hga_attend_fwd for the same arguments. Delta is recomputed in fp32 from P
  * and dP rather than taken as dO . O, because the bf16 rounding of O would
  * reach dS undamped wherever attention concentrates on a few keys; O is

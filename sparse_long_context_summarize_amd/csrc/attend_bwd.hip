@@ -155,17 +155,8 @@ void bwd_dq_kernel(
     const uint16_t *Vg = V + g * T_cap * kD;
 
     if (wave == 0) {
-        int cnt = 0;
-        const int32_t *row = ids + (g * n_blocks + b) * k;
-        for (int base = 0; base < k; base += 64) {
-            const int r = base + lane;
-            const int c = (r < k) ? row[r] : -1;
-            const bool ok = c >= 0 && (int64_t)c < local_chunk;
-            const uint64_t m = __ballot(ok);
-            if (ok) list[cnt + lanes_below(m)] = c;
-            cnt += __popcll(m);
-        }
-        if (lane == 0) { list[cnt] = (int)local_chunk; list_n = cnt + 1; }
+        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, local_chunk, list);
+        if (lane == 0) list_n = n;
     }
     // the dkdv kernel that follows counts finished workgroups per (kv head, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;

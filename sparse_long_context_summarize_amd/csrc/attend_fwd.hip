@@ -152,19 +152,11 @@ void attend_fwd_kernel(
     const uint16_t *Kg = K + g * T_cap * kD;
     const uint16_t *Vg = V + g * T_cap * kD;
 
-    // Chunk list: valid routed ids (0 <= c < P/C) in order, then the local block.
+    // Chunk list: valid routed ids (0 <= c < P/C) in order, repeats dropped,
+    // then the local block.
     if (wave == 0) {
-        int cnt = 0;
-        const int32_t *row = ids + (g * n_blocks + b) * k;
-        for (int base = 0; base < k; base += 64) {
-            const int r = base + lane;
-            const int c = (r < k) ? row[r] : -1;
-            const bool ok = c >= 0 && (int64_t)c < local_chunk;
-            const uint64_t m = __ballot(ok);
-            if (ok) list[cnt + lanes_below(m)] = c;
-            cnt += __popcll(m);
-        }
-        if (lane == 0) { list[cnt] = (int)local_chunk; list_n = cnt + 1; }
+        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, local_chunk, list);
+        if (lane == 0) list_n = n;
     }
     __syncthreads();
     const int n_tiles = list_n;

@@ -37,6 +37,48 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Tile list of one (query block, kv head) for the attention kernels, built by
+// one wave: the valid routed ids of `row` (0 <= c < local_chunk) in their
+// given order with repeats dropped (the first occurrence stays: the routed
+// chunks form a set), then the local chunk. Returns the list length. A
+// router-made row (ascending, distinct) passes one neighbour check; only a
+// row with a repeat pays the quadratic pass. `list` holds k + 1 entries and
+// is read back by the same wave only.
+__device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
+                                                int64_t local_chunk, int *list)
+{
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int base = 0; base < k; base += 64) {
+        const int r = base + lane;
+        const int c = (r < k) ? row[r] : -1;
+        const bool ok = c >= 0 && (int64_t)c < local_chunk;
+        const uint64_t m = __ballot(ok);
+        if (ok) list[cnt + lanes_below(m)] = c;
+        cnt += __popcll(m);
+    }
+    bool unsorted = false;
+    for (int i = 1 + lane; i < cnt; i += 64) unsorted |= list[i] <= list[i - 1];
+    if (__ballot(unsorted) != 0) {
+        // Keep an entry unless an earlier one holds the same id; compact in
+        // place in index order (every write lands at or below its read).
+        int out = 0;
+        for (int base = 0; base < cnt; base += 64) {
+            const int i = base + lane;
+            const int c = (i < cnt) ? list[i] : -1;
+            bool keep = i < cnt;
+            for (int j = 0; j < base + 64 && j < cnt; ++j)
+                if (j < i && list[j] == c) keep = false;
+            const uint64_t m = __ballot(keep);
+            if (keep) list[out + lanes_below(m)] = c;
+            out += __popcll(m);
+        }
+        cnt = out;
+    }
+    if (lane == 0) list[cnt] = (int)local_chunk;
+    return cnt + 1;
+}
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger
 // key); -0 is folded onto +0 so equal scores give equal keys.
 __device__ __forceinline__ uint32_t score_key(float s) {

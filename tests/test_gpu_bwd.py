@@ -151,3 +151,17 @@ def test_ids_outside_the_causal_range_are_skipped():
                      [1, 3, 12, 14, 15, 2 ** 30]]], dtype=np.int32)
     res = gpu_fwd_bwd(x, p0, 6, ids_override=ids)
     check_grads(x, p0, res, "skipped ids")
+
+
+def test_repeated_and_unsorted_ids_count_once():
+    T, n_q, k = 1024, 256, 80
+    x = inputs.small_random(34, 4, 1, 128, T, n_q, bf16=True, with_dO=True)
+    p0 = T - n_q
+    rng = np.random.default_rng(6)
+    ids = np.full((1, n_q // C, k), -1, np.int32)
+    ids[0, 0] = rng.integers(0, 12, k)
+    ids[0, 1, :6] = [12, 2, 12, 7, 2, 2]                 # active chunk 12 twice
+    ids[0, 2, :5] = [13, 3, 13, 12, 3]
+    ids[0, 3] = np.arange(k) % 15
+    res = gpu_fwd_bwd(x, p0, k, ids_override=ids)
+    check_grads(x, p0, res, "repeated ids")

@@ -309,3 +309,22 @@ def test_route_exact_ties_take_lowest_ids(n_chunks):
     ids_ref = oracle.route(x["Q"], S_ref, p0, k, Hkv)
     np.testing.assert_array_equal(res["ids"], ids_ref)
     check_attend(x, res, p0, where="ties")
+
+
+def test_repeated_and_unsorted_ids_count_once():
+    """A caller's id row is a set: repeats are attended once, in any order
+    (the oracle takes the same definition); k = 80 also exercises rows longer
+    than one wave's 64 lanes."""
+    T, n_q, k = 1024, 256, 80
+    x = inputs.small_random(14, 4, 1, 128, T, n_q, bf16=True)
+    p0 = T - n_q
+    rng = np.random.default_rng(5)
+    ids = np.full((1, n_q // C, k), -1, np.int32)
+    ids[0, 0] = rng.integers(0, 12, k)                    # 80 draws of 12 ids
+    ids[0, 1, :6] = [9, 2, 9, 7, 2, 2]                    # unsorted with repeats
+    ids[0, 2, :4] = [3, 3, 3, 3]
+    ids[0, 3] = np.arange(k) % 15                         # 0..14, each >= 5 times
+    res = gpu_forward(x, p0, k, ids_override=ids)
+    O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0)
+    check_close("repeats O", res["O"], O_ref)
+    check_close("repeats lse", res["lse"], lse_ref, atol=1e-3, rtol=0, rel_l2=None)
