@@ -50,6 +50,9 @@ def _load():
     lib.oracle_summarize.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _f64p, _i64]
     lib.oracle_route.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                  _f64p, _i64, _i64, _i32p, ctypes.c_void_p]
+    lib.oracle_route_groups.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _f64p, _i64, _i32p, _i64, _i64, _i32p,
+                                        ctypes.c_void_p]
     lib.oracle_attend_fwd.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _i32p, _i64,
                                       ctypes.c_double, ctypes.c_void_p, _f64p, _f64p]
@@ -115,9 +118,34 @@ def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_score
     return (ids, sig) if want_scores else ids
 
 
+def route_groups(Q, SG, p0: int, chunk_ids, m: int, Hkv: int, C: int = 64, Bq: int = 64,
+                 U: int = 8, want_scores=False):
+    """Per (kv head, block) top-m groups of U tokens among the groups of the
+    block's routed chunks (chunk_ids [Hkv][n_blocks][k]), ascending, -1 padded.
+
+    SG holds group summaries [Hkv][n_gcap][D] (summarize with C = U). Returns
+    gids [Hkv][n_blocks][m] int32 (and sigma [Hkv][n_blocks][n_gcap] float64,
+    NaN for groups that are not candidates, if want_scores)."""
+    Q = _f32(Q)
+    Hq, n_q, D = Q.shape
+    SG = np.ascontiguousarray(SG, dtype=np.float64)
+    assert SG.shape[0] == Hkv and SG.shape[2] == D and C % U == 0
+    n_gcap = SG.shape[1]
+    chunk_ids = np.ascontiguousarray(chunk_ids, dtype=np.int32)
+    n_blocks = n_q // Bq
+    assert chunk_ids.shape[:2] == (Hkv, n_blocks)
+    gids = np.empty((Hkv, n_blocks, m), dtype=np.int32)
+    sig = np.empty((Hkv, n_blocks, n_gcap)) if want_scores else None
+    _load().oracle_route_groups(Q, Hq, Hkv, n_q, D, p0, C, Bq, U, SG, n_gcap, chunk_ids,
+                                chunk_ids.shape[2], m, gids,
+                                sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None)
+    return (gids, sig) if want_scores else gids
+
+
 def attend_fwd(Q, K, V, ids, p0: int, C: int = 64, Bq: int = 64, scale: float | None = None,
                unit_mask=None):
-    """Exact attention over routed chunks + causal local block.
+    """Exact attention over the routed units + causal local block. ids count
+    units of C tokens: chunks (C = 64) or groups (C = 8, with Bq = 64).
 
     Returns (O [Hq][n_q][D], lse [Hq][n_q]) float64; rows of units excluded by
     ``unit_mask`` ([Hq][n_blocks]) are NaN."""

@@ -17,6 +17,11 @@
  * values); every sum, dot product and exponential is taken in double, in
  * plain ascending index order. Outputs are double.
  *
+ * The same functions serve the second routing level, 8-token groups inside
+ * the chosen chunks: oracle_summarize with C = 8 gives group summaries,
+ * oracle_route_groups keeps the best groups of the routed chunks, and the
+ * attention functions take group ids with C = 8 (the query block stays Bq).
+ *
  * Readings of points the pages leave open (each is listed with its reason in
  * the design notes of this repository):
  *   - summary of a chunk = arithmetic mean of its C key vectors (keys only);
@@ -163,6 +168,90 @@ void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
         for (int64_t r = take; r < k; ++r) out[r] = -1;
 
         free(cand);
+        free(qbar);
+    }
+}
+
+/* -------------------------------------------------------------- route groups
+ * Group routing, the second routing level (technical summary 2.1, group
+ * selection: the chosen chunks are split into smaller groups, e.g. 8 tokens,
+ * whose summaries the router scores to keep the best groups inside the chosen
+ * chunks; exact attention then covers the tokens of the kept groups).
+ *
+ * With U tokens per group (C % U == 0) and group summaries SG[g][u] = mean of
+ * the U keys of group u (oracle_summarize with C = U), for kv head g and query
+ * block b (qbar as in oracle_route):
+ *     Ch       = the chunk ids of chunk_ids[g][b] with 0 <= c < P/C, as a set
+ *     cand     = { u : u / (C/U) in Ch }              the groups of those chunks
+ *     sigma_u  = sum_d qbar[d] * SG[g][u][d]
+ *     keep the first min(m, |cand|) groups ordered by (sigma desc, u asc),
+ *     write them in ascending id order, pad with -1.
+ * chunk_ids is [Hkv][n_blocks][k]; gids is [Hkv][n_blocks][m]. If sigma_out is
+ * not NULL it receives sigma_u for every u < n_gcap as
+ * [Hkv][n_blocks][n_gcap] (NaN for groups that are not candidates).
+ */
+void oracle_route_groups(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
+                         int64_t D, int64_t p0, int64_t C, int64_t Bq, int64_t U,
+                         const double *SG, int64_t n_gcap,
+                         const int32_t *chunk_ids, int64_t k, int64_t m,
+                         int32_t *gids, double *sigma_out)
+{
+    int64_t G = Hq / Hkv;
+    int64_t n_blocks = n_q / Bq;
+    int64_t per = C / U;                    /* groups per chunk */
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t w = 0; w < Hkv * n_blocks; ++w) {
+        int64_t g = w / n_blocks, b = w % n_blocks;
+        int64_t P = p0 + b * Bq;
+
+        double *qbar = (double *)malloc((size_t)D * sizeof(double));
+        for (int64_t d = 0; d < D; ++d) {
+            double sum = 0.0;
+            for (int64_t h = g * G; h < g * G + G; ++h)
+                for (int64_t i = b * Bq; i < b * Bq + Bq; ++i)
+                    sum += (double)Q[(h * n_q + i) * D + d];
+            qbar[d] = sum / (double)(G * Bq);
+        }
+
+        /* the distinct valid chunks of the row, in any order */
+        const int32_t *row = chunk_ids + (g * n_blocks + b) * k;
+        int64_t *chs = (int64_t *)malloc((size_t)(k > 0 ? k : 1) * sizeof(int64_t));
+        int64_t n_ch = 0;
+        for (int64_t r = 0; r < k; ++r) {
+            int64_t c = row[r];
+            if (c < 0 || c >= P / C) continue;
+            int dup = 0;
+            for (int64_t q = 0; q < n_ch; ++q) dup |= chs[q] == c;
+            if (!dup) chs[n_ch++] = c;
+        }
+
+        int64_t n_cand = n_ch * per;
+        scored_chunk *cand = (scored_chunk *)malloc((size_t)(n_cand > 0 ? n_cand : 1) * sizeof(scored_chunk));
+        for (int64_t q = 0; q < n_ch; ++q)
+            for (int64_t j = 0; j < per; ++j) {
+                int64_t u = chs[q] * per + j;
+                double sigma = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    sigma += qbar[d] * SG[(g * n_gcap + u) * D + d];
+                cand[q * per + j].sigma = sigma;
+                cand[q * per + j].c = u;
+            }
+        if (sigma_out) {
+            double *srow = sigma_out + (g * n_blocks + b) * n_gcap;
+            for (int64_t u = 0; u < n_gcap; ++u) srow[u] = NAN;
+            for (int64_t q = 0; q < n_cand; ++q)
+                if (cand[q].c < n_gcap) srow[cand[q].c] = cand[q].sigma;
+        }
+
+        qsort(cand, (size_t)n_cand, sizeof(scored_chunk), by_score_desc_then_id);
+        int64_t take = n_cand < m ? n_cand : m;
+        int32_t *out = gids + (g * n_blocks + b) * m;
+        for (int64_t r = 0; r < take; ++r) out[r] = (int32_t)cand[r].c;
+        qsort(out, (size_t)take, sizeof(int32_t), by_id_asc);
+        for (int64_t r = take; r < m; ++r) out[r] = -1;
+
+        free(cand);
+        free(chs);
         free(qbar);
     }
 }

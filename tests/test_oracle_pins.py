@@ -470,3 +470,111 @@ def test_attend_bwd_masks_limit_work():
     np.testing.assert_array_equal(part[0][1, 16:24], full[0][1, 16:24])
     np.testing.assert_array_equal(part[1][0, 8:16], full[1][0, 8:16])
     assert np.isnan(part[0][0]).all() and np.isnan(part[2][0, :8]).all()
+
+
+# ---------------------------------------------------- group routing (U = 8)
+
+def _group_setup(seed, Hq=4, Hkv=2, D=16, T=1024, n_q=128, C=64, k=3):
+    x = inputs.small_random(seed, Hq, Hkv, D, T, n_q, C=C, bf16=True, with_dO=True)
+    p0 = T - n_q
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(x["Q"], S, p0, k, Hkv, C, 64)
+    SG = oracle.summarize(x["K"], 8, 0, T // 8)
+    return x, p0, ids, SG
+
+
+def test_group_summaries_average_to_their_chunk_summary():
+    x, p0, ids, SG = _group_setup(40)
+    S = oracle.summarize(x["K"], 64, 0, 1024 // 64)
+    np.testing.assert_allclose(SG.reshape(2, 16, 8, 16).mean(axis=2), S, rtol=1e-13, atol=1e-15)
+    K = x["K"].astype(np.float64)
+    np.testing.assert_allclose(SG[1, 37], K[1, 296:304].mean(axis=0), rtol=1e-14, atol=1e-15)
+
+
+def test_route_groups_score_equals_mean_pairwise_logit_over_candidates():
+    x, p0, ids, SG = _group_setup(41)
+    gids, sig = oracle.route_groups(x["Q"], SG, p0, ids, 5, 2, want_scores=True)
+    Q = x["Q"].astype(np.float64)
+    K = x["K"].astype(np.float64)
+    for g in range(2):
+        for b in range(2):
+            P = p0 + 64 * b
+            chunks = {int(c) for c in ids[g, b] if 0 <= c < P // 64}
+            q = Q[2 * g:2 * g + 2, 64 * b:64 * (b + 1)].reshape(-1, 16)
+            for u in range(1024 // 8):
+                if u // 8 in chunks:
+                    pair = (q @ K[g, 8 * u:8 * u + 8].T).mean()
+                    assert abs(sig[g, b, u] - pair) <= 1e-12 * max(1.0, abs(pair))
+                else:
+                    assert np.isnan(sig[g, b, u])
+
+
+@pytest.mark.parametrize("m", [0, 1, 5, 24, 40])
+def test_route_groups_keeps_the_top_m_candidate_groups(m):
+    x, p0, ids, SG = _group_setup(42)
+    gids, sig = oracle.route_groups(x["Q"], SG, p0, ids, m, 2, want_scores=True)
+    for g in range(2):
+        for b in range(2):
+            cand = [u for u in range(1024 // 8) if not np.isnan(sig[g, b, u])]
+            assert len(cand) == 8 * 3
+            best = sorted(cand, key=lambda u: (-sig[g, b, u], u))[:m]
+            want = sorted(best) + [-1] * (m - len(best))
+            assert gids[g, b].tolist() == want
+
+
+def test_route_groups_planted_group_is_selected():
+    x, p0, ids, SG = _group_setup(43)
+    g, b = 1, 1
+    c = int(ids[g, b][ids[g, b] >= 0][0])
+    u = 8 * c + 5                                   # one group of a routed chunk
+    qbar = x["Q"][2 * g:2 * g + 2, 64 * b:64 * (b + 1)].astype(np.float64).mean(axis=(0, 1))
+    x["K"][g, 8 * u:8 * u + 8] += (40.0 * qbar / np.linalg.norm(qbar)).astype(np.float32)
+    SG = oracle.summarize(x["K"], 8, 0, 1024 // 8)
+    gids = oracle.route_groups(x["Q"], SG, p0, ids, 2, 2)
+    assert u in gids[g, b].tolist()
+
+
+def test_route_groups_chunk_rows_are_sets():
+    x, p0, ids, SG = _group_setup(44)
+    ref = oracle.route_groups(x["Q"], SG, p0, ids, 7, 2)
+    local = (p0 // 64 + np.arange(2))[None, :, None].repeat(2, axis=0)   # the chunk at P/C
+    messy = np.concatenate([ids[:, :, ::-1], ids, np.full_like(ids, -1), local,
+                            np.full_like(ids, 10 ** 6)], axis=2)      # reversed, repeated, junk
+    np.testing.assert_array_equal(oracle.route_groups(x["Q"], SG, p0, messy, 7, 2), ref)
+
+
+def test_attend_over_all_groups_of_the_chunks_is_chunk_attention():
+    # attended sets are the same positions in the same order: exact equality
+    x, p0, ids, SG = _group_setup(45)
+    gids = oracle.route_groups(x["Q"], SG, p0, ids, 24, 2)
+    O1, l1 = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0, 64, 64)
+    O2, l2 = oracle.attend_fwd(x["Q"], x["K"], x["V"], gids, p0, 8, 64)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(l1, l2)
+    g1 = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], ids, p0, 64, 64)
+    g2 = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], gids, p0, 8, 64)
+    for a, b2 in zip(g1, g2):
+        np.testing.assert_array_equal(a, b2)
+
+
+def test_attend_groups_matches_masked_sdpa_and_autograd():
+    Hq, Hkv, D, T, n_q = 4, 2, 16, 1024, 128
+    x, p0, ids, SG = _group_setup(46)
+    gids = oracle.route_groups(x["Q"], SG, p0, ids, 7, 2)
+    O, lse = oracle.attend_fwd(x["Q"], x["K"], x["V"], gids, p0, 8, 64)
+    M = _mask_from_ids(gids, Hq, Hkv, n_q, p0, T, 8, 64)
+    O_ref, lse_ref = _sdpa_masked(x["Q"], x["K"], x["V"], M, 1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+    dQ, dK, dV = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], gids, p0, 8, 64)
+    G = Hq // Hkv
+    q = torch.tensor(x["Q"], dtype=torch.float64, requires_grad=True)
+    kk = torch.tensor(x["K"], dtype=torch.float64, requires_grad=True)
+    vv = torch.tensor(x["V"], dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q, kk.repeat_interleave(G, 0), vv.repeat_interleave(G, 0),
+        attn_mask=torch.from_numpy(M), scale=1 / math.sqrt(D))
+    (out * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(dQ, q.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dK, kk.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dV, vv.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
