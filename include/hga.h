@@ -166,6 +166,69 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K,
                           float *dV_active, void *workspace, size_t ws_bytes,
                           hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Second routing level: groups of HGA_GROUP tokens inside the chosen chunks
+ * (technical summary 2.1, group selection: the selected chunks are split into
+ * smaller groups, e.g. 8 tokens, the router keeps the best groups of the
+ * chosen chunks by their summaries, and only the exact K/V of the kept groups
+ * enter attention). Group u covers tokens [8u, 8u + 8); chunk c holds groups
+ * 8c .. 8c + 7. The local block stays a whole causal chunk.
+ * ---------------------------------------------------------------------- */
+#define HGA_GROUP 8
+
+/*
+ * hga_summarize_groups -- group summaries, the group-level analogue of
+ * hga_summarize: for kv head g and every group u of chunks
+ * tok_begin/C .. (tok_begin + n_tok)/C - 1,
+ *     group_summaries[g][u][d] = (1/8) * sum_{t = 8u}^{8u+7} K[g][t][d]   (f32)
+ *   K                device bf16 [Hkv][T_cap][D]
+ *   group_summaries  device f32 [Hkv][n_group_cap][D]; rows of other groups
+ *                    are not touched
+ *   tok_begin, n_tok multiples of C; tok_begin + n_tok <= T_cap, else
+ *                    HGA_ERR_INVALID_ARG; (tok_begin + n_tok)/8 <= n_group_cap,
+ *                    else HGA_ERR_CAPACITY
+ */
+hga_status hga_summarize_groups(const hga_config *cfg, const void *K, int64_t T_cap,
+                                int64_t tok_begin, int64_t n_tok, float *group_summaries,
+                                int64_t n_group_cap, hipStream_t stream);
+
+/*
+ * hga_route_groups -- per query block, the best groups inside the block's
+ * routed chunks. For kv head g and block b (first position P), with qbar the
+ * block mean of hga_route:
+ *     candidates = the groups of the distinct chunk ids c of chunk_ids[g][b]
+ *                  with 0 <= c < P/C (the row is a set; other entries skipped)
+ *     score_u    = qbar . group_summaries[g][u]
+ *     group_ids[g][b][:] = the min(group_top_k, #candidates) groups of highest
+ *                  score, ties to the lower group id, written ascending and
+ *                  padded with -1
+ *   chunk_ids        device int32 [Hkv][n_q/Bq][cfg->top_k] (hga_route's ids)
+ *   group_summaries  device f32 [Hkv][n_group_cap][D] (hga_summarize_groups);
+ *                    every group of a chunk c < (p0 + n_q - Bq)/C must be
+ *                    summarized: 8 * that many <= n_group_cap, else
+ *                    HGA_ERR_CAPACITY
+ *   group_top_k      0 .. 2048 (= 8 * 256, every group of the largest top_k)
+ *   group_ids        device int32 [Hkv][n_q/Bq][group_top_k]
+ *   scores_or_null   device f32 like group_ids (the fp32 score of each id,
+ *                    -inf in padding) or NULL
+ */
+hga_status hga_route_groups(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                            const float *group_summaries, int64_t n_group_cap,
+                            const int32_t *chunk_ids, int32_t group_top_k, int32_t *group_ids,
+                            float *scores_or_null, hipStream_t stream);
+
+/*
+ * hga_attend_fwd_groups -- hga_attend_fwd over routed groups: for query i of
+ * block b (first position P, position p),
+ *     A(i) = union_{u in group_ids[g][b], 0 <= u < P/8} [8u, 8u + 8)  U  [P, p]
+ * with the rest as in hga_attend_fwd (the group row is a set; group_ids
+ * [Hkv][n_q/Bq][group_top_k], group_top_k in 0 .. 2048).
+ */
+hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                 const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                 const int32_t *group_ids, int32_t group_top_k, void *O,
+                                 float *lse, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hga_status_string(hga_status status);
 

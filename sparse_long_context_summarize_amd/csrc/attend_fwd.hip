@@ -62,14 +62,39 @@ struct TileRegs {
     u32x4 p[kPieces];
 };
 
+// The loaders take the first token of a chunk tile (consecutive rows), or
+// row_tok(r), the token of tile row r (0..63), for a tile whose rows come 8 at
+// a time from its groups.
 // K group, u = thread - 256: piece j is key row 16*j + u/16, d = 8*(u%16) .. +8
-// (each load instruction reads four whole 256-B rows).
+// (each load instruction reads four 256-B rows).
 __device__ __forceinline__ void load_k(TileRegs &tr, const uint16_t *Kg, int64_t tok0)
 {
     const int u = threadIdx.x - kThreads / 2;
     const uint16_t *src = Kg + (tok0 + (u >> 4)) * kD + (u & 15) * 8;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + 16 * j * kD);
+}
+
+// Group tiles: the K group thread takes rows r0 + 2*j of one 8-row group,
+// r0 = 8*(u/32) + (u/16)%2, so a single row_tok call serves its four pieces
+// (each load instruction still reads four 256-B rows).
+template <typename RowTok>
+__device__ __forceinline__ void load_k(TileRegs &tr, const uint16_t *Kg, RowTok row_tok)
+{
+    const int u = threadIdx.x - kThreads / 2;
+    const int r0 = 8 * (u >> 5) + ((u >> 4) & 1);
+    const uint16_t *src = Kg + row_tok(r0) * kD + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + 2 * j * kD);
+}
+
+__device__ __forceinline__ void store_k_grp(const TileRegs &tr, uint16_t *Ks)
+{
+    const int u = threadIdx.x - kThreads / 2;
+    const int r0 = 8 * (u >> 5) + ((u >> 4) & 1);
+    uint16_t *dst = Ks + r0 * kKStride + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) *(u32x4 *)(dst + 2 * j * kKStride) = tr.p[j];
 }
 
 __device__ __forceinline__ void store_k(const TileRegs &tr, uint16_t *Ks)
@@ -87,6 +112,17 @@ __device__ __forceinline__ void load_v(TileRegs &tr, const uint16_t *Vg, int64_t
     const int u = threadIdx.x, lane = u & 63;
     const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
     const uint16_t *src = Vg + (tok0 + 4 * kg) * kD + dp * 8;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + j * kD);
+}
+
+// (rows 4*kg .. 4*kg+3 lie in one 8-row group, so one row_tok call serves them)
+template <typename RowTok>
+__device__ __forceinline__ void load_v(TileRegs &tr, const uint16_t *Vg, RowTok row_tok)
+{
+    const int u = threadIdx.x, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+    const uint16_t *src = Vg + row_tok(4 * kg) * kD + dp * 8;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + j * kD);
 }
@@ -124,7 +160,11 @@ __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vt, int dt, int ks,
     return *(const bf16x8 *)(Vt + (32 * dt + (lane & 31)) * kVtStride + 16 * ks + 8 * (lane >> 5));
 }
 
-template <int G>
+// kUnit = kC: ids are chunk ids, one tile per routed chunk. kUnit = kGroup:
+// ids are 8-token group ids (the second routing level); each routed tile is
+// gathered from 8 groups, and the last one masks the keys of its missing
+// groups when their number is not a multiple of 8.
+template <int G, int kUnit>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -136,7 +176,7 @@ void attend_fwd_kernel(
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVtTile];
-    __shared__ int list[kMaxTopK + 1];
+    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 1];
     __shared__ int list_n;
 
     const int tid = threadIdx.x;
@@ -152,14 +192,35 @@ void attend_fwd_kernel(
     const uint16_t *Kg = K + g * T_cap * kD;
     const uint16_t *Vg = V + g * T_cap * kD;
 
-    // Chunk list: valid routed ids (0 <= c < P/C) in order, repeats dropped,
-    // then the local block.
+    // Unit list: valid routed ids (0 <= u < P/kUnit) in order, repeats
+    // dropped, then the local chunk.
     if (wave == 0) {
-        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, local_chunk, list);
-        if (lane == 0) list_n = n;
+        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, P / kUnit, list);
+        if (lane == 0) {
+            list[n - 1] = (int)local_chunk;
+            list_n = n;
+        }
     }
     __syncthreads();
-    const int n_tiles = list_n;
+    const int n_units = list_n - 1;                 // routed units
+    const int n_tiles = (kUnit == kC ? n_units : (n_units + 7) / 8) + 1;
+    // token of row r of tile t (tiles past the end repeat the last one)
+    const int *lst = list;
+    auto rows_of = [&](int t) __attribute__((always_inline)) {
+        const int tt = min(t, n_tiles - 1);
+        if constexpr (kUnit == kC) {
+            return (int64_t)lst[tt] * kC;          // a chunk tile: its first token
+        } else {
+            const bool local = tt == n_tiles - 1;
+            const int64_t lbase = (int64_t)lst[n_units] * kC;
+            const int g0 = 8 * tt, glast = n_units - 1;
+            return [=](int r) __attribute__((always_inline)) -> int64_t {
+                if (local) return lbase + r;
+                // padding rows of the last routed tile repeat its last group (masked)
+                return (int64_t)lst[min(g0 + (r >> 3), glast)] * kGroup + (r & 7);
+            };
+        }
+    };
 
     // Group A = waves 0-3, group B = waves 4-7: wave w computes head
     // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
@@ -177,16 +238,15 @@ void attend_fwd_kernel(
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
     }
-    auto tile_tok = [&](int t) __attribute__((always_inline)) { return (int64_t)list[min(t, n_tiles - 1)] * kC; };
     TileRegs r0, r1;
     if (grp == 0) {
-        load_v(r0, Vg, tile_tok(0));
-        load_v(r1, Vg, tile_tok(1));
+        load_v(r0, Vg, rows_of(0));
+        load_v(r1, Vg, rows_of(1));
     } else {
-        load_k(r0, Kg, tile_tok(0));
-        load_k(r1, Kg, tile_tok(1));
-        store_k(r0, Ks[0]);
-        load_k(r0, Kg, tile_tok(2));
+        load_k(r0, Kg, rows_of(0));
+        load_k(r1, Kg, rows_of(1));
+        if constexpr (kUnit == kC) store_k(r0, Ks[0]); else store_k_grp(r0, Ks[0]);
+        load_k(r0, Kg, rows_of(2));
     }
     // The Q loads were issued first: let them land here (the eight newer tile
     // loads may stay in flight), so no wait for them is left in the loop.
@@ -226,12 +286,14 @@ void attend_fwd_kernel(
 #pragma unroll
                 for (int j = 0; j < 16; ++j) s[kt][j] = 0.f;
         }
+        // group tiles hold a little more addressing state: a shorter lookahead
+        constexpr int kLk = kUnit == kC ? kLook : kLook - 3;
         bf16x8 op[NS];
 #pragma unroll
-        for (int i = 0; i < kLook; ++i) op[i] = read(i);
+        for (int i = 0; i < kLk; ++i) op[i] = read(i);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            if (i + kLook < NS) op[i + kLook] = read(i + kLook);
+            if (i + kLk < NS) op[i + kLk] = read(i + kLk);
             const int j = idx(i);
             if (is_s(i))
                 s[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i], qf[j >> 1], s[j & 1], 0, 0, 0);
@@ -252,6 +314,15 @@ void attend_fwd_kernel(
                 for (int j = 0; j < 16; ++j) {
                     const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
                     if (key > 32 * qt + col) s[kt][j] = -INFINITY;
+                }
+        } else if (kUnit != kC && t == n_tiles - 2 && (n_units & 7) != 0) {
+            const int n_keys = kGroup * (n_units & 7);      // keys of the tile's groups
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
+                    if (key >= n_keys) s[kt][j] = -INFINITY;
                 }
         }
         // (four independent max / sum chains keep the VALU pipeline full)
@@ -288,11 +359,13 @@ void attend_fwd_kernel(
     // to LDS, prefetch V(t+2). K group, tile t: K(t+2) to LDS, prefetch K(t+4).
     auto duty_v = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
         store_v(rr, Vs[t & 1]);
-        load_v(rr, Vg, tile_tok(t + 2));
+        load_v(rr, Vg, rows_of(t + 2));
     };
     auto duty_k = [&](int t, TileRegs &rr) __attribute__((always_inline)) {
-        if (t + 2 < n_tiles) store_k(rr, Ks[t & 1]);
-        load_k(rr, Kg, tile_tok(t + 4));
+        if (t + 2 < n_tiles) {
+            if constexpr (kUnit == kC) store_k(rr, Ks[t & 1]); else store_k_grp(rr, Ks[t & 1]);
+        }
+        load_k(rr, Kg, rows_of(t + 4));
     };
     const std::true_type Y{};
     const std::false_type N{};
@@ -381,7 +454,7 @@ void attend_fwd_kernel(
         lse[row] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
-template <int G>
+template <int G, int kUnit>
 hipError_t launch_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                     int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
                     const int32_t *ids, int32_t k, float scale, uint16_t *O,
@@ -390,10 +463,26 @@ hipError_t launch_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(attend_fwd_kernel<G>, dim3((unsigned)(n_blocks * Hkv * NHG)),
+    hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * NHG)),
                        dim3(kThreads), 0, stream, Q, K, V, n_q, Hkv, T_cap, p0, ids, k,
                        scale_log2, O, lse);
     return hipGetLastError();
+}
+
+template <int kUnit>
+hipError_t launch_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                       int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
+                       const int32_t *ids, int32_t k, float scale, uint16_t *O, float *lse,
+                       hipStream_t stream)
+{
+    if (n_q == 0) return hipSuccess;
+    switch (Hq / Hkv) {
+    case 1: return launch_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    case 2: return launch_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    case 4: return launch_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    case 8: return launch_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -404,14 +493,17 @@ hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const int32_t *ids, int32_t k, float scale,
                              uint16_t *O, float *lse, hipStream_t stream)
 {
-    if (n_q == 0) return hipSuccess;
-    switch (Hq / Hkv) {
-    case 1: return launch_g<1>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 2: return launch_g<2>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 4: return launch_g<4>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 8: return launch_g<8>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+}
+
+hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
+                                    const uint16_t *V, int64_t Hq, int64_t Hkv,
+                                    int64_t T_cap, int64_t p0, int64_t n_q,
+                                    const int32_t *gids, int32_t m, float scale,
+                                    uint16_t *O, float *lse, hipStream_t stream)
+{
+    return launch_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, scale, O, lse,
+                               stream);
 }
 
 }  // namespace hga

@@ -178,6 +178,86 @@ hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, c
                       "hga_attend_fwd launch");
 }
 
+hga_status hga_summarize_groups(const hga_config *cfg, const void *K, int64_t T_cap,
+                                int64_t tok_begin, int64_t n_tok, float *group_summaries,
+                                int64_t n_group_cap, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    if (tok_begin < 0 || n_tok < 0 || T_cap < 0 || n_group_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative size or position");
+    if (tok_begin % hga::kC != 0 || n_tok % hga::kC != 0)
+        return fail(HGA_ERR_INVALID_ARG, "tok_begin (%lld) and n_tok (%lld) must be multiples of %d",
+                    (long long)tok_begin, (long long)n_tok, hga::kC);
+    if (tok_begin + n_tok > T_cap)
+        return fail(HGA_ERR_INVALID_ARG, "tok_begin + n_tok (%lld) exceeds T_cap (%lld)",
+                    (long long)(tok_begin + n_tok), (long long)T_cap);
+    const int64_t c_begin = tok_begin / hga::kC, c_end = (tok_begin + n_tok) / hga::kC;
+    if ((tok_begin + n_tok) / hga::kGroup > n_group_cap)
+        return fail(HGA_ERR_CAPACITY, "group summary buffer holds %lld groups, %lld needed",
+                    (long long)n_group_cap, (long long)((tok_begin + n_tok) / hga::kGroup));
+    if (n_tok == 0) return HGA_OK;
+    if (!K || !group_summaries) return fail(HGA_ERR_INVALID_ARG, "K or group_summaries is NULL");
+    return hip_status(hga::launch_summarize_groups((const uint16_t *)K, cfg->n_kv_heads, T_cap,
+                                                   c_begin, c_end, group_summaries, n_group_cap,
+                                                   stream),
+                      "hga_summarize_groups launch");
+}
+
+hga_status hga_route_groups(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                            const float *group_summaries, int64_t n_group_cap,
+                            const int32_t *chunk_ids, int32_t group_top_k, int32_t *group_ids,
+                            float *scores_or_null, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, 0, false);
+    if (st != HGA_OK) return st;
+    if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
+        return fail(HGA_ERR_INVALID_ARG, "group_top_k must be in [0, %d] (got %d)",
+                    hga::kMaxGroupTopK, group_top_k);
+    if (n_group_cap < 0) return fail(HGA_ERR_INVALID_ARG, "negative group count");
+    if (n_q == 0 || group_top_k == 0) return HGA_OK;
+    // every group of a chunk a block may route to (c < P/C) must be in the buffer
+    const int64_t need = ((p0 + n_q - hga::kC) / hga::kC) * (hga::kC / hga::kGroup);
+    if (cfg->top_k > 0 && need > n_group_cap)
+        return fail(HGA_ERR_CAPACITY, "the last query block may route to %lld groups, the buffer holds %lld",
+                    (long long)need, (long long)n_group_cap);
+    if (!Q || !group_ids || (cfg->top_k > 0 && (!chunk_ids || !group_summaries)))
+        return fail(HGA_ERR_INVALID_ARG, "Q, chunk_ids, group_summaries or group_ids is NULL");
+    return hip_status(hga::launch_route_groups((const uint16_t *)Q, cfg->n_q_heads,
+                                               cfg->n_kv_heads, p0, n_q, group_summaries,
+                                               n_group_cap, chunk_ids, cfg->top_k, group_top_k,
+                                               group_ids, scores_or_null, stream),
+                      "hga_route_groups launch");
+}
+
+hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                 const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                 const int32_t *group_ids, int32_t group_top_k, void *O,
+                                 float *lse, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
+        return fail(HGA_ERR_INVALID_ARG, "group_top_k must be in [0, %d] (got %d)",
+                    hga::kMaxGroupTopK, group_top_k);
+    if (n_q == 0) return HGA_OK;
+    if (!Q || !K || !V || !O || !lse || (group_top_k > 0 && !group_ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    return hip_status(hga::launch_attend_fwd_groups((const uint16_t *)Q, (const uint16_t *)K,
+                                                    (const uint16_t *)V, cfg->n_q_heads,
+                                                    cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
+                                                    group_top_k, effective_scale(cfg),
+                                                    (uint16_t *)O, lse, stream),
+                      "hga_attend_fwd_groups launch");
+}
+
 size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)
 {
     if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;

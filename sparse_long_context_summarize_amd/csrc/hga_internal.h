@@ -12,6 +12,8 @@ namespace hga {
 constexpr int kD = 128;      // head dim
 constexpr int kC = 64;       // chunk length == query block length
 constexpr int kMaxTopK = 256;
+constexpr int kGroup = 8;                  // tokens per group (second routing level)
+constexpr int kMaxGroupTopK = kMaxTopK * (64 / kGroup);   // every group of kMaxTopK chunks
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -92,15 +94,30 @@ hipError_t launch_summarize(const uint16_t *K, int64_t Hkv, int64_t T_cap,
                             int64_t c_begin, int64_t c_end, float *S,
                             int64_t n_cap, hipStream_t stream);
 
+hipError_t launch_summarize_groups(const uint16_t *K, int64_t Hkv, int64_t T_cap,
+                                   int64_t c_begin, int64_t c_end, float *SG,
+                                   int64_t n_gcap, hipStream_t stream);
+
 hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                         int64_t n_q, const float *S, int64_t n_cap, int32_t k,
                         int32_t *ids, float *scores, hipStream_t stream);
+
+hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
+                               int64_t n_q, const float *SG, int64_t n_gcap,
+                               const int32_t *chunk_ids, int32_t kc, int32_t m,
+                               int32_t *gids, float *scores, hipStream_t stream);
 
 hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
                              const int32_t *ids, int32_t k, float scale,
                              uint16_t *O, float *lse, hipStream_t stream);
+
+hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
+                                    const uint16_t *V, int64_t Hq, int64_t Hkv,
+                                    int64_t T_cap, int64_t p0, int64_t n_q,
+                                    const int32_t *gids, int32_t m, float scale,
+                                    uint16_t *O, float *lse, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
 

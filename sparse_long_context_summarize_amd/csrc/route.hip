@@ -130,13 +130,141 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-template <int G, int NI>
+// Wave-level top-k of keys[0..nE) (LDS), nE <= NI*64, by (key desc, candidate
+// index asc): one wave holds every key in registers (candidate c = it*64 +
+// lane), finds the k-th largest key bit by bit from ballot counts (stopping
+// as soon as exactly k keys reach the threshold being built), takes ties at
+// that key from the lowest candidates, and writes id_of(c) of the chosen
+// candidates in ascending candidate order (ballot + mbcnt compaction) to
+// out[], their scores to sout[] (if not null), padding both to k. Empty slots
+// hold key 0, below every finite score's key (>= 0x00800000) and every
+// threshold tried (>= 1), so no test needs a bounds check. Every lane of the
+// wave must call it.
+template <int NI, typename IdOf>
+__device__ __forceinline__ void select_top_k_reg(const uint32_t *keys, int nE, int k,
+                                                 IdOf id_of, int32_t *out, float *sout)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t key[NI];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+        const int c = it * 64 + lane;
+        key[it] = (c < nE) ? keys[c] : 0u;
+    }
+    int n_sel;
+    if (nE <= k) {
+        n_sel = nE;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const int c = it * 64 + lane;
+            if (c < nE) {
+                out[c] = id_of(c);
+                if (sout) sout[c] = key_to_score(key[it]);
+            }
+        }
+    } else {
+        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            mx = max(mx, key[it]);
+            mn = min(mn, key[it] ? key[it] : 0xFFFFFFFFu);
+        }
+        mx = wave_max_u32(mx);
+        mn = wave_min_u32(mn);
+        // Bits above the highest bit in which the keys differ are shared.
+        const uint32_t diff = mx ^ mn;
+        const int top = diff ? 31 - __builtin_clz(diff) : -1;
+        uint32_t T = (top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)));
+        // Largest T with #{key >= T} >= k, one bit at a time; once exactly k
+        // keys reach a candidate threshold they are the k largest.
+        for (int bit = top; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
+            if (cnt >= k) T = cand;
+            if (cnt == k) break;
+        }
+        int n_gt = 0;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));
+        const int need = k - n_gt;          // equal keys to take, lowest candidates first
+        int eq_seen = 0, pos = 0;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const bool eq = key[it] == T;
+            const uint64_t em = __ballot(eq);
+            const bool take = key[it] > T || (eq && eq_seen + lanes_below(em) < need);
+            eq_seen += __popcll(em);
+            const uint64_t sm = __ballot(take);
+            if (take) {
+                const int r = pos + lanes_below(sm);
+                out[r] = id_of(it * 64 + lane);
+                if (sout) sout[r] = key_to_score(key[it]);
+            }
+            pos += __popcll(sm);
+        }
+        n_sel = pos;
+    }
+    for (int r = n_sel + lane; r < k; r += 64) {
+        out[r] = -1;
+        if (sout) sout[r] = -INFINITY;
+    }
+}
+
+
+// The distinct valid chunks (0 <= c < limit) of a chunk row, ascending, into
+// chl; returns their number. A router-made row (ascending, distinct) passes
+// one neighbour check; any other row has its repeats dropped (first kept) and
+// is rank-sorted through tmp (k entries). One wave calls it.
+__device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64_t limit,
+                                                int *chl, int *tmp)
+{
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int base = 0; base < k; base += 64) {
+        const int r = base + lane;
+        const int c = (r < k) ? row[r] : -1;
+        const bool ok = c >= 0 && (int64_t)c < limit;
+        const uint64_t m = __ballot(ok);
+        if (ok) chl[cnt + lanes_below(m)] = c;
+        cnt += __popcll(m);
+    }
+    bool unsorted = false;
+    for (int i = 1 + lane; i < cnt; i += 64) unsorted |= chl[i] <= chl[i - 1];
+    if (__ballot(unsorted) == 0) return cnt;
+    int n = 0;
+    for (int base = 0; base < cnt; base += 64) {
+        const int i = base + lane;
+        const int c = (i < cnt) ? chl[i] : -1;
+        bool keep = i < cnt;
+        for (int j = 0; j < base + 64 && j < cnt; ++j)
+            if (j < i && chl[j] == c) keep = false;
+        const uint64_t m = __ballot(keep);
+        if (keep) tmp[n + lanes_below(m)] = c;
+        n += __popcll(m);
+    }
+    for (int i = lane; i < n; i += 64) {
+        const int v = tmp[i];
+        int r = 0;
+        for (int j = 0; j < n; ++j) r += tmp[j] < v;
+        chl[r] = v;
+    }
+    return n;
+}
+
+// kGroups = false: chunk routing, candidates every chunk c < P/C, rows of S.
+// kGroups = true: group routing (second level), candidates the 8 groups of
+// each distinct valid chunk of chunk_ids[g][b], in ascending group order, rows
+// of the group summaries S; k is then the group budget.
+template <int G, int NI, bool kGroups>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
     const float *__restrict__ S, int64_t n_cap, int k,
+    const int32_t *__restrict__ chunk_ids, int kc,
     int32_t *__restrict__ ids, float *__restrict__ scores)
 {
-    extern __shared__ uint32_t keys[];          // [n_eligible of this block]
+    extern __shared__ uint32_t keys[];          // [candidates of this block]
     __shared__ float part[16][kD];
     __shared__ float qbar[kD];
     __shared__ int surv[kRouteWaves][kMaxTopK];
@@ -144,6 +272,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     __shared__ uint32_t cand_key[kRouteWaves * kMaxTopK];
     __shared__ int cand_pos[kRouteWaves * kMaxTopK];
     __shared__ int chosen[kMaxTopK];
+    __shared__ int chl[kGroups ? kMaxTopK : 1];
+    __shared__ int n_ch_s;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -152,7 +282,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int64_t g = blockIdx.x % Hkv;
     const int64_t b = blockIdx.x / Hkv;
     const int64_t P = p0 + b * kC;
-    const int nE = (int)(P / kC);
+    int nE = (int)(P / kC);
+    if (kGroups) {
+        // 0. the block's distinct valid routed chunks, ascending
+        if (wave == 0) {
+            const int n = sorted_chunk_set(chunk_ids + (g * n_blocks + b) * kc, kc, P / kC,
+                                           chl, (int *)keys);
+            if (lane == 0) n_ch_s = n;
+        }
+        __syncthreads();
+        nE = (kC / kGroup) * n_ch_s;
+    }
+    // summary row of candidate c (its chunk, or its group)
+    auto row_of = [&](int c) __attribute__((always_inline)) {
+        return kGroups ? chl[c >> 3] * (kC / kGroup) + (c & 7) : c;
+    };
 
     // Every load that does not depend on qbar is issued first: all of this
     // thread's query rows and the first batch of summary rows, so the two
@@ -166,7 +310,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             // past the end: re-read the last row (in bounds, result unused)
-            const int c = min(base + u * kRouteWaves * 4 + sub, nE - 1);
+            const int c = row_of(min(base + u * kRouteWaves * 4 + sub, nE - 1));
             slo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
             shi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
         }
@@ -236,76 +380,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t *out = ids + (g * n_blocks + b) * k;
     float *sout = scores ? scores + (g * n_blocks + b) * k : nullptr;
 
-    if (NI * 64 >= nE) {
-        // 3. one wave, keys in registers: candidate c = it*64 + lane. Empty
-        // slots hold key 0, below every finite score's key (>= 0x00800000) and
-        // below every threshold tried (>= 1), so no test needs a bounds check.
+    if (kGroups || NI * 64 >= nE) {
+        // 3. one wave, keys in registers (group routing never has more than
+        // 8 * kMaxTopK = NI * 64 candidates)
         if (wave != 0) return;
-        uint32_t key[NI];
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const int c = it * 64 + lane;
-            key[it] = (c < nE) ? keys[c] : 0u;
-        }
-        int n_sel;
-        if (nE <= k) {
-            n_sel = nE;
-#pragma unroll
-            for (int it = 0; it < NI; ++it) {
-                const int c = it * 64 + lane;
-                if (c < nE) {
-                    out[c] = c;
-                    if (sout) sout[c] = key_to_score(key[it]);
-                }
-            }
-        } else {
-            uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-#pragma unroll
-            for (int it = 0; it < NI; ++it) {
-                mx = max(mx, key[it]);
-                mn = min(mn, key[it] ? key[it] : 0xFFFFFFFFu);
-            }
-            mx = wave_max_u32(mx);
-            mn = wave_min_u32(mn);
-            // Bits above the highest bit in which the keys differ are shared.
-            const uint32_t diff = mx ^ mn;
-            const int top = diff ? 31 - __builtin_clz(diff) : -1;
-            uint32_t T = (top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)));
-            // Largest T with #{key >= T} >= k, one bit at a time (stopping
-            // early once exactly k keys reach the candidate, as above).
-            for (int bit = top; bit >= 0; --bit) {
-                const uint32_t cand = T | (1u << bit);
-                int cnt = 0;
-#pragma unroll
-                for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
-                if (cnt >= k) T = cand;
-                if (cnt == k) break;
-            }
-            int n_gt = 0;
-#pragma unroll
-            for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));
-            const int need = k - n_gt;          // equal keys to take, lowest ids first
-            int eq_seen = 0, pos = 0;
-#pragma unroll
-            for (int it = 0; it < NI; ++it) {
-                const bool eq = key[it] == T;
-                const uint64_t em = __ballot(eq);
-                const bool take = key[it] > T || (eq && eq_seen + lanes_below(em) < need);
-                eq_seen += __popcll(em);
-                const uint64_t sm = __ballot(take);
-                if (take) {
-                    const int r = pos + lanes_below(sm);
-                    out[r] = it * 64 + lane;
-                    if (sout) sout[r] = key_to_score(key[it]);
-                }
-                pos += __popcll(sm);
-            }
-            n_sel = pos;
-        }
-        for (int r = n_sel + lane; r < k; r += 64) {
-            out[r] = -1;
-            if (sout) sout[r] = -INFINITY;
-        }
+        select_top_k_reg<NI>(keys, nE, k, row_of, out, sout);
         return;
     }
 
@@ -343,35 +422,59 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
-template <int G, int NI>
+template <int G, int NI, bool kGroups>
 hipError_t launch_route_gn(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
-                           const float *S, int64_t n_cap, int32_t k, int32_t *ids,
-                           float *scores, size_t shmem, hipStream_t stream)
+                           const float *S, int64_t n_cap, int32_t k, const int32_t *chunk_ids,
+                           int32_t kc, int32_t *ids, float *scores, size_t shmem,
+                           hipStream_t stream)
 {
     const int64_t n_blocks = n_q / kC;
-    hipLaunchKernelGGL((route_kernel<G, NI>), dim3((unsigned)(n_blocks * Hkv)),
+    hipLaunchKernelGGL((route_kernel<G, NI, kGroups>), dim3((unsigned)(n_blocks * Hkv)),
                        dim3(kRouteThreads), shmem, stream, Q, n_q, Hkv, p0, S, n_cap, k,
-                       ids, scores);
+                       chunk_ids, kc, ids, scores);
     return hipGetLastError();
 }
 
 // Keys per lane of the register selection: the smallest class that holds the
-// last (largest) block's candidates; beyond 2048 the LDS path takes over.
-template <int G>
+// largest candidate count; beyond 2048 (chunk routing only) the LDS path
+// takes over.
+template <int G, bool kGroups>
 hipError_t launch_route_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
-                          const float *S, int64_t n_cap, int32_t k, int32_t *ids,
-                          float *scores, hipStream_t stream)
+                          const float *S, int64_t n_cap, int32_t k, const int32_t *chunk_ids,
+                          int32_t kc, int32_t *ids, float *scores, hipStream_t stream)
 {
-    const int64_t max_eligible = (p0 + n_q - kC) / kC;
-    const size_t shmem = (size_t)(max_eligible > 0 ? max_eligible : 1) * sizeof(uint32_t);
+    const int64_t max_chunks = (p0 + n_q - kC) / kC;
+    const int64_t max_eligible = kGroups ? (kC / kGroup) * (max_chunks < kc ? max_chunks : kc)
+                                         : max_chunks;
+    // chunk routing keeps the keys; group routing also sorts up to kc ids there
+    int64_t slots = max_eligible > kc ? max_eligible : (kGroups ? kc : max_eligible);
+    const size_t shmem = (size_t)(slots > 0 ? slots : 1) * sizeof(uint32_t);
     if (max_eligible <= 4 * 64)
-        return launch_route_gn<G, 4>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
+        return launch_route_gn<G, 4, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
+                                              scores, shmem, stream);
     if (max_eligible <= 8 * 64)
-        return launch_route_gn<G, 8>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
+        return launch_route_gn<G, 8, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
+                                              scores, shmem, stream);
     if (max_eligible <= 16 * 64)
-        return launch_route_gn<G, 16>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem, stream);
-    return launch_route_gn<G, kMaxRegKeys>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, shmem,
-                                           stream);
+        return launch_route_gn<G, 16, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
+                                               scores, shmem, stream);
+    return launch_route_gn<G, kMaxRegKeys, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids,
+                                                    kc, ids, scores, shmem, stream);
+}
+
+template <bool kGroups>
+hipError_t launch_route_any(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
+                            int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                            const int32_t *chunk_ids, int32_t kc, int32_t *ids, float *scores,
+                            hipStream_t stream)
+{
+    switch (Hq / Hkv) {
+    case 1: return launch_route_g<1, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
+    case 2: return launch_route_g<2, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
+    case 4: return launch_route_g<4, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
+    case 8: return launch_route_g<8, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -381,13 +484,18 @@ hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                         int32_t *ids, float *scores, hipStream_t stream)
 {
     if (n_q == 0 || k == 0) return hipSuccess;
-    switch (Hq / Hkv) {
-    case 1: return launch_route_g<1>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, stream);
-    case 2: return launch_route_g<2>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, stream);
-    case 4: return launch_route_g<4>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, stream);
-    case 8: return launch_route_g<8>(Q, Hkv, p0, n_q, S, n_cap, k, ids, scores, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_route_any<false>(Q, Hq, Hkv, p0, n_q, S, n_cap, k, nullptr, 0, ids, scores,
+                                   stream);
+}
+
+hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
+                               int64_t n_q, const float *SG, int64_t n_gcap,
+                               const int32_t *chunk_ids, int32_t kc, int32_t m,
+                               int32_t *gids, float *scores, hipStream_t stream)
+{
+    if (n_q == 0 || m == 0) return hipSuccess;
+    return launch_route_any<true>(Q, Hq, Hkv, p0, n_q, SG, n_gcap, m, chunk_ids, kc, gids,
+                                  scores, stream);
 }
 
 }  // namespace hga

@@ -23,7 +23,9 @@ HGA_BF16 = 0
 
 EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
+            "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
             "hga_status_string", "hga_last_error", "hga_version")
+HGA_GROUP = 8
 
 
 class hga_config(ctypes.Structure):
@@ -70,7 +72,13 @@ def lib() -> ctypes.CDLL:
     L.hga_attend_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.hga_attend_bwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-    for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd"):
+    L.hga_summarize_groups.argtypes = [_cfgp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
+    L.hga_route_groups.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _vp, ctypes.c_int32,
+                                   _vp, _vp, _vp]
+    L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
+                                        ctypes.c_int32, _vp, _vp, _vp]
+    for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
+               "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
@@ -159,8 +167,40 @@ def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV
             _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream))
 
 
+def _m_summarize_groups(cfg: hga_config, K, tok_begin: int, n_tok: int, group_summaries,
+                        stream=None):
+    return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), K.shape[1], tok_begin, n_tok,
+            _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
+            _stream(stream))
+
+
+def _m_route_groups(cfg: hga_config, Q, p0: int, group_summaries, chunk_ids, group_ids,
+                    scores=None, stream=None):
+    if group_ids.dim() != 3:
+        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
+            _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
+            _dev(chunk_ids, "chunk_ids", torch.int32), group_ids.shape[2],
+            _dev(group_ids, "group_ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _stream(stream))
+
+
+def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, stream=None):
+    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16))
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    if group_ids.dim() != 3:
+        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
+            _dev(group_ids, "group_ids", torch.int32), group_ids.shape[2],
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
+
+
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
-            "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd}
+            "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
+            "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
+            "hga_attend_fwd_groups": _m_attend_fwd_groups}
 
 
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
@@ -195,6 +235,30 @@ def hga_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, d
     """dQ f32 [Hq][n_q][D]; dK, dV f32 [Hkv][n_q][D] (active keys) are written."""
     _check("hga_attend_bwd", lib().hga_attend_bwd(
         *_m_attend_bwd(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, workspace, stream)))
+
+
+def hga_summarize_groups(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
+                         group_summaries: torch.Tensor, stream=None) -> None:
+    """K bf16 [Hkv][T_cap][D]; group_summaries f32 [Hkv][n_group_cap][D]."""
+    _check("hga_summarize_groups", lib().hga_summarize_groups(
+        *_m_summarize_groups(cfg, K, tok_begin, n_tok, group_summaries, stream)))
+
+
+def hga_route_groups(cfg: hga_config, Q: torch.Tensor, p0: int, group_summaries: torch.Tensor,
+                     chunk_ids: torch.Tensor, group_ids: torch.Tensor,
+                     scores: torch.Tensor | None = None, stream=None) -> None:
+    """chunk_ids int32 [Hkv][n_q/64][top_k] (from hga_route); group_ids int32
+    [Hkv][n_q/64][group_top_k] is written (group_top_k = its last dimension)."""
+    _check("hga_route_groups", lib().hga_route_groups(
+        *_m_route_groups(cfg, Q, p0, group_summaries, chunk_ids, group_ids, scores, stream)))
+
+
+def hga_attend_fwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                          p0: int, group_ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
+                          stream=None) -> None:
+    """Attention over routed 8-token groups plus the causal local block."""
+    _check("hga_attend_fwd_groups", lib().hga_attend_fwd_groups(
+        *_m_attend_fwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, stream)))
 
 
 def prepare(name: str, *args, **kwargs):

@@ -44,6 +44,7 @@ class Workload:
     C: int = 64      # chunk length
     Bq: int = 64     # query block length
     k: int = 16      # routed chunks per block
+    m: int = 0       # routed 8-token groups per block (0: whole chunks)
     bf16: bool = True
     with_dO: bool = False
 
@@ -68,6 +69,9 @@ LAYER16K = Workload("qwen3-8b-layer-16k", seed=1, Hq=32, Hkv=8, D=128,
 # Long-context evaluation shape, 4096 active queries over 126976 history, top-32.
 LAYER128K = Workload("qwen3-8b-layer-128k", seed=2, Hq=32, Hkv=8, D=128,
                      p0=126976, n_q=4096, T=131072, k=32)
+# The 16K layer with the second routing level: of the 16 routed chunks (128
+# groups of 8 tokens) each block keeps its best 64 groups, half the tokens.
+LAYER16K_GROUPS = LAYER16K.replace(name="qwen3-8b-layer-16k-groups", m=64)
 # Segment-wise backward at the 16K layer shape.
 BWD16K = Workload("qwen3-8b-bwd-16k", seed=4, Hq=32, Hkv=8, D=128,
                   p0=14336, n_q=2048, T=16384, k=16, with_dO=True)

@@ -91,3 +91,40 @@ def summary_bound(K: np.ndarray, c_begin: int, c_end: int, C: int = 64) -> np.nd
         a = np.abs(K[g, c_begin * C:c_end * C]).reshape(c_end - c_begin, C, K.shape[2])
         out[g] = a.mean(axis=1, dtype=np.float64)
     return (C - 1) * 2.0 ** -24 * out * 1.0001 + 2.0 ** -24 * out
+
+
+def group_candidates(chunk_row: np.ndarray, P: int, C: int = 64, U: int = 8) -> np.ndarray:
+    """Candidate groups of one block: the U-token groups of the distinct chunk
+    ids c of its routed row with 0 <= c < P/C, ascending."""
+    ch = sorted({int(c) for c in chunk_row if 0 <= c < P // C})
+    return np.array([c * (C // U) + j for c in ch for j in range(C // U)], dtype=np.int64)
+
+
+def check_group_ids(gpu_gids: np.ndarray, ref_gids: np.ndarray, sigma: np.ndarray,
+                    chunk_ids: np.ndarray, p0: int, C: int = 64, Bq: int = 64, U: int = 8,
+                    where: str = "") -> int:
+    """The id rule of check_ids at the group level: the candidates of a block
+    are the groups of its routed chunks (group_candidates), M is the largest
+    |score| among them. Returns the number of rows that differ within the gap."""
+    assert gpu_gids.shape == ref_gids.shape, (gpu_gids.shape, ref_gids.shape)
+    Hkv, nb, m = gpu_gids.shape
+    near_ties = 0
+    for g in range(Hkv):
+        for b in range(nb):
+            a, r = gpu_gids[g, b], ref_gids[g, b]
+            cand = group_candidates(chunk_ids[g, b], p0 + b * Bq, C, U)
+            na, nr = int((a >= 0).sum()), int((r >= 0).sum())
+            ctx = f"{where} head {g} block {b}: gpu {a.tolist()} oracle {r.tolist()}"
+            assert na == nr == min(m, cand.size), ctx
+            assert np.all(a[na:] == -1), ctx
+            assert np.all(np.diff(a[:na]) > 0), ctx
+            assert np.all(np.isin(a[:na], cand)), ctx
+            if np.array_equal(a, r):
+                continue
+            sig = sigma[g, b, cand]
+            M = np.max(np.abs(sig))
+            kth = np.sort(sig)[::-1][nr - 1]
+            for u in set(a[:na].tolist()) ^ set(r[:nr].tolist()):
+                assert abs(sigma[g, b, u] - kth) <= GAP * M, (ctx, u, sigma[g, b, u], kth, M)
+            near_ties += 1
+    return near_ties

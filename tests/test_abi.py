@@ -145,3 +145,36 @@ def test_binding_rejects_host_tensors():
     S = torch.zeros(8, 1, 128)
     with pytest.raises(ValueError, match="GPU"):
         hga.hga_summarize(cfg, K, 0, 64, S)
+
+
+def test_group_entry_point_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    c = ctypes.byref(cfg)
+    s = L.hga_summarize_groups
+    assert s(c, FAKE, 16384, 32, 64, FAKE, 2048, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(c, FAKE, 16384, 0, 16384, FAKE, 2047, None) == hga.HGA_ERR_CAPACITY
+    assert "2048" in hga.hga_last_error()
+    assert s(c, None, 16384, 0, 64, FAKE, 2048, None) == hga.HGA_ERR_INVALID_ARG
+    assert s(c, FAKE, 16384, 64, 0, FAKE, 2048, None) == hga.HGA_OK
+    r = L.hga_route_groups
+    assert r(c, FAKE, 14336, 2048, FAKE, 2040, FAKE, 2049, FAKE, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert r(c, FAKE, 14336, 2048, FAKE, 2040, FAKE, -1, FAKE, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    # the last block may route to chunk 254, i.e. groups up to 2039
+    assert r(c, FAKE, 14336, 2048, FAKE, 2039, FAKE, 64, FAKE, None,
+             None) == hga.HGA_ERR_CAPACITY
+    assert r(c, FAKE, 14336, 2048, FAKE, 2040, None, 64, FAKE, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert r(c, FAKE, 14336, 2047, FAKE, 2040, FAKE, 64, FAKE, None,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert r(c, FAKE, 14336, 2048, FAKE, 2040, FAKE, 0, None, None, None) == hga.HGA_OK
+    a = L.hga_attend_fwd_groups
+    assert a(c, FAKE, FAKE, FAKE, 16384, 14336, 2048, FAKE, 2049, FAKE, FAKE,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert a(c, FAKE, FAKE, FAKE, 16384, 14336, 2048, None, 64, FAKE, FAKE,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert a(c, FAKE, FAKE, FAKE, 16383, 14336, 2048, FAKE, 64, FAKE, FAKE,
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert a(c, FAKE, FAKE, FAKE, 16384, 14336, 0, None, 64, FAKE, FAKE, None) == hga.HGA_OK
