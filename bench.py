@@ -40,8 +40,8 @@ C = 64
 # to the kernel source whose sha256 prefix is recorded; for any other source
 # the traffic is reported as null.
 MEASURED_TRAFFIC = {"source": "sparse_long_context_summarize_amd/csrc/attend_fwd.hip",
-                    "sha256_prefix": "7cee16cc15ffe102",
-                    "fetch_kib": 20910.2, "fetch_factor": 2.0,
+                    "sha256_prefix": "e3d633426ae32dbc",
+                    "fetch_kib": 20920.4, "fetch_factor": 2.0,
                     "write_kib": 16640.0, "write_factor": 1.0}
 
 
@@ -69,26 +69,52 @@ def parse():
     return ap.parse_args()
 
 
-def attend_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int) -> float:
-    """Algorithmic flops of hga_attend_fwd: 4*D per attended (query, key) pair
-    (2*D for q.k, 2*D for p*v), summed over every query of every head."""
+def _n_valid_units(ids: np.ndarray, p0: int, unit: int) -> int:
+    """Distinct ids u with 0 <= u < P/unit, summed over (kv head, block) rows."""
+    Hkv, nb, _ = ids.shape
+    n = 0
+    for b in range(nb):
+        lim = (p0 + b * C) // unit
+        for g in range(Hkv):
+            row = ids[g, b]
+            n += np.unique(row[(row >= 0) & (row < lim)]).size
+    return n
+
+
+def attend_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int, unit: int = C) -> float:
+    """Algorithmic flops of hga_attend_fwd (unit = 64, chunk ids) or
+    hga_attend_fwd_groups (unit = 8, group ids): 4*D per attended (query, key)
+    pair (2*D for q.k, 2*D for p*v), summed over every query of every head."""
     Hkv, nb, k = ids.shape
-    P = p0 + np.arange(nb) * C
-    valid = ((ids >= 0) & (ids < (P // C)[None, :, None])).sum(axis=2)      # [Hkv][nb]
-    routed_pairs = valid.sum() * C * C * G                                   # 64 queries x 64 keys
+    routed_pairs = _n_valid_units(ids, p0, unit) * unit * C * G   # unit keys x 64 queries
     local_pairs = Hkv * G * nb * (C * (C + 1) // 2)
     return 4.0 * D * float(routed_pairs + local_pairs)
 
 
-def attend_bytes(ids: np.ndarray, n_q: int, Hq: int, D: int, p0: int) -> float:
-    """Algorithmic HBM bytes of hga_attend_fwd: each (block, kv head) gathers
-    its routed chunks' and local block's K and V once (bf16), reads Q once,
-    writes O (bf16) and lse (fp32)."""
+def attend_bytes(ids: np.ndarray, n_q: int, Hq: int, D: int, p0: int, unit: int = C) -> float:
+    """Algorithmic HBM bytes of the attention call: each (block, kv head)
+    gathers its routed units' and local block's K and V once (bf16), reads Q
+    once, writes O (bf16) and lse (fp32)."""
     Hkv, nb, k = ids.shape
-    P = p0 + np.arange(nb) * C
-    valid = ((ids >= 0) & (ids < (P // C)[None, :, None])).sum(axis=2)
-    gathered = (valid.sum() + Hkv * nb) * C * D * 2 * 2
+    gathered = (_n_valid_units(ids, p0, unit) * unit + Hkv * nb * C) * D * 2 * 2
     return float(gathered + Hq * n_q * D * 2 * 2 + Hq * n_q * 4)
+
+
+def _median_ms(torch, fn, pre=None, n=10):
+    """Median HIP-event time of fn (after 3 untimed launches); pre runs before
+    each launch, outside the events."""
+    ts = []
+    for i in range(n + 3):
+        if pre is not None:
+            pre()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ts[3:])
+    return t[len(t) // 2]
 
 
 def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int) -> float:
@@ -101,7 +127,7 @@ def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int) -> float:
     for b in range(nb):
         for g in range(Hkv):
             row = ids[g, b]
-            ok = row[(row >= 0) & (row < P[b] // C)]
+            ok = np.unique(row[(row >= 0) & (row < P[b] // C)])
             a = int((ok * C >= p0).sum())
             act += a * C * C
             hist += (len(ok) - a) * C * C
@@ -263,6 +289,7 @@ def extra_timings(torch, hga, inputs, dev):
     ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg, w.n_q), dtype=torch.uint8,
                      device=dev)
     res.update(segloop_timing(torch, hga, inputs, dev))
+    res.update(group_timings(torch, hga, inputs, dev))
     res.update(attend_timings(torch, hga, inputs, dev))
     try:
         times = []
@@ -295,18 +322,7 @@ def attend_timings(torch, hga, inputs, dev):
         return torch.from_numpy(a).to(torch.bfloat16).to(dev)
 
     def med(fn, pre=None, n=10):
-        ts = []
-        for i in range(n + 3):
-            if pre is not None:
-                pre()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            ts.append((a, b))
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ts[3:])
-        return t[len(t) // 2]
+        return _median_ms(torch, fn, pre, n)
 
     for w, tag in ((inputs.LAYER128K, "layer128k"), (inputs.LAYER16K, "layer16k")):
         x = inputs.generate(w)
@@ -335,6 +351,63 @@ def attend_timings(torch, hga, inputs, dev):
             res["layer16k_attend_cold_gathered_GBps"] = abytes / (ms_cold * 1e-3) / 1e9
             del flush
         del Q, K, V, S, ids, O, lse
+    return res
+
+
+def group_timings(torch, hga, inputs, dev):
+    """The second routing level at the 16K layer (16 routed chunks, best 64
+    of their 128 groups per block): each call HIP-event timed alone (median
+    of 10), and the whole group-level forward of one layer (chunk and group
+    summaries of the active segment, both routers, group attention)."""
+    w = inputs.LAYER16K_GROUPS
+    x = inputs.generate(w)
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    Q, K, V = up(x["Q"]), up(x["K"]), up(x["V"])
+    cfg = hga.make_config(w.Hq, w.Hkv, w.k)
+    nb = w.n_q // C
+    S = torch.zeros((w.Hkv, w.T // C, w.D), device=dev)
+    SG = torch.zeros((w.Hkv, w.T // hga.HGA_GROUP, w.D), device=dev)
+    ids = torch.empty((w.Hkv, nb, w.k), dtype=torch.int32, device=dev)
+    gids = torch.empty((w.Hkv, nb, w.m), dtype=torch.int32, device=dev)
+    O = torch.empty((w.Hq, w.n_q, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.Hq, w.n_q), device=dev)
+    hga.hga_summarize(cfg, K, 0, w.T, S)
+    hga.hga_summarize_groups(cfg, K, 0, w.T, SG)
+    calls = {
+        "summarize": hga.prepare("hga_summarize", cfg, K, w.p0, w.n_q, S),
+        "summarize_groups": hga.prepare("hga_summarize_groups", cfg, K, w.p0, w.n_q, SG),
+        "route": hga.prepare("hga_route", cfg, Q, w.p0, S, w.T // C, ids),
+        "route_groups": hga.prepare("hga_route_groups", cfg, Q, w.p0, SG, ids, gids),
+        "attend_fwd_groups": hga.prepare("hga_attend_fwd_groups", cfg, Q, K, V, w.p0, gids,
+                                         O, lse),
+    }
+    for fn in calls.values():
+        fn()
+    res = {}
+    for name, fn in calls.items():
+        if name != "summarize":
+            res[f"groups16k_{name}_us"] = _median_ms(torch, fn) * 1e3
+
+    def layer():
+        for fn in calls.values():
+            fn()
+
+    ms = _median_ms(torch, layer)
+    g = gids.cpu().numpy()
+    fl = attend_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
+    ab = attend_bytes(g, w.n_q, w.Hq, w.D, w.p0, unit=hga.HGA_GROUP)
+    t_att = res["groups16k_attend_fwd_groups_us"] * 1e-6
+    res.update({
+        "groups16k_layer_fwd_us": ms * 1e3,
+        "groups16k_query_tokens_per_s": w.n_q / (ms * 1e-3),
+        "groups16k_group_top_k": w.m,
+        "groups16k_attend_algorithmic_gflop": fl / 1e9,
+        "groups16k_attend_tflops": fl / t_att / 1e12,
+        "groups16k_attend_gathered_GBps": ab / t_att / 1e9,
+    })
     return res
 
 
