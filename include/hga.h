@@ -131,6 +131,21 @@ hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
                           hipStream_t stream);
 
 /*
+ * hga_route_attend_fwd -- hga_route followed by hga_attend_fwd on its ids, in
+ * one launch where the candidates fit (each workgroup routes its own query
+ * block with the routing kernel's code, then attends): ids, scores_or_null, O
+ * and lse are bit-identical to those two calls with the same arguments, and
+ * the arguments, layouts and errors are theirs. With more than 8704
+ * candidate chunks in the last block the two kernels run one after the other
+ * (same results).
+ */
+hga_status hga_route_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
+                                const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                const float *summaries, int64_t n_chunk_cap,
+                                int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                                void *O, float *lse, hipStream_t stream);
+
+/*
  * hga_attend_bwd_workspace_bytes -- size of the device workspace that
  * hga_attend_bwd needs for n_q active queries (0 on invalid arguments).
  */

@@ -36,7 +36,7 @@
 // Workgroup w serves kv head w % Hkv: with 8 kv heads every block of one head
 // runs on the same XCD, where neighbouring blocks' overlapping chunk choices
 // hit that XCD's L2.
-#include "hga_internal.h"
+#include "route_core.h"
 
 #include <type_traits>
 
@@ -52,6 +52,8 @@ constexpr int kPieces = kC * kD * 2 * 2 / 16 / kThreads;      // 16-byte pieces 
 constexpr float kLazy = 8.0f;               // log2 growth that forces a rescale
 // s_waitcnt immediates (gfx9 encoding).
 constexpr int kWaitVm8 = 0x0F78;       // vector memory count 8, others no wait
+constexpr int kWaitLgkm0 = 0xC07F;     // LDS/scalar count 0, others no wait
+constexpr int kOStride = 136;          // output staging row: 128 bf16 + 8 pad
 constexpr int kLook = 6;                // MFMA operands read this many MFMAs ahead
 
 static_assert(kPieces == 4, "tile loader assumes 4 pieces per thread");
@@ -164,20 +166,28 @@ __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vt, int dt, int ks,
 // ids are 8-token group ids (the second routing level); each routed tile is
 // gathered from 8 groups, and the last one masks the keys of its missing
 // groups when their number is not a multiple of 8.
-template <int G, int kUnit>
+// kRouteNI = 0: ids are an input. kRouteNI > 0 (chunk tiles only): the
+// workgroup first routes its block itself with the router's own code
+// (route_block, NI = kRouteNI keys per lane), writes ids (and scores, if not
+// null) exactly as the routing kernel would, and attends over that choice;
+// S / n_cap are the chunk summaries.
+template <int G, int kUnit, int kRouteNI>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int64_t T_cap,
-    int64_t p0, const int32_t *__restrict__ ids, int k, float scale_log2,
-    uint16_t *__restrict__ O, float *__restrict__ lse)
+    int64_t p0, int32_t *__restrict__ ids, int k, float scale_log2,
+    uint16_t *__restrict__ O, float *__restrict__ lse,
+    const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores)
 {
+    static_assert(kRouteNI == 0 || kUnit == kC, "fused routing picks chunks");
     constexpr int HW = G < 4 ? G : 4;            // query heads per workgroup
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVtTile];
-    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 1];
+    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 2];
     __shared__ int list_n;
+    __shared__ __attribute__((aligned(16))) uint16_t Os[8][32 * kOStride];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -192,13 +202,88 @@ void attend_fwd_kernel(
     const uint16_t *Kg = K + g * T_cap * kD;
     const uint16_t *Vg = V + g * T_cap * kD;
 
-    // Unit list: valid routed ids (0 <= u < P/kUnit) in order, repeats
-    // dropped, then the local chunk.
-    if (wave == 0) {
-        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, P / kUnit, list);
-        if (lane == 0) {
-            list[n - 1] = (int)local_chunk;
-            list_n = n;
+    // Group A = waves 0-3, group B = waves 4-7: wave w computes head
+    // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
+    const int grp = wave >> 2;
+    const int hw = wave & 3, qt = grp;
+    const bool computes = hw < HW;
+    const int64_t h = g * G + hg * HW + hw;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    // Tile 0 is the causal local block, whose rows need no routing result:
+    // its loads go out with the Q loads, and wave 0 issues the id row's load
+    // before both (loads complete in order), so the list is ready early.
+    int32_t *id_row = ids + (g * n_blocks + b) * k;
+    const int id_first = (kRouteNI == 0 && wave == 0 && lane < k) ? id_row[lane] : -1;
+    // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
+    bf16x8 qf[8];
+    if (computes) {
+        const uint16_t *qrow = Q + (h * n_q + b * kC + 32 * qt + col) * kD + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
+    }
+    TileRegs r0, r1;
+    if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
+
+    // Unit list: the local chunk, then the valid routed ids (0 <= u <
+    // P/kUnit) in order, repeats dropped.
+    if constexpr (kRouteNI == 0) {
+        if (wave == 0) {
+            const int n = build_chunk_list(id_row, k, P / kUnit, list + 1, id_first);
+            if (lane == 0) {
+                list[0] = (int)local_chunk;
+                list_n = n;
+            }
+        }
+    } else {
+        // Route first. Its scratch lives in LDS the kernel has not used yet:
+        // the V tiles (first written after the first MFMA half-step), the K
+        // tiles (the local tile is stored after routing) and the output
+        // staging area (used in the epilogue only). With all G heads in this
+        // workgroup (G <= 4) the router reads the block's query rows from an
+        // LDS copy of the Q registers rather than from memory a second time.
+        // The chosen ids come out ascending and distinct: the list needs no
+        // clean-up.
+        static_assert(sizeof(RouteLds) <= sizeof(Vs), "router scratch must fit the V tiles");
+        static_assert(NHG > 1 || G * kC * kOStride <= (int)(sizeof(Os) / sizeof(uint16_t)),
+                      "the block's query rows must fit the staging area");
+        RouteLds &sh = *reinterpret_cast<RouteLds *>(&Vs[0][0]);
+        uint32_t *keys = reinterpret_cast<uint32_t *>(&Ks[0][0]);
+        uint16_t *qcopy = &Os[0][0];                // row r = head hw*64 + query
+        constexpr bool kQInLds = NHG == 1;
+        if constexpr (kQInLds) {
+            if (computes) {
+                uint16_t *dst = qcopy + (hw * kC + 32 * qt + col) * kOStride + 8 * half;
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) *(bf16x8 *)(dst + 16 * ks) = qf[ks];
+            }
+            __syncthreads();
+        }
+        auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {
+            if constexpr (kQInLds) {
+                return *(const u32x4 *)(qcopy + row * kOStride + dseg * 8);
+            } else {
+                const int64_t hh = g * G + row / kC;
+                const int64_t i = b * kC + row % kC;
+                return *(const u32x4 *)(Q + (hh * n_q + i) * kD + dseg * 8);
+            }
+        };
+        const bool wr = hg == 0;            // one workgroup of a unit writes the ids
+        float *sc_row = (scores && wr) ? scores + (g * n_blocks + b) * k : nullptr;
+        constexpr int kBatchR = G >= 8 ? 4 : 8;
+        const int n_sel = route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
+            sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, nullptr, 0,
+            [&](int r, int id, float sc) __attribute__((always_inline)) {
+                list[1 + r] = id;
+                if (wr) {
+                    id_row[r] = id;
+                    if (sc_row) sc_row[r] = sc;
+                }
+            });
+        if (wave == 0 && lane == 0) {
+            list[0] = (int)local_chunk;
+            list_n = n_sel + 1;
         }
     }
     __syncthreads();
@@ -211,9 +296,9 @@ void attend_fwd_kernel(
         if constexpr (kUnit == kC) {
             return (int64_t)lst[tt] * kC;          // a chunk tile: its first token
         } else {
-            const bool local = tt == n_tiles - 1;
-            const int64_t lbase = (int64_t)lst[n_units] * kC;
-            const int g0 = 8 * tt, glast = n_units - 1;
+            const bool local = tt == 0;
+            const int64_t lbase = (int64_t)lst[0] * kC;
+            const int g0 = 8 * tt - 7, glast = n_units;
             return [=](int r) __attribute__((always_inline)) -> int64_t {
                 if (local) return lbase + r;
                 // padding rows of the last routed tile repeat its last group (masked)
@@ -221,31 +306,11 @@ void attend_fwd_kernel(
             };
         }
     };
-
-    // Group A = waves 0-3, group B = waves 4-7: wave w computes head
-    // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
-    const int grp = wave >> 2;
-    const int hw = wave & 3, qt = grp;
-    const bool computes = hw < HW;
-    const int64_t h = g * G + hg * HW + hw;
-    const int col = lane & 31;
-    const int half = lane >> 5;
-
-    // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
-    bf16x8 qf[8];
-    if (computes) {
-        const uint16_t *qrow = Q + (h * n_q + b * kC + 32 * qt + col) * kD + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
-    }
-    TileRegs r0, r1;
     if (grp == 0) {
-        load_v(r0, Vg, rows_of(0));
         load_v(r1, Vg, rows_of(1));
     } else {
-        load_k(r0, Kg, rows_of(0));
         load_k(r1, Kg, rows_of(1));
-        if constexpr (kUnit == kC) store_k(r0, Ks[0]); else store_k_grp(r0, Ks[0]);
+        store_k(r0, Ks[0]);         // the local tile, loaded as consecutive rows
         load_k(r0, Kg, rows_of(2));
     }
     // The Q loads were issued first: let them land here (the eight newer tile
@@ -303,11 +368,11 @@ void attend_fwd_kernel(
         }
     };
 
-    // Softmax half-step of tile t: causal mask on the local block (the last
-    // tile), online softmax in the log2 domain with a lazy rescale, P^T to bf16.
+    // Softmax half-step of tile t: causal mask on the local block (tile 0),
+    // online softmax in the log2 domain with a lazy rescale, P^T to bf16.
     auto va = [&](int t) __attribute__((always_inline)) {
         if (!computes) return;
-        if (t == n_tiles - 1) {
+        if (t == 0) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -315,7 +380,7 @@ void attend_fwd_kernel(
                     const int key = 32 * kt + 8 * (j >> 2) + 4 * half + (j & 3);
                     if (key > 32 * qt + col) s[kt][j] = -INFINITY;
                 }
-        } else if (kUnit != kC && t == n_tiles - 2 && (n_units & 7) != 0) {
+        } else if (kUnit != kC && t == n_tiles - 1 && (n_units & 7) != 0) {
             const int n_keys = kGroup * (n_units & 7);      // keys of the tile's groups
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -436,11 +501,13 @@ void attend_fwd_kernel(
     }
 
     if (!computes) return;
-    // Normalise and store: lane holds query 32*qt + col, d = 32*dt + 8*u + 4*half + 0..3.
+    // Normalise; lane holds query 32*qt + col, d = 32*dt + 8*u + 4*half + 0..3.
+    // The wave's 32 x 128 output goes through its own LDS area so that each
+    // store instruction writes four whole 256-B rows (1 KiB contiguous)
+    // instead of 16-B pieces of 32 rows.
     const float l_tot = l_run + partner32(l_run);
     const float inv = 1.0f / l_tot;
-    const int64_t row = h * n_q + b * kC + 32 * qt + col;
-    uint16_t *orow = O + row * kD;
+    uint16_t *st = Os[wave];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -448,39 +515,57 @@ void attend_fwd_kernel(
             bf16x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][4 * u + e] * inv);
-            *(bf16x4 *)(orow + 32 * dt + 8 * u + 4 * half) = v;
+            *(bf16x4 *)(st + col * kOStride + 32 * dt + 8 * u + 4 * half) = v;
         }
+    const int64_t row0 = h * n_q + b * kC + 32 * qt;
     if (half == 0)
-        lse[row] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+        lse[row0 + col] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    // (a wave's LDS accesses complete in order: its reads see its writes)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    const int piece = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        *(u32x4 *)(O + (row0 + r) * kD + 8 * piece) =
+            *(const u32x4 *)(st + r * kOStride + 8 * piece);
+    }
 }
 
-template <int G, int kUnit>
-hipError_t launch_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
-                    int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
-                    const int32_t *ids, int32_t k, float scale, uint16_t *O,
-                    float *lse, hipStream_t stream)
+struct FwdArgs {
+    const uint16_t *Q, *K, *V;
+    int64_t Hq, Hkv, T_cap, p0, n_q;
+    int32_t *ids;
+    int32_t k;
+    float scale;
+    uint16_t *O;
+    float *lse;
+    const float *S;          // fused routing only
+    int64_t n_cap;
+    float *scores;
+};
+
+template <int G, int kUnit, int kRouteNI>
+hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int NHG = G < 4 ? 1 : G / 4;
-    const int64_t n_blocks = n_q / kC;
-    const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * NHG)),
-                       dim3(kThreads), 0, stream, Q, K, V, n_q, Hkv, T_cap, p0, ids, k,
-                       scale_log2, O, lse);
+    const int64_t n_blocks = a.n_q / kC;
+    const float scale_log2 = a.scale * 1.44269504088896340736f;
+    hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit, kRouteNI>),
+                       dim3((unsigned)(n_blocks * a.Hkv * NHG)), dim3(kThreads), 0, stream,
+                       a.Q, a.K, a.V, a.n_q, a.Hkv, a.T_cap, a.p0, a.ids, a.k, scale_log2, a.O,
+                       a.lse, a.S, a.n_cap, a.scores);
     return hipGetLastError();
 }
 
-template <int kUnit>
-hipError_t launch_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
-                       int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
-                       const int32_t *ids, int32_t k, float scale, uint16_t *O, float *lse,
-                       hipStream_t stream)
+template <int kUnit, int kRouteNI>
+hipError_t launch_unit(const FwdArgs &a, hipStream_t stream)
 {
-    if (n_q == 0) return hipSuccess;
-    switch (Hq / Hkv) {
-    case 1: return launch_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 2: return launch_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 4: return launch_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
-    case 8: return launch_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    if (a.n_q == 0) return hipSuccess;
+    switch (a.Hq / a.Hkv) {
+    case 1: return launch_g<1, kUnit, kRouteNI>(a, stream);
+    case 2: return launch_g<2, kUnit, kRouteNI>(a, stream);
+    case 4: return launch_g<4, kUnit, kRouteNI>(a, stream);
+    case 8: return launch_g<8, kUnit, kRouteNI>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -493,7 +578,9 @@ hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const int32_t *ids, int32_t k, float scale,
                              uint16_t *O, float *lse, hipStream_t stream)
 {
-    return launch_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, stream);
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(ids), k, scale, O,
+                    lse, nullptr, 0, nullptr};
+    return launch_unit<kC, 0>(a, stream);
 }
 
 hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
@@ -502,8 +589,31 @@ hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     const int32_t *gids, int32_t m, float scale,
                                     uint16_t *O, float *lse, hipStream_t stream)
 {
-    return launch_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, scale, O, lse,
-                               stream);
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(gids), m, scale, O,
+                    lse, nullptr, 0, nullptr};
+    return launch_unit<kGroup, 0>(a, stream);
+}
+
+int64_t route_attend_max_candidates()
+{
+    return (int64_t)(sizeof(uint16_t) * 2 * kKTile / sizeof(uint32_t));   // keys in the K tiles
+}
+
+hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                   int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                   int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                                   float scale, int32_t *ids, float *scores, uint16_t *O,
+                                   float *lse, hipStream_t stream)
+{
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, S, n_cap, scores};
+    if (k == 0) return launch_unit<kC, 0>(a, stream);
+    // keys per lane of the router's register selection: the smallest class
+    // that holds the largest candidate count (beyond 2048 the LDS path)
+    const int64_t max_eligible = (p0 + n_q - kC) / kC;
+    if (max_eligible <= 4 * 64) return launch_unit<kC, 4>(a, stream);
+    if (max_eligible <= 8 * 64) return launch_unit<kC, 8>(a, stream);
+    if (max_eligible <= 16 * 64) return launch_unit<kC, 16>(a, stream);
+    return launch_unit<kC, 32>(a, stream);
 }
 
 }  // namespace hga

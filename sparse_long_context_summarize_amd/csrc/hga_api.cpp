@@ -178,6 +178,57 @@ hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, c
                       "hga_attend_fwd launch");
 }
 
+hga_status hga_route_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
+                                const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                const float *summaries, int64_t n_chunk_cap,
+                                int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                                void *O, float *lse, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (n_chunks_valid < 0 || n_chunk_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative chunk count");
+    if (n_chunks_valid > n_chunk_cap)
+        return fail(HGA_ERR_CAPACITY, "n_chunks_valid (%lld) exceeds n_chunk_cap (%lld)",
+                    (long long)n_chunks_valid, (long long)n_chunk_cap);
+    if (n_q == 0) return HGA_OK;
+    const int64_t need = (p0 + n_q - hga::kC) / hga::kC;   // eligible chunks of the last block
+    if (cfg->top_k > 0) {
+        if (need > n_chunks_valid)
+            return fail(HGA_ERR_CAPACITY, "the last query block needs %lld summaries, %lld valid",
+                        (long long)need, (long long)n_chunks_valid);
+        if (need > kMaxEligible)
+            return fail(HGA_ERR_UNSUPPORTED, "more than %lld candidate chunks per block",
+                        (long long)kMaxEligible);
+    }
+    if (!Q || !K || !V || !O || !lse || (cfg->top_k > 0 && (!ids || (need > 0 && !summaries))))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const float scale = effective_scale(cfg);
+    if (cfg->top_k > 0 && need > hga::route_attend_max_candidates()) {
+        // more candidates than the fused kernel keeps in LDS: the routing
+        // kernel, then the attention kernel (the same ids, scores and outputs)
+        st = hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads,
+                                          p0, n_q, summaries, n_chunk_cap, cfg->top_k, ids,
+                                          scores_or_null, stream),
+                        "hga_route_attend_fwd route launch");
+        if (st != HGA_OK) return st;
+        return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
+                                                 (const uint16_t *)V, cfg->n_q_heads,
+                                                 cfg->n_kv_heads, T_cap, p0, n_q, ids,
+                                                 cfg->top_k, scale, (uint16_t *)O, lse, stream),
+                          "hga_route_attend_fwd attend launch");
+    }
+    return hip_status(hga::launch_route_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
+                                                   (const uint16_t *)V, cfg->n_q_heads,
+                                                   cfg->n_kv_heads, T_cap, p0, n_q, summaries,
+                                                   n_chunk_cap, cfg->top_k, scale, ids,
+                                                   scores_or_null, (uint16_t *)O, lse, stream),
+                      "hga_route_attend_fwd launch");
+}
+
 hga_status hga_summarize_groups(const hga_config *cfg, const void *K, int64_t T_cap,
                                 int64_t tok_begin, int64_t n_tok, float *group_summaries,
                                 int64_t n_group_cap, hipStream_t stream)

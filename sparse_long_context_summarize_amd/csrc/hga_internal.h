@@ -46,14 +46,16 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // router-made row (ascending, distinct) passes one neighbour check; only a
 // row with a repeat pays the quadratic pass. `list` holds k + 1 entries and
 // is read back by the same wave only.
+// first = row[lane] if lane < k, else -1: a caller may load it early, so the
+// load's latency overlaps the caller's other loads.
 __device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
-                                                int64_t local_chunk, int *list)
+                                                int64_t local_chunk, int *list, int first)
 {
     const int lane = threadIdx.x & 63;
     int cnt = 0;
     for (int base = 0; base < k; base += 64) {
         const int r = base + lane;
-        const int c = (r < k) ? row[r] : -1;
+        const int c = base == 0 ? first : (r < k) ? row[r] : -1;
         const bool ok = c >= 0 && (int64_t)c < local_chunk;
         const uint64_t m = __ballot(ok);
         if (ok) list[cnt + lanes_below(m)] = c;
@@ -79,6 +81,13 @@ __device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
     }
     if (lane == 0) list[cnt] = (int)local_chunk;
     return cnt + 1;
+}
+
+__device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
+                                                int64_t local_chunk, int *list)
+{
+    const int lane = threadIdx.x & 63;
+    return build_chunk_list(row, k, local_chunk, list, lane < k ? row[lane] : -1);
 }
 
 // Order-preserving map of a finite float to uint32 (larger float -> larger
@@ -118,6 +127,15 @@ hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     int64_t T_cap, int64_t p0, int64_t n_q,
                                     const int32_t *gids, int32_t m, float scale,
                                     uint16_t *O, float *lse, hipStream_t stream);
+// Routing and attention in one launch (ids and scores written as
+// launch_route would write them). Needs (p0 + n_q - C)/C <=
+// route_attend_max_candidates().
+hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                   int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                   int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                                   float scale, int32_t *ids, float *scores, uint16_t *O,
+                                   float *lse, hipStream_t stream);
+int64_t route_attend_max_candidates();
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
 

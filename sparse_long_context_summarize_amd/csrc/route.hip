@@ -1,262 +1,18 @@
-// route.hip -- per query block top-k chunk routing (arXiv 2607.15105,
-// gist.science technical summary 2.1: the current query block scores the
-// resident chunk summaries and keeps the most relevant earlier chunks; no
-// gradient flows through the choice).
+// route.hip -- per query block top-k chunk routing, and its group-level
+// variant (arXiv 2607.15105, gist.science technical summary 2.1: the current
+// query block scores the resident chunk summaries and keeps the most relevant
+// earlier chunks; the chosen chunks' 8-token groups are ranked the same way
+// by their own summaries; no gradient flows through the choice).
 //
-// One 256-thread workgroup per (query block b, kv head g):
-//   1. qbar = mean of the block's G*64 query rows (fp32, LDS reduction); the
-//      first batch of summary rows is loaded together with the query rows;
-//   2. score_c = qbar . S[g][c] for every chunk c < P/C: 16 lanes per chunk
-//      read one 512-byte summary row with coalesced 16-byte loads (16 chunks
-//      per wave in flight), each lane holding its 8-wide slice of qbar in
-//      registers; the 16 partial sums are folded with four DPP row adds.
-//      Scores become order-preserving uint32 keys in LDS;
-//   3. top-k by (score desc, id asc), for up to 2048 candidates: one wave
-//      holds every key in registers (NI per lane, candidate it*64 + lane); the
-//      k-th largest key is found one bit at a time from ballot/popcount counts
-//      -- no barrier, no memory traffic per bit, and done as soon as exactly k
-//      keys reach the threshold being built -- ties at that key go to the
-//      lowest ids, and the chosen ids come out ascending from a ballot + mbcnt
-//      compaction, so no sort is needed. Larger candidate sets take a
-//      two-stage selection over the keys in LDS (every wave over its id range,
-//      then wave 0 over the survivors).
-// Workgroup w serves kv head w % Hkv: with 8 kv heads the blocks of one head
-// land on one XCD and share its L2 copy of that head's summaries.
-#include "hga_internal.h"
+// One 256-thread workgroup per (query block b, kv head g) runs route_block
+// (route_core.h). Workgroup w serves kv head w % Hkv: with 8 kv heads the
+// blocks of one head land on one XCD and share its L2 copy of that head's
+// summaries.
+#include "route_core.h"
 
 namespace hga {
 namespace {
 
-constexpr int kRouteThreads = 256;
-constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kMaxRegKeys = 32;             // keys per lane of the register selection (2048)
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-
-// Max / min over the wave: within each 16-lane row by DPP (quad swaps, then
-// mirrors within 8 and 16 lanes), then across row pairs and half-waves with
-// the gfx950 lane-swap instructions. Every lane receives the result.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    x = max(x, dpp_u32<0xB1>(x));
-    x = max(x, dpp_u32<0x4E>(x));
-    x = max(x, dpp_u32<0x141>(x));
-    x = max(x, dpp_u32<0x140>(x));
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = max((uint32_t)r[0], (uint32_t)r[1]);
-    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return max((uint32_t)q[0], (uint32_t)q[1]);
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-    x = min(x, dpp_u32<0xB1>(x));
-    x = min(x, dpp_u32<0x4E>(x));
-    x = min(x, dpp_u32<0x141>(x));
-    x = min(x, dpp_u32<0x140>(x));
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = min((uint32_t)r[0], (uint32_t)r[1]);
-    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return min((uint32_t)q[0], (uint32_t)q[1]);
-}
-
-// Sum over each 16-lane row, result in every lane of the row: quad swaps
-// (lane ^ 1, lane ^ 2), then mirrors within 8 and within 16 lanes (DPP).
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-    return x;
-}
-
-// Wave-level selection of the k largest keys[0..n) (ties: lower position
-// first). Writes the chosen positions, ascending, to out_pos (LDS) and
-// returns their number, min(k, n). Every lane of the wave must call it.
-__device__ int wave_select(const uint32_t *keys, int n, int k, int *out_pos)
-{
-    const int lane = threadIdx.x & 63;
-    if (n <= k) {
-        for (int base = 0; base < n; base += 64)
-            if (base + lane < n) out_pos[base + lane] = base + lane;
-        return n;
-    }
-    uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-    for (int base = 0; base < n; base += 64) {
-        const int p = base + lane;
-        if (p < n) { const uint32_t x = keys[p]; mx = max(mx, x); mn = min(mn, x); }
-    }
-    mx = wave_max_u32(mx);
-    mn = wave_min_u32(mn);
-    // Bits above the highest bit in which the keys differ are shared by all.
-    const uint32_t diff = mx ^ mn;
-    int top = diff ? 31 - __builtin_clz(diff) : -1;
-    uint32_t T = (top >= 31) ? 0u : (mx & ~((2u << top) - 1u));
-    // Largest T with #{key >= T} >= k, one bit at a time; once exactly k keys
-    // reach a candidate threshold they are the k largest, and no lower bit
-    // can change which keys are taken.
-    for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        int cnt = 0;
-        for (int base = 0; base < n; base += 64) {
-            const int p = base + lane;
-            cnt += __popcll(__ballot(p < n && keys[p] >= cand));
-        }
-        if (cnt >= k) T = cand;
-        if (cnt == k) break;
-    }
-    int n_gt = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int p = base + lane;
-        n_gt += __popcll(__ballot(p < n && keys[p] > T));
-    }
-    const int need = k - n_gt;   // equal keys to take, lowest positions first
-    int eq_seen = 0, out = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int p = base + lane;
-        const uint32_t x = (p < n) ? keys[p] : 0u;
-        const bool eq = (p < n) && x == T;
-        const uint64_t em = __ballot(eq);
-        const bool take = (p < n && x > T) || (eq && eq_seen + lanes_below(em) < need);
-        eq_seen += __popcll(em);
-        const uint64_t sm = __ballot(take);
-        if (take) out_pos[out + lanes_below(sm)] = p;
-        out += __popcll(sm);
-    }
-    return out;
-}
-
-__device__ __forceinline__ float key_to_score(uint32_t key) {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
-// Wave-level top-k of keys[0..nE) (LDS), nE <= NI*64, by (key desc, candidate
-// index asc): one wave holds every key in registers (candidate c = it*64 +
-// lane), finds the k-th largest key bit by bit from ballot counts (stopping
-// as soon as exactly k keys reach the threshold being built), takes ties at
-// that key from the lowest candidates, and writes id_of(c) of the chosen
-// candidates in ascending candidate order (ballot + mbcnt compaction) to
-// out[], their scores to sout[] (if not null), padding both to k. Empty slots
-// hold key 0, below every finite score's key (>= 0x00800000) and every
-// threshold tried (>= 1), so no test needs a bounds check. Every lane of the
-// wave must call it.
-template <int NI, typename IdOf>
-__device__ __forceinline__ void select_top_k_reg(const uint32_t *keys, int nE, int k,
-                                                 IdOf id_of, int32_t *out, float *sout)
-{
-    const int lane = threadIdx.x & 63;
-    uint32_t key[NI];
-#pragma unroll
-    for (int it = 0; it < NI; ++it) {
-        const int c = it * 64 + lane;
-        key[it] = (c < nE) ? keys[c] : 0u;
-    }
-    int n_sel;
-    if (nE <= k) {
-        n_sel = nE;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const int c = it * 64 + lane;
-            if (c < nE) {
-                out[c] = id_of(c);
-                if (sout) sout[c] = key_to_score(key[it]);
-            }
-        }
-    } else {
-        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            mx = max(mx, key[it]);
-            mn = min(mn, key[it] ? key[it] : 0xFFFFFFFFu);
-        }
-        mx = wave_max_u32(mx);
-        mn = wave_min_u32(mn);
-        // Bits above the highest bit in which the keys differ are shared.
-        const uint32_t diff = mx ^ mn;
-        const int top = diff ? 31 - __builtin_clz(diff) : -1;
-        uint32_t T = (top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)));
-        // Largest T with #{key >= T} >= k, one bit at a time; once exactly k
-        // keys reach a candidate threshold they are the k largest.
-        for (int bit = top; bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
-            if (cnt >= k) T = cand;
-            if (cnt == k) break;
-        }
-        int n_gt = 0;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));
-        const int need = k - n_gt;          // equal keys to take, lowest candidates first
-        int eq_seen = 0, pos = 0;
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const bool eq = key[it] == T;
-            const uint64_t em = __ballot(eq);
-            const bool take = key[it] > T || (eq && eq_seen + lanes_below(em) < need);
-            eq_seen += __popcll(em);
-            const uint64_t sm = __ballot(take);
-            if (take) {
-                const int r = pos + lanes_below(sm);
-                out[r] = id_of(it * 64 + lane);
-                if (sout) sout[r] = key_to_score(key[it]);
-            }
-            pos += __popcll(sm);
-        }
-        n_sel = pos;
-    }
-    for (int r = n_sel + lane; r < k; r += 64) {
-        out[r] = -1;
-        if (sout) sout[r] = -INFINITY;
-    }
-}
-
-
-// The distinct valid chunks (0 <= c < limit) of a chunk row, ascending, into
-// chl; returns their number. A router-made row (ascending, distinct) passes
-// one neighbour check; any other row has its repeats dropped (first kept) and
-// is rank-sorted through tmp (k entries). One wave calls it.
-__device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64_t limit,
-                                                int *chl, int *tmp)
-{
-    const int lane = threadIdx.x & 63;
-    int cnt = 0;
-    for (int base = 0; base < k; base += 64) {
-        const int r = base + lane;
-        const int c = (r < k) ? row[r] : -1;
-        const bool ok = c >= 0 && (int64_t)c < limit;
-        const uint64_t m = __ballot(ok);
-        if (ok) chl[cnt + lanes_below(m)] = c;
-        cnt += __popcll(m);
-    }
-    bool unsorted = false;
-    for (int i = 1 + lane; i < cnt; i += 64) unsorted |= chl[i] <= chl[i - 1];
-    if (__ballot(unsorted) == 0) return cnt;
-    int n = 0;
-    for (int base = 0; base < cnt; base += 64) {
-        const int i = base + lane;
-        const int c = (i < cnt) ? chl[i] : -1;
-        bool keep = i < cnt;
-        for (int j = 0; j < base + 64 && j < cnt; ++j)
-            if (j < i && chl[j] == c) keep = false;
-        const uint64_t m = __ballot(keep);
-        if (keep) tmp[n + lanes_below(m)] = c;
-        n += __popcll(m);
-    }
-    for (int i = lane; i < n; i += 64) {
-        const int v = tmp[i];
-        int r = 0;
-        for (int j = 0; j < n; ++j) r += tmp[j] < v;
-        chl[r] = v;
-    }
-    return n;
-}
-
-// kGroups = false: chunk routing, candidates every chunk c < P/C, rows of S.
-// kGroups = true: group routing (second level), candidates the 8 groups of
-// each distinct valid chunk of chunk_ids[g][b], in ascending group order, rows
-// of the group summaries S; k is then the group budget.
 template <int G, int NI, bool kGroups>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
@@ -265,161 +21,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t *__restrict__ ids, float *__restrict__ scores)
 {
     extern __shared__ uint32_t keys[];          // [candidates of this block]
-    __shared__ float part[16][kD];
-    __shared__ float qbar[kD];
-    __shared__ int surv[kRouteWaves][kMaxTopK];
-    __shared__ int surv_n[kRouteWaves];
-    __shared__ uint32_t cand_key[kRouteWaves * kMaxTopK];
-    __shared__ int cand_pos[kRouteWaves * kMaxTopK];
-    __shared__ int chosen[kMaxTopK];
-    __shared__ int chl[kGroups ? kMaxTopK : 1];
-    __shared__ int n_ch_s;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t n_blocks = n_q / kC;
+    __shared__ RouteLds sh;
     const int64_t g = blockIdx.x % Hkv;
     const int64_t b = blockIdx.x / Hkv;
-    const int64_t P = p0 + b * kC;
-    int nE = (int)(P / kC);
-    if (kGroups) {
-        // 0. the block's distinct valid routed chunks, ascending
-        if (wave == 0) {
-            const int n = sorted_chunk_set(chunk_ids + (g * n_blocks + b) * kc, kc, P / kC,
-                                           chl, (int *)keys);
-            if (lane == 0) n_ch_s = n;
-        }
-        __syncthreads();
-        nE = (kC / kGroup) * n_ch_s;
-    }
-    // summary row of candidate c (its chunk, or its group)
-    auto row_of = [&](int c) __attribute__((always_inline)) {
-        return kGroups ? chl[c >> 3] * (kC / kGroup) + (c & 7) : c;
+    int32_t *out = ids + (g * (n_q / kC) + b) * k;
+    float *sout = scores ? scores + (g * (n_q / kC) + b) * k : nullptr;
+    auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {
+        const int64_t h = g * G + row / kC;
+        const int64_t i = b * kC + row % kC;
+        return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
     };
-
-    // Every load that does not depend on qbar is issued first: all of this
-    // thread's query rows and the first batch of summary rows, so the two
-    // memory round trips overlap.
-    constexpr int kBatch = 16;                  // chunk steps per wave per batch
-    constexpr int kStride = kRouteWaves * 4 * kBatch;     // chunks per batch
-    const int sdseg = lane & 15, sub = lane >> 4;
-    const float *Sg = S + g * n_cap * kD + sdseg * 8;
-    f32x4 slo[kBatch], shi[kBatch];
-    auto load_batch = [&](int base) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            // past the end: re-read the last row (in bounds, result unused)
-            const int c = row_of(min(base + u * kRouteWaves * 4 + sub, nE - 1));
-            slo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
-            shi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
-        }
-    };
-
-    // 1. qbar over the G heads x 64 queries of this block: thread (r0, dseg)
-    // sums rows r0, r0 + 16, ... at d = 8*dseg .. +8.
-    {
-        const int dseg = tid & 15, r0 = tid >> 4;
-        u32x4 w[G * 4];
-#pragma unroll
-        for (int m = 0; m < G * 4; ++m) {
-            const int row = r0 + 16 * m;                   // 0 .. G*64-1
-            const int64_t h = g * G + row / kC;
-            const int64_t i = b * kC + row % kC;
-            w[m] = *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
-        }
-        if (wave * 4 < nE) load_batch(wave * 4);
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int m = 0; m < G * 4; ++m)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] += bf16_lo(w[m][q]);
-                acc[2 * q + 1] += bf16_hi(w[m][q]);
-            }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part[r0][dseg * 8 + e] = acc[e];
-    }
-    __syncthreads();
-    if (tid < kD) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s += part[r][tid];
-        qbar[tid] = s * (1.0f / (float)(G * kC));      // a power of two: exact
-    }
-    __syncthreads();
-
-    // 2. scores -> keys. Each wave scores 4 chunks per step (16 lanes per
-    // chunk, each holding its 8-wide slice of qbar), kBatch steps per batch.
-    {
-        float qv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = qbar[sdseg * 8 + e];
-        for (int base = wave * 4; base < nE; base += kStride) {
-            if (base != wave * 4) load_batch(base);
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                float s = qv[0] * slo[u][0];
-                s = fmaf(qv[1], slo[u][1], s);
-                s = fmaf(qv[2], slo[u][2], s);
-                s = fmaf(qv[3], slo[u][3], s);
-                s = fmaf(qv[4], shi[u][0], s);
-                s = fmaf(qv[5], shi[u][1], s);
-                s = fmaf(qv[6], shi[u][2], s);
-                s = fmaf(qv[7], shi[u][3], s);
-                s = row16_sum(s);
-                const int c = base + u * kRouteWaves * 4 + sub;
-                if (sdseg == 0 && c < nE) keys[c] = score_key(s);
-            }
-        }
-    }
-    __syncthreads();
-
-    int32_t *out = ids + (g * n_blocks + b) * k;
-    float *sout = scores ? scores + (g * n_blocks + b) * k : nullptr;
-
-    if (kGroups || NI * 64 >= nE) {
-        // 3. one wave, keys in registers (group routing never has more than
-        // 8 * kMaxTopK = NI * 64 candidates)
-        if (wave != 0) return;
-        select_top_k_reg<NI>(keys, nE, k, row_of, out, sout);
-        return;
-    }
-
-    // 3'. more than 2048 candidates: each wave selects over its contiguous id
-    // range (keys in LDS), then wave 0 selects among the survivors.
-    const int per = (nE + kRouteWaves - 1) / kRouteWaves;
-    const int lo = min(nE, wave * per);
-    const int hi = min(nE, lo + per);
-    const int got = wave_select(keys + lo, hi - lo, k, surv[wave]);
-    if (lane == 0) surv_n[wave] = got;
-    __syncthreads();
-    if (wave == 0) {
-        int m = 0;
-        for (int w = 0; w < kRouteWaves; ++w) {
-            const int cnt = surv_n[w];
-            const int off = min(nE, w * per);
-            for (int j = lane; j < cnt; j += 64) {
-                const int pos = off + surv[w][j];
-                cand_pos[m + j] = pos;
-                cand_key[m + j] = keys[pos];
-            }
-            m += cnt;
-        }
-        // cand_pos is ascending: wave ranges are in order, each list ascending.
-        const int n_sel = wave_select(cand_key, m, k, chosen);
-        for (int r = lane; r < k; r += 64) {
-            if (r < n_sel) {
-                out[r] = cand_pos[chosen[r]];
-                if (sout) sout[r] = key_to_score(cand_key[chosen[r]]);
-            } else {
-                out[r] = -1;
-                if (sout) sout[r] = -INFINITY;
-            }
-        }
-    }
+    route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, chunk_ids, kc,
+                                    [&](int r, int id, float sc) __attribute__((always_inline)) {
+                                        out[r] = id;
+                                        if (sout) sout[r] = sc;
+                                    });
 }
 
 template <int G, int NI, bool kGroups>

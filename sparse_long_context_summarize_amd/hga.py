@@ -21,7 +21,7 @@ HGA_ERR_CAPACITY = 3
 HGA_ERR_HIP = 4
 HGA_BF16 = 0
 
-EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd",
+EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
             "hga_status_string", "hga_last_error", "hga_version")
@@ -72,12 +72,15 @@ def lib() -> ctypes.CDLL:
     L.hga_attend_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.hga_attend_bwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.hga_route_attend_fwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64,
+                                       _vp, _vp, _vp, _vp, _vp]
     L.hga_summarize_groups.argtypes = [_cfgp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
     L.hga_route_groups.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _vp, ctypes.c_int32,
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
     for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
+               "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +170,18 @@ def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV
             _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream))
 
 
+def _m_route_attend_fwd(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int, ids,
+                        O, lse, scores=None, stream=None):
+    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16))
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
+
+
 def _m_summarize_groups(cfg: hga_config, K, tok_begin: int, n_tok: int, group_summaries,
                         stream=None):
     return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), K.shape[1], tok_begin, n_tok,
@@ -199,6 +214,7 @@ def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, s
 
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
+            "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
             "hga_attend_fwd_groups": _m_attend_fwd_groups}
 
@@ -235,6 +251,17 @@ def hga_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, d
     """dQ f32 [Hq][n_q][D]; dK, dV f32 [Hkv][n_q][D] (active keys) are written."""
     _check("hga_attend_bwd", lib().hga_attend_bwd(
         *_m_attend_bwd(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, workspace, stream)))
+
+
+def hga_route_attend_fwd(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                         p0: int, summaries: torch.Tensor, n_chunks_valid: int,
+                         ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
+                         scores: torch.Tensor | None = None, stream=None) -> None:
+    """hga_route then hga_attend_fwd in one launch; ids (and scores) are
+    written as hga_route writes them."""
+    _check("hga_route_attend_fwd", lib().hga_route_attend_fwd(
+        *_m_route_attend_fwd(cfg, Q, K, V, p0, summaries, n_chunks_valid, ids, O, lse, scores,
+                             stream)))
 
 
 def hga_summarize_groups(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,

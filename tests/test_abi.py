@@ -178,3 +178,26 @@ def test_group_entry_point_checks():
     assert a(c, FAKE, FAKE, FAKE, 16383, 14336, 2048, FAKE, 64, FAKE, FAKE,
              None) == hga.HGA_ERR_INVALID_ARG
     assert a(c, FAKE, FAKE, FAKE, 16384, 14336, 0, None, 64, FAKE, FAKE, None) == hga.HGA_OK
+
+
+def test_route_attend_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    c = ctypes.byref(cfg)
+    f = L.hga_route_attend_fwd
+    args = dict(T=16384, p0=14336, n_q=2048, cap=256, valid=256, ids=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(c, FAKE, FAKE, FAKE, a["T"], a["p0"], a["n_q"], FAKE, a["cap"], a["valid"],
+                 a["ids"], None, FAKE, FAKE, None)
+
+    # the last block needs 255 valid summaries
+    assert call(valid=254) == hga.HGA_ERR_CAPACITY
+    assert call(valid=257) == hga.HGA_ERR_CAPACITY          # valid > capacity
+    assert call(T=16383) == hga.HGA_ERR_INVALID_ARG
+    assert call(ids=None) == hga.HGA_ERR_INVALID_ARG
+    assert call(n_q=0) == hga.HGA_OK
+    cfg0 = _cfg(top_k=0)
+    assert f(ctypes.byref(cfg0), FAKE, FAKE, FAKE, 16384, 14336, 0, None, 0, 0, None, None,
+             FAKE, FAKE, None) == hga.HGA_OK
