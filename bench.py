@@ -125,20 +125,21 @@ def _median_ms(torch, fn, pre=None, n=10):
     return t[len(t) // 2]
 
 
-def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int) -> float:
-    """Algorithmic flops of hga_attend_bwd: per attended (query, key) pair
-    2*D each for S, dP and dQ, plus 2*D each for dK and dV where the key is
-    in the active segment (history is detached)."""
+def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int, unit: int = C) -> float:
+    """Algorithmic flops of hga_attend_bwd (unit = 64, chunk ids) or
+    hga_attend_bwd_groups (unit = 8): per attended (query, key) pair 2*D each
+    for S, dP and dQ, plus 2*D each for dK and dV where the key is in the
+    active segment (history is detached)."""
     Hkv, nb, k = ids.shape
     P = p0 + np.arange(nb) * C
     hist = act = 0
     for b in range(nb):
         for g in range(Hkv):
             row = ids[g, b]
-            ok = np.unique(row[(row >= 0) & (row < P[b] // C)])
-            a = int((ok * C >= p0).sum())
-            act += a * C * C
-            hist += (len(ok) - a) * C * C
+            ok = np.unique(row[(row >= 0) & (row < P[b] // unit)])
+            a = int((ok * unit >= p0).sum())
+            act += a * unit * C
+            hist += (len(ok) - a) * unit * C
         act += Hkv * (C * (C + 1) // 2)
     return float(G * (6 * D * hist + 10 * D * act))
 
@@ -408,8 +409,20 @@ def group_timings(torch, hga, inputs, dev):
         for fn in calls.values():
             fn()
 
+    # backward of the group attention at the same layer (dO ~ N(0, 1))
+    dO = up(np.random.default_rng(5).standard_normal((w.Hq, w.n_q, w.D), dtype=np.float32))
+    dQ = torch.empty((w.Hq, w.n_q, w.D), device=dev)
+    dK = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+    dV = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+    ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg, w.n_q), dtype=torch.uint8,
+                     device=dev)
+    bwd = hga.prepare("hga_attend_bwd_groups", cfg, Q, K, V, w.p0, gids, O, lse, dO, dQ, dK,
+                      dV, ws)
+
     ms = _median_ms(torch, layer)
+    ms_bwd = _median_ms(torch, bwd)
     g = gids.cpu().numpy()
+    fl_bwd = bwd_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
     fl = attend_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
     ab = attend_bytes(g, w.n_q, w.Hq, w.D, w.p0, unit=hga.HGA_GROUP)
     t_att = res["groups16k_attend_fwd_groups_us"] * 1e-6
@@ -420,6 +433,9 @@ def group_timings(torch, hga, inputs, dev):
         "groups16k_attend_algorithmic_gflop": fl / 1e9,
         "groups16k_attend_tflops": fl / t_att / 1e12,
         "groups16k_attend_gathered_GBps": ab / t_att / 1e9,
+        "groups16k_bwd_us": ms_bwd * 1e3,
+        "groups16k_bwd_algorithmic_gflop": fl_bwd / 1e9,
+        "groups16k_bwd_tflops": fl_bwd / (ms_bwd * 1e-3) / 1e12,
     })
     return res
 

@@ -244,6 +244,21 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
                                  const int32_t *group_ids, int32_t group_top_k, void *O,
                                  float *lse, hipStream_t stream);
 
+/*
+ * hga_attend_bwd_groups -- hga_attend_bwd for hga_attend_fwd_groups: the same
+ * gradients (dQ of every active query; dK, dV of the active keys, summed over
+ * the G heads; history detached) with A(i) built from group_ids as in
+ * hga_attend_fwd_groups. lse is that call's output; O is not read (may be
+ * NULL). The workspace is hga_attend_bwd_workspace_bytes(cfg, n_q) bytes, with
+ * the same rules as for hga_attend_bwd; results are deterministic.
+ */
+hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                 const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                 const int32_t *group_ids, int32_t group_top_k, const void *O,
+                                 const float *lse, const void *dO, float *dQ, float *dK_active,
+                                 float *dV_active, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hga_status_string(hga_status status);
 

@@ -78,6 +78,18 @@ __device__ __forceinline__ void dq_load_k(DqRegs &r, const uint16_t *Kg, int64_t
     for (int j = 0; j < kDqPieces; ++j) r.p[j] = *(const u32x4 *)(src + j * kD);
 }
 
+// Group tiles: the same rows, 4*kg + j, lie in one 8-row group, so one
+// row_tok(4*kg) call serves the thread's four pieces.
+template <typename RowTok>
+__device__ __forceinline__ void dq_load_k(DqRegs &r, const uint16_t *Kg, RowTok row_tok)
+{
+    const int u = threadIdx.x - kDqThreads / 2, lane = u & 63;
+    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
+    const uint16_t *src = Kg + row_tok(4 * kg) * kD + dp * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) r.p[j] = *(const u32x4 *)(src + j * kD);
+}
+
 // K to LDS twice: row-major (272-B rows) for the S^T operand, and transposed,
 // K^T[d][t_pos(key)], for the dQ^T operand (the 4 keys x 8 d a lane holds are
 // transposed with byte permutes; with kg = lane%16 the 64 lanes' 8-byte
@@ -117,6 +129,27 @@ __device__ __forceinline__ void dq_store_v(const DqRegs &r, uint16_t *Vs)
     for (int j = 0; j < kDqPieces; ++j) *(u32x4 *)(dst + 16 * j * kRowStride) = r.p[j];
 }
 
+// Group tiles, V group: thread u takes rows r0 + 2*j of one 8-row group,
+// r0 = 8*(u/32) + (u/16)%2, d = 8*(u%16) .. +8 (one row_tok call per tile).
+template <typename RowTok>
+__device__ __forceinline__ void dq_load_v(DqRegs &r, const uint16_t *Vg, RowTok row_tok)
+{
+    const int u = threadIdx.x;
+    const int r0 = 8 * (u >> 5) + ((u >> 4) & 1);
+    const uint16_t *src = Vg + row_tok(r0) * kD + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) r.p[j] = *(const u32x4 *)(src + 2 * j * kD);
+}
+
+__device__ __forceinline__ void dq_store_v_grp(const DqRegs &r, uint16_t *Vs)
+{
+    const int u = threadIdx.x;
+    const int r0 = 8 * (u >> 5) + ((u >> 4) & 1);
+    uint16_t *dst = Vs + r0 * kRowStride + (u & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < kDqPieces; ++j) *(u32x4 *)(dst + 2 * j * kRowStride) = r.p[j];
+}
+
 // Work unit: query block b of kv head g, as in the forward. 8 waves, two per
 // SIMD: wave w computes head g*G + hg*HW + w%4 for queries 32*(w/4) .. +32,
 // with Q^T and dO^T in registers as MFMA B operands, in the transposed form
@@ -124,7 +157,10 @@ __device__ __forceinline__ void dq_store_v(const DqRegs &r, uint16_t *Vs)
 // lane pair). Steps walk the tile list twice (pass 1, then pass 2); tiles are
 // loaded two steps ahead into registers and written to double-buffered LDS
 // one barrier before use. Each 64-key tile is processed as two 32-key halves.
-template <int G>
+// kUnit = kC: ids are chunk ids. kUnit = kGroup: ids are 8-token group ids;
+// each routed tile is gathered from 8 groups, and a last routed tile with
+// fewer masks its missing groups' keys.
+template <int G, int kUnit>
 __global__ __launch_bounds__(kDqThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -138,7 +174,7 @@ void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Kts[2][kTTile];
-    __shared__ int list[kMaxTopK + 1];
+    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 1];
     __shared__ int list_n;
 
     const int tid = threadIdx.x;
@@ -154,14 +190,21 @@ void bwd_dq_kernel(
     const uint16_t *Kg = K + g * T_cap * kD;
     const uint16_t *Vg = V + g * T_cap * kD;
 
+    // routed units (0 <= u < P/kUnit, repeats dropped), then the local chunk
     if (wave == 0) {
-        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, local_chunk, list);
-        if (lane == 0) list_n = n;
+        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, P / kUnit, list);
+        if (lane == 0) {
+            list[n - 1] = (int)local_chunk;
+            list_n = n;
+        }
     }
     // the dkdv kernel that follows counts finished workgroups per (kv head, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
     __syncthreads();
-    const int n_tiles = list_n;
+    const int n_units = list_n - 1;
+    const int n_tiles = (kUnit == kC ? n_units : (n_units + 7) / 8) + 1;
+    // keys of the last routed tile (groups: 8 per group present; else 64)
+    const int pad_keys = (kUnit != kC && (n_units & 7) != 0) ? kGroup * (n_units & 7) : kC;
     // Each pass walks the tile list once, padded to an even number of steps
     // (a padding step moves data but computes nothing), so both pass loops
     // run whole pairs with the register sets in one fixed order.
@@ -185,9 +228,22 @@ void bwd_dq_kernel(
         }
         lse2 = lse[qrow] * 1.44269504088896340736f;
     }
+    const int *lst = list;
+    // first token of a chunk tile, or the token of row r of a group tile
+    // (the local tile is last; padding rows repeat the tile's last group)
     auto step_tok = [&](int st) __attribute__((always_inline)) {
         const int i = min(st % n_pass, n_tiles - 1);
-        return (int64_t)list[i] * kC;
+        if constexpr (kUnit == kC) {
+            return (int64_t)lst[i] * kC;
+        } else {
+            const bool local = i == n_tiles - 1;
+            const int64_t lbase = (int64_t)lst[n_units] * kC;
+            const int g0 = 8 * i, glast = n_units - 1;
+            return [=](int r) __attribute__((always_inline)) -> int64_t {
+                if (local) return lbase + r;
+                return (int64_t)lst[min(g0 + (r >> 3), glast)] * kGroup + (r & 7);
+            };
+        }
     };
     auto load = [&](DqRegs &r, int st) __attribute__((always_inline)) {
         if (kgrp) dq_load_k(r, Kg, step_tok(min(st, n_steps - 1)));
@@ -195,7 +251,8 @@ void bwd_dq_kernel(
     };
     auto store = [&](const DqRegs &r, int buf) __attribute__((always_inline)) {
         if (kgrp) dq_store_k(r, Ks[buf], Kts[buf]);
-        else dq_store_v(r, Vs[buf]);
+        else if constexpr (kUnit == kC) dq_store_v(r, Vs[buf]);
+        else dq_store_v_grp(r, Vs[buf]);
     };
     DqRegs r0, r1;
     load(r0, 0);
@@ -205,9 +262,10 @@ void bwd_dq_kernel(
     __syncthreads();
 
     // S^T and dP^T of one 32-key half kt of the tile in buffer buf, P in place
-    // of S^T (causal mask on the local block: key 32*kt + 8*(j/4) + 4*half +
-    // j%4 is masked above query 32*qt + col, i.e. when 8*(j/4) + j%4 > thr).
-    auto sdp = [&](int buf, int kt, bool diag, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+    // of S^T. Masks: key 32*kt + 8*(j/4) + 4*half + j%4 is dropped when
+    // 8*(j/4) + j%4 > thr -- on the local block above query 32*qt + col
+    // (causal), on a last group tile from key pad_keys on.
+    auto sdp = [&](int buf, int kt, int mode, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
         const uint16_t *Kb = Ks[buf];
         const uint16_t *Vb = Vs[buf];
         s = zero16();
@@ -226,7 +284,8 @@ void bwd_dq_kernel(
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        const int thr = diag ? 32 * (qt - kt) + col - 4 * half : 1 << 20;
+        const int thr = mode == 1 ? 32 * (qt - kt) + col - 4 * half
+                      : mode == 2 ? pad_keys - 32 * kt - 4 * half - 1 : 1 << 20;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -lse2));
@@ -241,17 +300,19 @@ void bwd_dq_kernel(
         const int buf = st & 1;
         load(pre, st + 2);
         const int it = st % n_pass;
-        if (computes && it < n_tiles) body(buf, it == n_tiles - 1);
+        // mode: 1 = local block (causal), 2 = last routed tile of groups
+        const int mode = it == n_tiles - 1 ? 1 : (it == n_tiles - 2 && pad_keys < kC) ? 2 : 0;
+        if (computes && it < n_tiles) body(buf, mode);
         if (st + 1 < n_steps) store(nxt, buf ^ 1);
         __syncthreads();
     };
 
     // pass 1: Delta_i = sum_j P_ij dP_ij
-    auto pass1 = [&](int buf, bool diag) __attribute__((always_inline)) {
+    auto pass1 = [&](int buf, int mode) __attribute__((always_inline)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x16 s, dp;
-            sdp(buf, kt, diag, s, dp);
+            sdp(buf, kt, mode, s, dp);
 #pragma unroll
             for (int j = 0; j < 16; ++j) dl = fmaf(s[j], dp[j], dl);
         }
@@ -270,12 +331,12 @@ void bwd_dq_kernel(
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
-    auto pass2 = [&](int buf, bool diag) __attribute__((always_inline)) {
+    auto pass2 = [&](int buf, int mode) __attribute__((always_inline)) {
         const uint16_t *Ktb = Kts[buf];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x16 s, dp;
-            sdp(buf, kt, diag, s, dp);
+            sdp(buf, kt, mode, s, dp);
             bf16x8 dsh[2];
             bool big = false;
 #pragma unroll
@@ -339,7 +400,10 @@ static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits"
 
 constexpr int kSplit = 2;                  // workgroups that share one chunk's block list
 
-template <int G>
+// kUnit = kGroup: a later block may have chosen only some of the chunk's 8
+// groups; the scan records them as an 8-bit mask per listed block, and the
+// keys of the other groups get P = 0 in that block's tiles.
+template <int G, int kUnit>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
@@ -350,6 +414,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];
     __shared__ int blist[kMaxBlocksDkdv];
+    __shared__ uint8_t bmask[kMaxBlocksDkdv];
+    __shared__ uint8_t rmask[kMaxBlocksDkdv];   // by block: the scan's result
     __shared__ int blist_n;
     __shared__ int is_last;
 
@@ -364,20 +430,62 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int64_t ca = p0 / kC + a;               // absolute chunk index
 
     // Query blocks that attend chunk a: its own (causal) and every later block
-    // whose routed ids list it, in ascending block order.
+    // whose routed ids list it (or, for group ids, any of its groups), in
+    // ascending block order, each with the mask of the chunk's groups it
+    // attends. The four waves scan the later blocks' id rows (wave w: blocks
+    // a+1+w, a+5+w, ...), each row spread over the 64 lanes and kScanRows rows
+    // loaded before any is used; the masks land in LDS by block and wave 0
+    // then lists the blocks in order.
+    {
+        constexpr int kScanRows = 4;
+        const int32_t ca32 = (int32_t)ca;
+        for (int64_t base = a + 1 + wave; base < n_blocks; base += 4 * kScanRows) {
+            uint32_t msk[kScanRows];
+#pragma unroll
+            for (int rr = 0; rr < kScanRows; ++rr) msk[rr] = 0u;
+            for (int c0 = 0; c0 < k; c0 += 64) {
+                int32_t u[kScanRows];
+#pragma unroll
+                for (int rr = 0; rr < kScanRows; ++rr) {
+                    const int64_t bb = base + 4 * rr;
+                    u[rr] = (bb < n_blocks && c0 + lane < k)
+                                ? ids[(g * n_blocks + bb) * k + c0 + lane] : -1;
+                }
+#pragma unroll
+                for (int rr = 0; rr < kScanRows; ++rr) {
+                    if constexpr (kUnit == kC) {
+                        msk[rr] |= __ballot(u[rr] == ca32) != 0 ? 0xFFu : 0u;
+                    } else {
+                        const bool in = (u[rr] >> 3) == ca32;
+#pragma unroll
+                        for (int bit = 0; bit < 8; ++bit)
+                            msk[rr] |= __ballot(in && (u[rr] & 7) == bit) != 0 ? 1u << bit : 0u;
+                    }
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < kScanRows; ++rr) {
+                const int64_t bb = base + 4 * rr;
+                if (lane == 0 && bb < n_blocks) rmask[bb] = (uint8_t)msk[rr];
+            }
+        }
+    }
+    __syncthreads();
     if (wave == 0) {
-        int cnt = 0;
-        if (lane == 0) blist[0] = (int)a;
-        cnt = 1;
+        if (lane == 0) {
+            blist[0] = (int)a;
+            bmask[0] = 0xFF;
+        }
+        int cnt = 1;
         for (int64_t base = a + 1; base < n_blocks; base += 64) {
             const int64_t bb = base + lane;
-            bool hit = false;
-            if (bb < n_blocks) {
-                const int32_t *row = ids + (g * n_blocks + bb) * k;
-                for (int r = 0; r < k; ++r) hit |= (row[r] == (int32_t)ca);
-            }
+            const uint32_t msk = bb < n_blocks ? rmask[bb] : 0u;
+            const bool hit = msk != 0;
             const uint64_t m = __ballot(hit);
-            if (hit) blist[cnt + lanes_below(m)] = (int)bb;
+            if (hit) {
+                blist[cnt + lanes_below(m)] = (int)bb;
+                bmask[cnt + lanes_below(m)] = (uint8_t)msk;
+            }
             cnt += __popcll(m);
         }
         if (lane == 0) blist_n = cnt;
@@ -502,6 +610,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
         // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
         const bool diag = split == 0 && (it / G) == 0;   // list entry 0 is the own block
+        // (group ids: this lane's key is dropped unless its group was chosen)
+        const bool kept = kUnit == kC ||
+                          ((bmask[split + kSplit * (it / G)] >> ((32 * kh + col) >> 3)) & 1);
         bf16x8 pb[2], dsb[2];
         bool big = false;
 #pragma unroll
@@ -513,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * u + e;
                 float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -l4[e]));
-                if (diag && 32 * kh + col > q0 + e) p = 0.f;
+                if ((diag && 32 * kh + col > q0 + e) || !kept) p = 0.f;
                 big |= p > kPairAbove;
                 s[j] = p;
                 dp[j] = p * (dp[j] - d4[e]);
@@ -652,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
 }
 
-template <int G>
+template <int G, int kUnit>
 hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                         int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
                         const int32_t *ids, int32_t k, float scale, const float *lse,
@@ -662,12 +773,12 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL(bwd_dq_kernel<G>, dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kDqThreads),
+    hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kDqThreads),
                        0, stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, T_cap, p0, ids,
                        k, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<G>, dim3((unsigned)(n_blocks * Hkv * kSplit)),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * kSplit)),
                        dim3(kThreads), 0, stream, Q, K, V, dO, lse, delta, n_q, Hkv, T_cap, p0,
                        ids, k, scale_log2, scale, dK, dV, part, counters);
     return hipGetLastError();
@@ -699,6 +810,32 @@ size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q)
 
 int64_t bwd_max_queries() { return (int64_t)kMaxBlocksDkdv * kC; }
 
+namespace {
+
+template <int kUnit>
+hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                           int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
+                           const int32_t *ids, int32_t k, float scale, const float *lse,
+                           const uint16_t *dO, float *dQ, float *dK, float *dV,
+                           void *workspace, hipStream_t stream)
+{
+    if (n_q == 0) return hipSuccess;
+    const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q);
+    uint8_t *ws = (uint8_t *)workspace;
+    float *delta = (float *)(ws + w.delta_off);
+    int *counters = (int *)(ws + w.counter_off);
+    float *part = (float *)(ws + w.part_off);
+    switch (Hq / Hkv) {
+    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                              int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                              int64_t n_q, const int32_t *ids, int32_t k, float scale,
@@ -707,19 +844,18 @@ hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K, const uint16_
                              hipStream_t stream)
 {
     (void)O;    // Delta is recomputed from P and dP (see the dq kernel)
-    if (n_q == 0) return hipSuccess;
-    const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q);
-    uint8_t *ws = (uint8_t *)workspace;
-    float *delta = (float *)(ws + w.delta_off);
-    int *counters = (int *)(ws + w.counter_off);
-    float *part = (float *)(ws + w.part_off);
-    switch (Hq / Hkv) {
-    case 1: return launch_bwd_g<1>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 2: return launch_bwd_g<2>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 4: return launch_bwd_g<4>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 8: return launch_bwd_g<8>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ,
+                               dK, dV, workspace, stream);
+}
+
+hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                    int64_t n_q, const int32_t *gids, int32_t m, float scale,
+                                    const float *lse, const uint16_t *dO, float *dQ, float *dK,
+                                    float *dV, void *workspace, hipStream_t stream)
+{
+    return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, scale, lse, dO,
+                                   dQ, dK, dV, workspace, stream);
 }
 
 }  // namespace hga

@@ -309,6 +309,42 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
                       "hga_attend_fwd_groups launch");
 }
 
+hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                 const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                 const int32_t *group_ids, int32_t group_top_k, const void *O,
+                                 const float *lse, const void *dO, float *dQ, float *dK_active,
+                                 float *dV_active, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
+        return fail(HGA_ERR_INVALID_ARG, "group_top_k must be in [0, %d] (got %d)",
+                    hga::kMaxGroupTopK, group_top_k);
+    if (n_q == 0) return HGA_OK;
+    if (n_q > hga::bwd_max_queries())
+        return fail(HGA_ERR_UNSUPPORTED, "backward supports at most %lld active queries",
+                    (long long)hga::bwd_max_queries());
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
+        (group_top_k > 0 && !group_ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+    if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    (void)O;
+    return hip_status(hga::launch_attend_bwd_groups((const uint16_t *)Q, (const uint16_t *)K,
+                                                    (const uint16_t *)V, cfg->n_q_heads,
+                                                    cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
+                                                    group_top_k, effective_scale(cfg), lse,
+                                                    (const uint16_t *)dO, dQ, dK_active,
+                                                    dV_active, workspace, stream),
+                      "hga_attend_bwd_groups launch");
+}
+
 size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)
 {
     if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;

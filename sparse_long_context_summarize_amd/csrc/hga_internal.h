@@ -136,6 +136,11 @@ hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const u
                                    float scale, int32_t *ids, float *scores, uint16_t *O,
                                    float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
+hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                    int64_t n_q, const int32_t *gids, int32_t m, float scale,
+                                    const float *lse, const uint16_t *dO, float *dQ, float *dK,
+                                    float *dV, void *workspace, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
 

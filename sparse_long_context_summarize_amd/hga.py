@@ -24,7 +24,7 @@ HGA_BF16 = 0
 EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
-            "hga_status_string", "hga_last_error", "hga_version")
+            "hga_attend_bwd_groups", "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
 
 
@@ -79,9 +79,13 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
+    L.hga_attend_bwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
+                                        ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
     for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
                "hga_route_attend_fwd",
-               "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups"):
+               "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
+               "hga_attend_bwd_groups"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
@@ -212,11 +216,31 @@ def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, s
             _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
 
 
+def _m_attend_bwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, dO, dQ, dK, dV,
+                        workspace, stream=None):
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    if group_ids.dim() != 3:
+        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+            _dev(group_ids, "group_ids", torch.int32), group_ids.shape[2],
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32),
+            _dev(dO, "dO", torch.bfloat16), _dev(dQ, "dQ", torch.float32),
+            _dev(dK, "dK", torch.float32), _dev(dV, "dV", torch.float32), workspace.data_ptr(),
+            ws_bytes, _stream(stream))
+
+
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
             "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
-            "hga_attend_fwd_groups": _m_attend_fwd_groups}
+            "hga_attend_fwd_groups": _m_attend_fwd_groups,
+            "hga_attend_bwd_groups": _m_attend_bwd_groups}
 
 
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
@@ -286,6 +310,16 @@ def hga_attend_fwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: 
     """Attention over routed 8-token groups plus the causal local block."""
     _check("hga_attend_fwd_groups", lib().hga_attend_fwd_groups(
         *_m_attend_fwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, stream)))
+
+
+def hga_attend_bwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                          p0: int, group_ids: torch.Tensor, O, lse: torch.Tensor,
+                          dO: torch.Tensor, dQ: torch.Tensor, dK: torch.Tensor, dV: torch.Tensor,
+                          workspace: torch.Tensor, stream=None) -> None:
+    """Gradients of hga_attend_fwd_groups (dQ; dK, dV of the active keys)."""
+    _check("hga_attend_bwd_groups", lib().hga_attend_bwd_groups(
+        *_m_attend_bwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, dO, dQ, dK, dV, workspace,
+                              stream)))
 
 
 def prepare(name: str, *args, **kwargs):

@@ -60,3 +60,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bwd_counts_for_groups():
+    # p0 = 128: groups 0..15 are history, 16.. active; block 1 (P = 192) may
+    # use groups < 24, block 0 (P = 128) groups < 16
+    ids = np.array([[[3, 3, 15, 16, -1], [0, 17, 23, 24, 17]]], np.int32)
+    G, D, U = 2, 128, 8
+    fl = bench.bwd_flops(ids, 128, G, D, 128, unit=U)
+    hist = (2 + 1) * U * 64            # block 0: {3, 15}; block 1: {0}
+    act = 2 * U * 64 + 2 * (64 * 65 // 2)   # block 1: {17, 23}; both local blocks
+    assert fl == G * (6 * D * hist + 10 * D * act)
