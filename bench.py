@@ -99,6 +99,14 @@ def attend_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int, unit: int =
     return 4.0 * D * float(routed_pairs + local_pairs)
 
 
+def attend_flops_executed(ids: np.ndarray, G: int, D: int, p0: int) -> float:
+    """Flops the attention kernel executes: every tile is a full 64 x 64 block,
+    the masked half of the local (diagonal) tile included."""
+    Hkv, nb, k = ids.shape
+    tiles = _n_valid_units(ids, p0, C) + Hkv * nb
+    return 4.0 * D * G * C * C * float(tiles)
+
+
 def attend_bytes(ids: np.ndarray, n_q: int, Hq: int, D: int, p0: int, unit: int = C) -> float:
     """Algorithmic HBM bytes of the attention call: each (block, kv head)
     gathers its routed units' and local block's K and V once (bf16), reads Q
@@ -261,6 +269,7 @@ def main():
         },
         "kernels_ms": ms,
         "attend_algorithmic": {"flops": flops, "bytes": abytes,
+                               "executed_flops": attend_flops_executed(ids_np, w.G, w.D, w.p0),
                                "gathered_GBps": abytes / (ms["route_attend"] * 1e-3) / 1e9,
                                "hbm_frac_of_algorithmic_bytes":
                                    abytes / (ms["route_attend"] * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -363,6 +372,16 @@ def attend_timings(torch, hga, inputs, dev):
             res["layer16k_attend_cold_us"] = ms_cold * 1e3
             res["layer16k_attend_warm_us"] = ms_warm * 1e3
             res["layer16k_attend_cold_gathered_GBps"] = abytes / (ms_cold * 1e-3) / 1e9
+            # the gather alone (hga_diag_gather: the same rows, no arithmetic)
+            sink = torch.empty(hga.hga_diag_gather_sink_words(cfg, w.n_q), dtype=torch.int32,
+                               device=dev)
+            gat = hga.prepare("hga_diag_gather", cfg, K, V, w.p0, w.n_q, ids, sink)
+            gbytes = abytes - (w.Hq * w.n_q * w.D * 2 * 2 + w.Hq * w.n_q * 4)
+            g_cold = med(gat, pre=lambda: flush.fill_(1))
+            g_warm = med(gat, pre=lambda: flush[:1].fill_(1))
+            res["layer16k_gather_only_cold_us"] = g_cold * 1e3
+            res["layer16k_gather_only_warm_us"] = g_warm * 1e3
+            res["layer16k_gather_only_cold_GBps"] = gbytes / (g_cold * 1e-3) / 1e9
             del flush
         del Q, K, V, S, ids, O, lse
     return res

@@ -259,6 +259,25 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
                                  float *dV_active, void *workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Diagnostic (not a step of the method).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * hga_diag_gather -- reads exactly the K and V rows hga_attend_fwd gathers for
+ * the same arguments (each block's valid routed chunks, repeats once, and its
+ * local block), with the attention kernel's addressing, and does nothing else
+ * but fold them into sink (one word per thread, contents meaningless): its
+ * time is the ceiling the gather alone puts on hga_attend_fwd.
+ *   sink   device memory of at least hga_diag_gather_sink_words(cfg, n_q)
+ *          32-bit words, else HGA_ERR_CAPACITY; other arguments and errors as
+ *          for hga_attend_fwd.
+ */
+size_t hga_diag_gather_sink_words(const hga_config *cfg, int64_t n_q);
+hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, int64_t T_cap,
+                           int64_t p0, int64_t n_q, const int32_t *ids, uint32_t *sink,
+                           size_t sink_words, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *hga_status_string(hga_status status);
 

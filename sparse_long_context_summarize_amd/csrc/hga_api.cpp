@@ -345,6 +345,33 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
                       "hga_attend_bwd_groups launch");
 }
 
+size_t hga_diag_gather_sink_words(const hga_config *cfg, int64_t n_q)
+{
+    if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;
+    return hga::gather_sink_words(cfg->n_kv_heads, n_q);
+}
+
+hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, int64_t T_cap,
+                           int64_t p0, int64_t n_q, const int32_t *ids, uint32_t *sink,
+                           size_t sink_words, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (n_q == 0) return HGA_OK;
+    if (!K || !V || !sink || (cfg->top_k > 0 && !ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (sink_words < hga::gather_sink_words(cfg->n_kv_heads, n_q))
+        return fail(HGA_ERR_CAPACITY, "sink holds %zu words, %zu needed", sink_words,
+                    hga::gather_sink_words(cfg->n_kv_heads, n_q));
+    return hip_status(hga::launch_gather((const uint16_t *)K, (const uint16_t *)V,
+                                         cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k, sink,
+                                         stream),
+                      "hga_diag_gather launch");
+}
+
 size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)
 {
     if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;

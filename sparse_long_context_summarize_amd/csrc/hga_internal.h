@@ -136,6 +136,11 @@ hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const u
                                    float scale, int32_t *ids, float *scores, uint16_t *O,
                                    float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
+// Gather-only diagnostic (diag.hip): sink holds gather_sink_words words.
+hipError_t launch_gather(const uint16_t *K, const uint16_t *V, int64_t Hkv, int64_t T_cap,
+                         int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, uint32_t *sink,
+                         hipStream_t stream);
+size_t gather_sink_words(int64_t Hkv, int64_t n_q);
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                     int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                     int64_t n_q, const int32_t *gids, int32_t m, float scale,

@@ -24,7 +24,8 @@ HGA_BF16 = 0
 EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
-            "hga_attend_bwd_groups", "hga_status_string", "hga_last_error", "hga_version")
+            "hga_attend_bwd_groups", "hga_diag_gather_sink_words", "hga_diag_gather",
+            "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
 
 
@@ -79,13 +80,17 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
+    L.hga_diag_gather_sink_words.argtypes = [_cfgp, _i64]
+    L.hga_diag_gather_sink_words.restype = ctypes.c_size_t
+    L.hga_diag_gather.argtypes = [_cfgp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t,
+                                  _vp]
     L.hga_attend_bwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
     for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
                "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
-               "hga_attend_bwd_groups"):
+               "hga_attend_bwd_groups", "hga_diag_gather"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
@@ -235,12 +240,21 @@ def _m_attend_bwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, d
             ws_bytes, _stream(stream))
 
 
+def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=None):
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), _dev(V, "V", torch.bfloat16),
+            K.shape[1], p0, n_q, _dev(ids, "ids", torch.int32), _dev(sink, "sink", torch.int32),
+            sink.numel(), _stream(stream))
+
+
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
             "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
             "hga_attend_fwd_groups": _m_attend_fwd_groups,
-            "hga_attend_bwd_groups": _m_attend_bwd_groups}
+            "hga_attend_bwd_groups": _m_attend_bwd_groups,
+            "hga_diag_gather": _m_diag_gather}
 
 
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
@@ -320,6 +334,18 @@ def hga_attend_bwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: 
     _check("hga_attend_bwd_groups", lib().hga_attend_bwd_groups(
         *_m_attend_bwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, dO, dQ, dK, dV, workspace,
                               stream)))
+
+
+def hga_diag_gather_sink_words(cfg: hga_config, n_q: int) -> int:
+    return int(lib().hga_diag_gather_sink_words(ctypes.byref(cfg), n_q))
+
+
+def hga_diag_gather(cfg: hga_config, K: torch.Tensor, V: torch.Tensor, p0: int, n_q: int,
+                    ids: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Diagnostic: read the rows hga_attend_fwd gathers, nothing else (sink is
+    int32 scratch of hga_diag_gather_sink_words words)."""
+    _check("hga_diag_gather", lib().hga_diag_gather(
+        *_m_diag_gather(cfg, K, V, p0, n_q, ids, sink, stream)))
 
 
 def prepare(name: str, *args, **kwargs):

@@ -121,3 +121,42 @@ def test_tiny_against_the_oracle():
     O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, w.p0)
     check_close("fused tiny O", from_dev(b["O"]), O_ref)
     check_close("fused tiny lse", from_dev(b["lse"]), lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+
+
+def test_gather_diagnostic_reads_the_attended_rows():
+    """hga_diag_gather folds exactly the rows the attention gathers: each
+    thread's word is the XOR of its slices of the block's distinct valid
+    routed chunks and local block (recomputed here from the bf16 bits)."""
+    Hq, Hkv, T, n_q, k = 4, 2, 1024, 256, 5
+    x = inputs.small_random(51, Hq, Hkv, 128, T, n_q, bf16=True)
+    p0 = T - n_q
+    ids = np.array([[[3, 1, 3, -1, 40], [0, 12, 13, 2, 2], [-1] * 5, [14, 15, 1, 0, 9]],
+                    [[11, 10, 9, 8, 7], [1, 1, 1, 1, 1], [5, 6, 7, 8, 9], [2, 3, 4, 5, 6]]],
+                   np.int32)
+    cfg = hga.make_config(Hq, Hkv, k)
+    K, V = to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    idd = torch.from_numpy(ids).cuda()
+    sink = torch.empty(hga.hga_diag_gather_sink_words(cfg, n_q), dtype=torch.int32, device="cuda")
+    hga.hga_diag_gather(cfg, K, V, p0, n_q, idd, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    kb = inputs.bf16_bits(x["K"]).view(np.uint16).astype(np.uint32)
+    vb = inputs.bf16_bits(x["V"]).view(np.uint16).astype(np.uint32)
+    # 32-bit words as the kernel reads them: pairs of bf16 (low half first)
+    kw = kb[..., 0::2] | (kb[..., 1::2] << 16)           # [Hkv][T][64]
+    vw = vb[..., 0::2] | (vb[..., 1::2] << 16)
+    nb = n_q // C
+    for g in range(Hkv):
+        for b in range(nb):
+            P = p0 + b * C
+            tiles = sorted({int(c) for c in ids[g, b] if 0 <= c < P // C}) + [P // C]
+            for tid in range(256):
+                acc = 0
+                for c in tiles:
+                    for j in range(4):
+                        r = c * C + (tid >> 4) + 16 * j
+                        sl = slice(4 * (tid & 15), 4 * (tid & 15) + 4)
+                        for wds in (kw[g, r, sl], vw[g, r, sl]):
+                            for wd in wds:
+                                acc ^= int(wd)
+                assert got[(b * Hkv + g) * 256 + tid] == acc, (g, b, tid)
