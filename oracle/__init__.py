@@ -49,17 +49,17 @@ def _load():
     lib.oracle_get_threads.restype = ctypes.c_int
     lib.oracle_summarize.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _f64p, _i64]
     lib.oracle_route.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
-                                 _f64p, _i64, _i64, _i32p, ctypes.c_void_p]
+                                 _f64p, _i64, _i64, _i32p, ctypes.c_void_p, _i64]
     lib.oracle_route_groups.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                         _i64, _f64p, _i64, _i32p, _i64, _i64, _i32p,
-                                        ctypes.c_void_p]
+                                        ctypes.c_void_p, _i64]
     lib.oracle_attend_fwd.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _i32p, _i64,
-                                      ctypes.c_double, ctypes.c_void_p, _f64p, _f64p]
+                                      ctypes.c_double, ctypes.c_void_p, _f64p, _f64p, _i64]
     lib.oracle_attend_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _i64, _i32p, _i64,
                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
-                                      _f64p, _f64p, _f64p]
+                                      _f64p, _f64p, _f64p, _i64]
     _lib = lib
     return lib
 
@@ -100,8 +100,11 @@ def summarize(K, C: int, c_begin: int, c_end: int, out=None, n_cap: int | None =
     return out
 
 
-def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_scores=False):
-    """Per (kv head, block) top-k chunk ids, ascending, -1 padded.
+def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_scores=False,
+          sink: int = 0):
+    """Per (kv head, block) top-k chunk ids, ascending, -1 padded. Candidates
+    are the closed chunks before the block that lie past the first ``sink``
+    tokens (the sink window, attended by every block; a multiple of C).
 
     Returns ids [Hkv][n_blocks][k] int32 (and sigma [Hkv][n_blocks][n_cap]
     float64, NaN for ineligible chunks, if want_scores)."""
@@ -113,15 +116,17 @@ def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_score
     n_blocks = n_q // Bq
     ids = np.empty((Hkv, n_blocks, k), dtype=np.int32)
     sig = np.empty((Hkv, n_blocks, n_cap)) if want_scores else None
+    assert sink % C == 0 and sink >= 0
     _load().oracle_route(Q, Hq, Hkv, n_q, D, p0, C, Bq, S, n_cap, k, ids,
-                         sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None)
+                         sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None, sink)
     return (ids, sig) if want_scores else ids
 
 
 def route_groups(Q, SG, p0: int, chunk_ids, m: int, Hkv: int, C: int = 64, Bq: int = 64,
-                 U: int = 8, want_scores=False):
+                 U: int = 8, want_scores=False, sink: int = 0):
     """Per (kv head, block) top-m groups of U tokens among the groups of the
-    block's routed chunks (chunk_ids [Hkv][n_blocks][k]), ascending, -1 padded.
+    block's routed chunks (chunk_ids [Hkv][n_blocks][k]) past the first
+    ``sink`` tokens, ascending, -1 padded.
 
     SG holds group summaries [Hkv][n_gcap][D] (summarize with C = U). Returns
     gids [Hkv][n_blocks][m] int32 (and sigma [Hkv][n_blocks][n_gcap] float64,
@@ -136,15 +141,18 @@ def route_groups(Q, SG, p0: int, chunk_ids, m: int, Hkv: int, C: int = 64, Bq: i
     assert chunk_ids.shape[:2] == (Hkv, n_blocks)
     gids = np.empty((Hkv, n_blocks, m), dtype=np.int32)
     sig = np.empty((Hkv, n_blocks, n_gcap)) if want_scores else None
+    assert sink % C == 0 and sink >= 0
     _load().oracle_route_groups(Q, Hq, Hkv, n_q, D, p0, C, Bq, U, SG, n_gcap, chunk_ids,
                                 chunk_ids.shape[2], m, gids,
-                                sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None)
+                                sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None,
+                                sink)
     return (gids, sig) if want_scores else gids
 
 
 def attend_fwd(Q, K, V, ids, p0: int, C: int = 64, Bq: int = 64, scale: float | None = None,
-               unit_mask=None):
-    """Exact attention over the routed units + causal local block. ids count
+               unit_mask=None, sink: int = 0):
+    """Exact attention over the first ``sink`` tokens (the sink window; a
+    multiple of C), the routed units and the causal local block. ids count
     units of C tokens: chunks (C = 64) or groups (C = 8, with Bq = 64).
 
     Returns (O [Hq][n_q][D], lse [Hq][n_q]) float64; rows of units excluded by
@@ -159,15 +167,17 @@ def attend_fwd(Q, K, V, ids, p0: int, C: int = 64, Bq: int = 64, scale: float | 
     O = np.full((Hq, n_q, D), np.nan)
     lse = np.full((Hq, n_q), np.nan)
     m, mp = _mask_ptr(unit_mask)
+    assert sink % C == 0 and sink >= 0
     _load().oracle_attend_fwd(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k,
-                              float(scale), mp, O, lse)
+                              float(scale), mp, O, lse, sink)
     return O, lse
 
 
 def attend_bwd(Q, K, V, dO, ids, p0: int, C: int = 64, Bq: int = 64,
-               scale: float | None = None, dq_mask=None, dkv_mask=None):
+               scale: float | None = None, dq_mask=None, dkv_mask=None, sink: int = 0):
     """Gradients of sum(O * dO): dQ [Hq][n_q][D], and dK, dV [Hkv][n_q][D] for
-    the active keys p0 .. p0+n_q-1 only (history detached)."""
+    the active keys p0 .. p0+n_q-1 only (history detached); the attended set
+    as in attend_fwd, sink window included."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
     Hq, n_q, D = Q.shape
     Hkv, T, _ = K.shape
@@ -180,6 +190,7 @@ def attend_bwd(Q, K, V, dO, ids, p0: int, C: int = 64, Bq: int = 64,
     dV = np.full((Hkv, n_q, D), np.nan)
     m1, p1 = _mask_ptr(dq_mask)
     m2, p2 = _mask_ptr(dkv_mask)
+    assert sink % C == 0 and sink >= 0
     _load().oracle_attend_bwd(Q, K, V, dO, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k,
-                              float(scale), p1, p2, dQ, dK, dV)
+                              float(scale), p1, p2, dQ, dK, dV, sink)
     return dQ, dK, dV

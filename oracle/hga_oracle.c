@@ -99,7 +99,9 @@ void oracle_summarize(const float *K, int64_t Hkv, int64_t T, int64_t D,
  * P = p0 + b*Bq):
  *     qbar[d]  = mean over the G query heads h of group g and the Bq queries i
  *                of block b of Q[h][i][d]
- *     E        = { c : (c + 1) * C <= P }           closed, causally earlier
+ *     E        = { c : sink <= c * C, (c + 1) * C <= P }   closed, causally
+ *                earlier, not in the sink window (the first `sink` tokens,
+ *                which every block attends anyway; a multiple of C)
  *     sigma_c  = sum_d qbar[d] * S[g][c][d]
  *     keep the first min(k, |E|) chunks of E ordered by (sigma desc, c asc),
  *     write them in ascending id order, pad with -1.
@@ -126,7 +128,7 @@ static int by_id_asc(const void *pa, const void *pb)
 void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
                   int64_t D, int64_t p0, int64_t C, int64_t Bq,
                   const double *S, int64_t n_cap, int64_t k,
-                  int32_t *ids, double *sigma_out)
+                  int32_t *ids, double *sigma_out, int64_t sink)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -134,8 +136,10 @@ void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
     for (int64_t u = 0; u < Hkv * n_blocks; ++u) {
         int64_t g = u / n_blocks, b = u % n_blocks;
         int64_t P = p0 + b * Bq;
-        int64_t nE = P / C;                 /* chunks c with (c+1)*C <= P */
-        if (nE > n_cap) nE = n_cap;
+        int64_t c_hi = P / C;               /* chunks c with (c+1)*C <= P */
+        if (c_hi > n_cap) c_hi = n_cap;
+        int64_t c_lo = (sink + C - 1) / C;  /* first chunk past the sink */
+        int64_t nE = c_hi > c_lo ? c_hi - c_lo : 0;
 
         double *qbar = (double *)malloc((size_t)D * sizeof(double));
         for (int64_t d = 0; d < D; ++d) {
@@ -147,17 +151,18 @@ void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
         }
 
         scored_chunk *cand = (scored_chunk *)malloc((size_t)(nE > 0 ? nE : 1) * sizeof(scored_chunk));
-        for (int64_t c = 0; c < nE; ++c) {
+        for (int64_t e = 0; e < nE; ++e) {
+            int64_t c = c_lo + e;
             double sigma = 0.0;
             for (int64_t d = 0; d < D; ++d)
                 sigma += qbar[d] * S[(g * n_cap + c) * D + d];
-            cand[c].sigma = sigma;
-            cand[c].c = c;
+            cand[e].sigma = sigma;
+            cand[e].c = c;
         }
         if (sigma_out) {
             double *row = sigma_out + (g * n_blocks + b) * n_cap;
             for (int64_t c = 0; c < n_cap; ++c) row[c] = NAN;
-            for (int64_t c = 0; c < nE; ++c) row[c] = cand[c].sigma;
+            for (int64_t e = 0; e < nE; ++e) row[cand[e].c] = cand[e].sigma;
         }
 
         qsort(cand, (size_t)nE, sizeof(scored_chunk), by_score_desc_then_id);
@@ -181,7 +186,9 @@ void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
  * With U tokens per group (C % U == 0) and group summaries SG[g][u] = mean of
  * the U keys of group u (oracle_summarize with C = U), for kv head g and query
  * block b (qbar as in oracle_route):
- *     Ch       = the chunk ids of chunk_ids[g][b] with 0 <= c < P/C, as a set
+ *     Ch       = the chunk ids of chunk_ids[g][b] with sink <= c*C and
+ *                c < P/C, as a set (chunks of the sink window are attended
+ *                whole anyway)
  *     cand     = { u : u / (C/U) in Ch }              the groups of those chunks
  *     sigma_u  = sum_d qbar[d] * SG[g][u][d]
  *     keep the first min(m, |cand|) groups ordered by (sigma desc, u asc),
@@ -194,7 +201,7 @@ void oracle_route_groups(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
                          int64_t D, int64_t p0, int64_t C, int64_t Bq, int64_t U,
                          const double *SG, int64_t n_gcap,
                          const int32_t *chunk_ids, int64_t k, int64_t m,
-                         int32_t *gids, double *sigma_out)
+                         int32_t *gids, double *sigma_out, int64_t sink)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -219,7 +226,7 @@ void oracle_route_groups(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
         int64_t n_ch = 0;
         for (int64_t r = 0; r < k; ++r) {
             int64_t c = row[r];
-            if (c < 0 || c >= P / C) continue;
+            if (c < 0 || c >= P / C || c * C < sink) continue;
             int dup = 0;
             for (int64_t q = 0; q < n_ch; ++q) dup |= chs[q] == c;
             if (!dup) chs[n_ch++] = c;
@@ -261,20 +268,23 @@ void oracle_route_groups(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
  * selected units enter attention; summaries are never attention values).
  * For active query i (absolute position p = p0 + i) in block b = i / Bq with
  * first position P = p0 + b*Bq and kv head g:
- *     A(i) = union over listed chunks c with 0 <= c < P/C of [cC, cC + C)
+ *     A(i) = [0, min(sink, P))                        the sink window
+ *            united with the listed units c with 0 <= c < P/C of [cC, cC + C)
  *            united with the causal local block [P, p].
- * The listed chunk set is taken as a set (a repeated id adds nothing).
+ * The listed units are taken as a set (a repeated id adds nothing), and a unit
+ * inside the sink window adds nothing either (sink is a multiple of C).
  * Returns the number of positions written to pos (ascending within each part).
  */
 static int64_t attended_positions(const int32_t *ids_gb, int64_t k, int64_t C,
                                   int64_t P, int64_t p, int64_t *pos,
-                                  unsigned char *seen, int64_t n_seen)
+                                  unsigned char *seen, int64_t n_seen, int64_t sink)
 {
     int64_t n = 0;
+    for (int64_t t = 0; t < sink && t < P; ++t) pos[n++] = t;
     memset(seen, 0, (size_t)n_seen);
     for (int64_t r = 0; r < k; ++r) {
         int64_t c = ids_gb[r];
-        if (c < 0 || c >= P / C || c >= n_seen || seen[c]) continue;
+        if (c < 0 || c >= P / C || c >= n_seen || c * C < sink || seen[c]) continue;
         seen[c] = 1;
     }
     for (int64_t c = 0; c < n_seen; ++c)
@@ -285,9 +295,10 @@ static int64_t attended_positions(const int32_t *ids_gb, int64_t k, int64_t C,
 }
 
 static int is_attended(const int32_t *ids_gb, int64_t k, int64_t C,
-                       int64_t P, int64_t p, int64_t j)
+                       int64_t P, int64_t p, int64_t j, int64_t sink)
 {
     if (j >= P) return j <= p;
+    if (j < sink) return 1;
     int64_t c = j / C;
     if (c >= P / C) return 0;
     for (int64_t r = 0; r < k; ++r)
@@ -316,7 +327,7 @@ void oracle_attend_fwd(const float *Q, const float *K, const float *V,
                        int64_t Hq, int64_t Hkv, int64_t D, int64_t T,
                        int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
                        const int32_t *ids, int64_t k, double scale,
-                       const uint8_t *unit_mask, double *O, double *lse)
+                       const uint8_t *unit_mask, double *O, double *lse, int64_t sink)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -334,7 +345,7 @@ void oracle_attend_fwd(const float *Q, const float *K, const float *V,
             if (unit_mask && !unit_mask[h * n_blocks + b]) continue;
             int64_t P = p0 + b * Bq, p = p0 + i;
             const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
-            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks);
+            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks, sink);
             const float *q = Q + (h * n_q + i) * D;
 
             double m = -INFINITY;
@@ -377,7 +388,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
                        int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
                        const int32_t *ids, int64_t k, double scale,
                        const uint8_t *dq_mask, const uint8_t *dkv_mask,
-                       double *dQ, double *dK, double *dV)
+                       double *dQ, double *dK, double *dV, int64_t sink)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -388,7 +399,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
 
     /* pass 1: lse, O and Delta for every active query */
     oracle_attend_fwd(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k, scale,
-                      NULL, Obuf, lse);
+                      NULL, Obuf, lse, sink);
 #pragma omp parallel for schedule(static)
     for (int64_t row = 0; row < Hq * n_q; ++row) {
         double s = 0.0;
@@ -410,7 +421,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
             if (dq_mask && !dq_mask[h * n_blocks + b]) continue;
             int64_t P = p0 + b * Bq, p = p0 + i;
             const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
-            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks);
+            int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks, sink);
             const float *q = Q + row * D;
             const float *go = dO + row * D;
             for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
@@ -441,7 +452,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
             for (int64_t h = g * G; h < g * G + G; ++h) {
                 for (int64_t i = 0; i < n_q; ++i) {
                     int64_t b = i / Bq, P = p0 + b * Bq, p = p0 + i;
-                    if (!is_attended(ids + (g * n_blocks + b) * k, k, C, P, p, j))
+                    if (!is_attended(ids + (g * n_blocks + b) * k, k, C, P, p, j, sink))
                         continue;
                     int64_t row = h * n_q + i;
                     const float *q = Q + row * D;

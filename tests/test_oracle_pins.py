@@ -578,3 +578,126 @@ def test_attend_groups_matches_masked_sdpa_and_autograd():
     np.testing.assert_allclose(dQ, q.grad.numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(dK, kk.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(dV, vv.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------------ sink window
+# (gist.science technical summary 2.1: the chosen chunks come alongside fixed
+# sink and local windows; the sink is read here as the first `sink` tokens, a
+# whole number of chunks, attended by every block past them and kept out of
+# the routing candidates.)
+
+def _mask_with_sink(ids, Hq, Hkv, n_q, p0, T, C, Bq, sink):
+    M = _mask_from_ids(ids, Hq, Hkv, n_q, p0, T, C, Bq)
+    for i in range(n_q):
+        P = p0 + (i // Bq) * Bq
+        M[:, i, :min(sink, P)] = True
+    return M
+
+
+@pytest.mark.parametrize("s", [1, 3])
+def test_sink_routing_is_routing_of_the_history_past_the_sink(s):
+    """Cutting the s sink chunks off the front (positions and ids shifted)
+    must not change which chunks are chosen."""
+    C, Bq, k, Hkv = 8, 8, 4, 2
+    x = _tiny(60 + s, T=256, n_q=64, C=C)
+    p0 = 192
+    S = oracle.summarize(x["K"], C, 0, 256 // C)
+    ids, sig = oracle.route(x["Q"], S, p0, k, Hkv, C, Bq, want_scores=True, sink=s * C)
+    ref, ref_sig = oracle.route(x["Q"], S[:, s:], p0 - s * C, k, Hkv, C, Bq, want_scores=True)
+    np.testing.assert_array_equal(ids, np.where(ref >= 0, ref + s, -1))
+    # the candidate set itself shifts by s chunks: chunk s is the first candidate
+    assert np.all(np.isnan(sig[:, :, :s]))
+    np.testing.assert_array_equal(sig[:, :, s:], ref_sig)
+    assert np.all(np.isfinite(sig[:, :, s]))
+
+
+@pytest.mark.parametrize("k,s", [(0, 2), (3, 1), (3, 5)])
+def test_sink_attention_matches_masked_sdpa(k, s):
+    Hq, Hkv, D, T, n_q, C, Bq = 4, 2, 16, 256, 64, 8, 16
+    x = _tiny(70 + k + s, Hq, Hkv, D, T, n_q, C)
+    p0 = T - n_q
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(x["Q"], S, p0, k, Hkv, C, Bq, sink=s * C)
+    # a caller-made id inside the sink adds nothing
+    if k:
+        ids[0, 0, 0] = 0
+    O, lse = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0, C, Bq, sink=s * C)
+    M = _mask_with_sink(ids, Hq, Hkv, n_q, p0, T, C, Bq, s * C)
+    O_ref, lse_ref = _sdpa_masked(x["Q"], x["K"], x["V"], M, 1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sink_over_the_whole_history_is_dense_causal_attention():
+    Hq, Hkv, D, T, n_q, C, Bq = 2, 1, 16, 128, 64, 8, 16
+    x = _tiny(80, Hq, Hkv, D, T, n_q, C)
+    p0 = T - n_q
+    ids = np.full((Hkv, n_q // Bq, 2), -1, np.int32)
+    O, lse = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0, C, Bq, sink=T)
+    q = torch.from_numpy(x["Q"].astype(np.float64))
+    kk = torch.from_numpy(np.repeat(x["K"].astype(np.float64), Hq // Hkv, 0))
+    vv = torch.from_numpy(np.repeat(x["V"].astype(np.float64), Hq // Hkv, 0))
+    causal = torch.from_numpy(np.arange(T)[None, :] <= (p0 + np.arange(n_q))[:, None])
+    O_ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, attn_mask=causal,
+                                                             scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_sink_backward_matches_autograd():
+    Hq, Hkv, D, T, n_q, C, Bq = 4, 2, 16, 256, 64, 8, 16
+    x = _tiny(81, Hq, Hkv, D, T, n_q, C, with_dO=True)
+    p0, s = T - n_q, 2
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(x["Q"], S, p0, 3, Hkv, C, Bq, sink=s * C)
+    dQ, dK, dV = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], ids, p0, C, Bq,
+                                   sink=s * C)
+    M = _mask_with_sink(ids, Hq, Hkv, n_q, p0, T, C, Bq, s * C)
+    G = Hq // Hkv
+    q = torch.tensor(x["Q"], dtype=torch.float64, requires_grad=True)
+    kk = torch.tensor(x["K"], dtype=torch.float64, requires_grad=True)
+    vv = torch.tensor(x["V"], dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q, kk.repeat_interleave(G, 0), vv.repeat_interleave(G, 0),
+        attn_mask=torch.from_numpy(M), scale=1 / math.sqrt(D))
+    (out * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(dQ, q.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dK, kk.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dV, vv.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+
+
+def test_sink_backward_with_active_sink_chunks():
+    # p0 = 0: the sink chunks are active keys, attended by every later block
+    Hq, Hkv, D, T, n_q, C, Bq = 2, 1, 16, 128, 128, 8, 16
+    x = _tiny(82, Hq, Hkv, D, T, n_q, C, with_dO=True)
+    s = 3
+    ids = oracle.route(x["Q"], oracle.summarize(x["K"], C, 0, T // C), 0, 2, Hkv, C, Bq,
+                       sink=s * C)
+    dQ, dK, dV = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], ids, 0, C, Bq, sink=s * C)
+    M = _mask_with_sink(ids, Hq, Hkv, n_q, 0, T, C, Bq, s * C)
+    q = torch.tensor(x["Q"], dtype=torch.float64, requires_grad=True)
+    kk = torch.tensor(x["K"], dtype=torch.float64, requires_grad=True)
+    vv = torch.tensor(x["V"], dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q, kk.repeat_interleave(Hq, 0), vv.repeat_interleave(Hq, 0),
+        attn_mask=torch.from_numpy(M), scale=1 / math.sqrt(D))
+    (out * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(dK, kk.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dV, vv.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def test_route_groups_ignores_chunks_inside_the_sink():
+    x, p0, ids, SG = _group_setup(83)
+    s = 2
+    rows = ids.copy()
+    rows[:, :, 0] = 0                      # chunk 0 and 1 sit in a 128-token sink
+    rows[:, 1, 1] = 1
+    g_sink = oracle.route_groups(x["Q"], SG, p0, rows, 12, 2, sink=s * 64)
+    cleaned = np.where(rows < s, -1, rows)
+    g_ref = oracle.route_groups(x["Q"], SG, p0, cleaned, 12, 2)
+    np.testing.assert_array_equal(g_sink, g_ref)
+    # group attention with the sink: the mask definition, in 8-token units
+    Hq, Hkv, D, T, n_q = 4, 2, 16, 1024, 128
+    O, lse = oracle.attend_fwd(x["Q"], x["K"], x["V"], g_sink, p0, 8, 64, sink=s * 64)
+    M = _mask_with_sink(g_sink, Hq, Hkv, n_q, p0, T, 8, 64, s * 64)
+    O_ref, lse_ref = _sdpa_masked(x["Q"], x["K"], x["V"], M, 1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref, rtol=1e-11, atol=1e-12)
