@@ -365,6 +365,11 @@ def attend_timings(torch, hga, inputs, dev):
         else:
             res["layer16k_route_us"] = med(hga.prepare("hga_route", cfg, Q, w.p0, S, w.T // C,
                                                        ids)) * 1e3
+            # routing + attention with a one-chunk sink window (64 more keys per query)
+            cfg_s = hga.make_config(w.Hq, w.Hkv, w.k, sink_chunks=1)
+            ids_s = torch.empty_like(ids)
+            res["layer16k_sink1_route_attend_us"] = med(hga.prepare(
+                "hga_route_attend_fwd", cfg_s, Q, K, V, w.p0, S, w.T // C, ids_s, O, lse)) * 1e3
             res["layer16k_attend_us"] = med(run) * 1e3
             flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
             ms_cold = med(run, pre=lambda: flush.fill_(1))

@@ -63,7 +63,20 @@ typedef struct hga_config {
     int32_t top_k;          /* k; 0 .. 256 routed chunks per query block       */
     float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                   */
     int32_t dtype;          /* HGA_BF16                                        */
+    int32_t sink_chunks;    /* s: 0 .. HGA_MAX_SINK_CHUNKS; see below          */
 } hga_config;
+
+/*
+ * Sink window (technical summary 2.1: the chosen chunks come alongside fixed
+ * sink and local windows; the pages give no size). The first s chunks,
+ * tokens [0, sC), are attended by every query block whose first position P is
+ * past them (tokens [0, min(sC, P))), and are not routing candidates: with
+ * s > 0, hga_route's candidates become the chunks c with s <= c < P/C, an id
+ * row's entries below s add nothing to the attended set (they are in it
+ * already), and the group level treats sink chunks the same way. s = 0 is the
+ * method without a sink.
+ */
+#define HGA_MAX_SINK_CHUNKS 64
 
 /*
  * hga_summarize -- append chunk summaries (technical summary 2.1, chunk
@@ -90,9 +103,10 @@ hga_status hga_summarize(const hga_config *cfg, const void *K, int64_t T_cap,
  * and block b, first query position P = p0 + b*Bq:
  *     qbar    = mean of Q[h][i] over the G heads of group g and the Bq
  *               queries of block b (fp32)
- *     score_c = qbar . summaries[g][c]     for every chunk c < P/C (fp32)
- *     ids[g][b][:] = the min(k, P/C) chunks of highest score, ties to the
- *               lower chunk id, written in ascending id order, then -1.
+ *     score_c = qbar . summaries[g][c]     for every chunk s <= c < P/C (fp32;
+ *               s = cfg->sink_chunks, see hga_config)
+ *     ids[g][b][:] = the min(k, P/C - s) chunks of highest score, ties to
+ *               the lower chunk id, written in ascending id order, then -1.
  *   Q              device bf16 [Hq][n_q][D]
  *   summaries      device f32 [Hkv][n_chunk_cap][D]; rows 0 .. n_chunks_valid-1
  *                  must hold summaries. Needs (p0 + n_q - Bq)/C <= n_chunks_valid
@@ -112,7 +126,8 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
  * causal local block (technical summary 2.1: only the exact K/V of the
  * selected units enter attention; summaries never act as values). For query
  * i (position p = p0 + i, block b, head h, kv head g = h/G):
- *     A(i) = union_{c in ids[g][b], 0 <= c < P/C} [cC, cC+C)  U  [P, p]
+ *     A(i) = [0, min(sC, P))  U  union_{c in ids[g][b], s <= c < P/C} [cC, cC+C)
+ *            U  [P, p]                 (s = cfg->sink_chunks, the sink window)
  *     z_j  = scale * Q[h][i] . K[g][j]
  *     O[h][i]   = sum_{j in A(i)} softmax(z)_j V[g][j]      (bf16, RNE)
  *     lse[h][i] = ln sum_{j in A(i)} exp(z_j)                (f32)

@@ -167,14 +167,14 @@ void bwd_dq_kernel(
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
     int64_t n_q, int64_t Hkv, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids,
-    int k, float scale_log2, float scale, float *__restrict__ dQ)
+    int k, int sink, float scale_log2, float scale, float *__restrict__ dQ)
 {
     constexpr int HW = G < 4 ? G : 4;
     constexpr int NHG = G / HW;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Kts[2][kTTile];
-    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 1];
+    __shared__ int list[(kUnit == kC ? kChunkListMax : kGroupListMax) + 1];
     __shared__ int list_n;
 
     const int tid = threadIdx.x;
@@ -190,12 +190,16 @@ void bwd_dq_kernel(
     const uint16_t *Kg = K + g * T_cap * kD;
     const uint16_t *Vg = V + g * T_cap * kD;
 
-    // routed units (0 <= u < P/kUnit, repeats dropped), then the local chunk
+    // the sink window's units, the routed units (past the sink, before P,
+    // repeats dropped), then the local chunk
     if (wave == 0) {
-        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, P / kUnit, list);
+        const int ns = sink_units(sink, P, kUnit);
+        write_sink_units(list, ns);
+        const int n = build_unit_list(ids + (g * n_blocks + b) * k, k,
+                                      (int64_t)sink * (kC / kUnit), P / kUnit, list + ns);
         if (lane == 0) {
-            list[n - 1] = (int)local_chunk;
-            list_n = n;
+            list[ns + n] = (int)local_chunk;
+            list_n = ns + n + 1;
         }
     }
     // the dkdv kernel that follows counts finished workgroups per (kv head, chunk)
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, int64_t n_q,
-    int64_t Hkv, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k,
+    int64_t Hkv, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k, int sink,
     float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV,
     float *__restrict__ part, int *__restrict__ counters)
 {
@@ -430,9 +434,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int64_t ca = p0 / kC + a;               // absolute chunk index
 
     // Query blocks that attend chunk a: its own (causal) and every later block
-    // whose routed ids list it (or, for group ids, any of its groups), in
-    // ascending block order, each with the mask of the chunk's groups it
-    // attends. The four waves scan the later blocks' id rows (wave w: blocks
+    // whose routed ids list it (or, for group ids, any of its groups) -- every
+    // later block if the chunk lies in the sink window -- in ascending block
+    // order, each with the mask of the chunk's groups it attends. The four waves scan the later blocks' id rows (wave w: blocks
     // a+1+w, a+5+w, ...), each row spread over the 64 lanes and kScanRows rows
     // loaded before any is used; the masks land in LDS by block and wave 0
     // then lists the blocks in order.
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
             for (int rr = 0; rr < kScanRows; ++rr) {
                 const int64_t bb = base + 4 * rr;
+                if (ca < sink) msk[rr] = 0xFFu;
                 if (lane == 0 && bb < n_blocks) rmask[bb] = (uint8_t)msk[rr];
             }
         }
@@ -766,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 template <int G, int kUnit>
 hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                         int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
-                        const int32_t *ids, int32_t k, float scale, const float *lse,
+                        const int32_t *ids, int32_t k, int32_t sink, float scale, const float *lse,
                         const uint16_t *dO, float *dQ, float *dK, float *dV,
                         float *delta, int *counters, float *part, hipStream_t stream)
 {
@@ -775,12 +780,12 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     const float scale_log2 = scale * 1.44269504088896340736f;
     hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kDqThreads),
                        0, stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, T_cap, p0, ids,
-                       k, scale_log2, scale, dQ);
+                       k, (int)sink, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * kSplit)),
                        dim3(kThreads), 0, stream, Q, K, V, dO, lse, delta, n_q, Hkv, T_cap, p0,
-                       ids, k, scale_log2, scale, dK, dV, part, counters);
+                       ids, k, (int)sink, scale_log2, scale, dK, dV, part, counters);
     return hipGetLastError();
 }
 
@@ -815,8 +820,8 @@ namespace {
 template <int kUnit>
 hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                            int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
-                           const int32_t *ids, int32_t k, float scale, const float *lse,
-                           const uint16_t *dO, float *dQ, float *dK, float *dV,
+                           const int32_t *ids, int32_t k, int32_t sink, float scale,
+                           const float *lse, const uint16_t *dO, float *dQ, float *dK, float *dV,
                            void *workspace, hipStream_t stream)
 {
     if (n_q == 0) return hipSuccess;
@@ -826,10 +831,10 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
     int *counters = (int *)(ws + w.counter_off);
     float *part = (float *)(ws + w.part_off);
     switch (Hq / Hkv) {
-    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -838,24 +843,24 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
 
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                              int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
-                             int64_t n_q, const int32_t *ids, int32_t k, float scale,
-                             const uint16_t *O, const float *lse, const uint16_t *dO,
-                             float *dQ, float *dK, float *dV, void *workspace,
-                             hipStream_t stream)
+                             int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
+                             float scale, const uint16_t *O, const float *lse,
+                             const uint16_t *dO, float *dQ, float *dK, float *dV,
+                             void *workspace, hipStream_t stream)
 {
     (void)O;    // Delta is recomputed from P and dP (see the dq kernel)
-    return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, lse, dO, dQ,
-                               dK, dV, workspace, stream);
+    return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO,
+                               dQ, dK, dV, workspace, stream);
 }
 
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                     int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
-                                    int64_t n_q, const int32_t *gids, int32_t m, float scale,
-                                    const float *lse, const uint16_t *dO, float *dQ, float *dK,
-                                    float *dV, void *workspace, hipStream_t stream)
+                                    int64_t n_q, const int32_t *gids, int32_t m, int32_t sink,
+                                    float scale, const float *lse, const uint16_t *dO, float *dQ,
+                                    float *dK, float *dV, void *workspace, hipStream_t stream)
 {
-    return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, scale, lse, dO,
-                                   dQ, dK, dV, workspace, stream);
+    return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, sink, scale, lse,
+                                   dO, dQ, dK, dV, workspace, stream);
 }
 
 }  // namespace hga

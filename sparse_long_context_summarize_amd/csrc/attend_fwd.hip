@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int64_t T_cap,
-    int64_t p0, int32_t *__restrict__ ids, int k, float scale_log2,
+    int64_t p0, int32_t *__restrict__ ids, int k, int sink, float scale_log2,
     uint16_t *__restrict__ O, float *__restrict__ lse,
     const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores)
 {
@@ -185,7 +185,7 @@ void attend_fwd_kernel(
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kVtTile];
-    __shared__ int list[(kUnit == kC ? kMaxTopK : kMaxGroupTopK) + 2];
+    __shared__ int list[(kUnit == kC ? kChunkListMax : kGroupListMax) + 1];
     __shared__ int list_n;
     __shared__ __attribute__((aligned(16))) uint16_t Os[8][32 * kOStride];
 
@@ -226,14 +226,17 @@ void attend_fwd_kernel(
     TileRegs r0, r1;
     if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
 
-    // Unit list: the local chunk, then the valid routed ids (0 <= u <
-    // P/kUnit) in order, repeats dropped.
+    // Unit list: the local chunk, the sink window's units, then the valid
+    // routed ids (past the sink, before P) in order, repeats dropped.
+    const int n_sink = sink_units(sink, P, kUnit);
     if constexpr (kRouteNI == 0) {
         if (wave == 0) {
-            const int n = build_chunk_list(id_row, k, P / kUnit, list + 1, id_first);
+            write_sink_units(list + 1, n_sink);
+            const int n = build_unit_list(id_row, k, (int64_t)sink * (kC / kUnit), P / kUnit,
+                                          list + 1 + n_sink, id_first);
             if (lane == 0) {
                 list[0] = (int)local_chunk;
-                list_n = n;
+                list_n = 1 + n_sink + n;
             }
         }
     } else {
@@ -273,17 +276,20 @@ void attend_fwd_kernel(
         float *sc_row = (scores && wr) ? scores + (g * n_blocks + b) * k : nullptr;
         constexpr int kBatchR = G >= 8 ? 4 : 8;
         const int n_sel = route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
-            sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, nullptr, 0,
+            sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, nullptr, 0, sink,
             [&](int r, int id, float sc) __attribute__((always_inline)) {
-                list[1 + r] = id;
+                list[1 + n_sink + r] = id;
                 if (wr) {
                     id_row[r] = id;
                     if (sc_row) sc_row[r] = sc;
                 }
             });
-        if (wave == 0 && lane == 0) {
-            list[0] = (int)local_chunk;
-            list_n = n_sel + 1;
+        if (wave == 0) {
+            write_sink_units(list + 1, n_sink);
+            if (lane == 0) {
+                list[0] = (int)local_chunk;
+                list_n = 1 + n_sink + n_sel;
+            }
         }
     }
     __syncthreads();
@@ -536,6 +542,7 @@ struct FwdArgs {
     int64_t Hq, Hkv, T_cap, p0, n_q;
     int32_t *ids;
     int32_t k;
+    int32_t sink;
     float scale;
     uint16_t *O;
     float *lse;
@@ -552,8 +559,8 @@ hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
     const float scale_log2 = a.scale * 1.44269504088896340736f;
     hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit, kRouteNI>),
                        dim3((unsigned)(n_blocks * a.Hkv * NHG)), dim3(kThreads), 0, stream,
-                       a.Q, a.K, a.V, a.n_q, a.Hkv, a.T_cap, a.p0, a.ids, a.k, scale_log2, a.O,
-                       a.lse, a.S, a.n_cap, a.scores);
+                       a.Q, a.K, a.V, a.n_q, a.Hkv, a.T_cap, a.p0, a.ids, a.k, (int)a.sink,
+                       scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
     return hipGetLastError();
 }
 
@@ -575,22 +582,22 @@ hipError_t launch_unit(const FwdArgs &a, hipStream_t stream)
 hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, float scale,
+                             const int32_t *ids, int32_t k, int32_t sink, float scale,
                              uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(ids), k, scale, O,
-                    lse, nullptr, 0, nullptr};
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(ids), k, sink,
+                    scale, O, lse, nullptr, 0, nullptr};
     return launch_unit<kC, 0>(a, stream);
 }
 
 hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     const uint16_t *V, int64_t Hq, int64_t Hkv,
                                     int64_t T_cap, int64_t p0, int64_t n_q,
-                                    const int32_t *gids, int32_t m, float scale,
+                                    const int32_t *gids, int32_t m, int32_t sink, float scale,
                                     uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(gids), m, scale, O,
-                    lse, nullptr, 0, nullptr};
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(gids), m, sink,
+                    scale, O, lse, nullptr, 0, nullptr};
     return launch_unit<kGroup, 0>(a, stream);
 }
 
@@ -602,14 +609,15 @@ int64_t route_attend_max_candidates()
 hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                    int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                                   float scale, int32_t *ids, float *scores, uint16_t *O,
-                                   float *lse, hipStream_t stream)
+                                   int32_t sink, float scale, int32_t *ids, float *scores,
+                                   uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, scale, O, lse, S, n_cap, scores};
+    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, S, n_cap,
+                    scores};
     if (k == 0) return launch_unit<kC, 0>(a, stream);
     // keys per lane of the router's register selection: the smallest class
     // that holds the largest candidate count (beyond 2048 the LDS path)
-    const int64_t max_eligible = (p0 + n_q - kC) / kC;
+    const int64_t max_eligible = (p0 + n_q - kC) / kC - sink;
     if (max_eligible <= 4 * 64) return launch_unit<kC, 4>(a, stream);
     if (max_eligible <= 8 * 64) return launch_unit<kC, 8>(a, stream);
     if (max_eligible <= 16 * 64) return launch_unit<kC, 16>(a, stream);

@@ -1,6 +1,7 @@
 // diag.hip -- gather-only diagnostic: the K/V tiles hga_attend_fwd gathers
-// (every routed chunk of the block's id row and the local block, per (query
-// block, kv head)), read with the attention kernel's addressing and 16-byte
+// (the sink window, every routed chunk of the block's id row and the local
+// block, per (query block, kv head)), read with the attention kernel's
+// addressing and 16-byte
 // loads and folded by XOR into one word per thread, with no arithmetic of the
 // method. Its time is the ceiling the gather alone sets for the attention
 // kernel (arXiv 2607.15105, gist.science technical summary 2.1: only the exact
@@ -14,19 +15,25 @@ constexpr int kGatherThreads = 256;
 
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv,
-    int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k,
+    int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k, int sink_chunks,
     uint32_t *__restrict__ sink)
 {
-    __shared__ int list[kMaxTopK + 1];
+    __shared__ int list[kChunkListMax];
     __shared__ int list_n;
     const int tid = threadIdx.x;
     const int64_t g = blockIdx.x % Hkv;
     const int64_t b = blockIdx.x / Hkv;
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
-    if (tid < 64) {
-        const int n = build_chunk_list(ids + (g * n_blocks + b) * k, k, P / kC, list);
-        if (tid == 0) list_n = n;          // the local chunk (= P / C) is last
+    if (tid < 64) {                         // sink chunks, routed chunks, local chunk
+        const int ns = sink_units(sink_chunks, P, kC);
+        write_sink_units(list, ns);
+        const int n = build_unit_list(ids + (g * n_blocks + b) * k, k, sink_chunks, P / kC,
+                                      list + ns);
+        if (tid == 0) {
+            list[ns + n] = (int)(P / kC);
+            list_n = ns + n + 1;
+        }
     }
     __syncthreads();
     const int n_tiles = list_n;
@@ -68,13 +75,13 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
 }  // namespace
 
 hipError_t launch_gather(const uint16_t *K, const uint16_t *V, int64_t Hkv, int64_t T_cap,
-                         int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, uint32_t *sink,
-                         hipStream_t stream)
+                         int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
+                         uint32_t *sink_out, hipStream_t stream)
 {
     const int64_t n_units = (n_q / kC) * Hkv;
     if (n_units == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_kernel, dim3((unsigned)n_units), dim3(kGatherThreads), 0, stream,
-                       K, V, n_q, Hkv, T_cap, p0, ids, k, sink);
+                       K, V, n_q, Hkv, T_cap, p0, ids, k, (int)sink, sink_out);
     return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ hga_status check_config(const hga_config *cfg)
         return fail(HGA_ERR_UNSUPPORTED, "dtype must be HGA_BF16 (got %d)", cfg->dtype);
     if (isnan(cfg->softmax_scale) || isinf(cfg->softmax_scale))
         return fail(HGA_ERR_INVALID_ARG, "softmax_scale is not finite");
+    if (cfg->sink_chunks < 0)
+        return fail(HGA_ERR_INVALID_ARG, "sink_chunks must be >= 0 (got %d)", cfg->sink_chunks);
+    if (cfg->sink_chunks > HGA_MAX_SINK_CHUNKS)
+        return fail(HGA_ERR_UNSUPPORTED, "sink_chunks must be at most %d (got %d)",
+                    HGA_MAX_SINK_CHUNKS, cfg->sink_chunks);
     return HGA_OK;
 }
 
@@ -154,8 +159,8 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
     if (!Q || !ids || (need > 0 && !summaries))
         return fail(HGA_ERR_INVALID_ARG, "Q, summaries or ids is NULL");
     return hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads, p0,
-                                        n_q, summaries, n_chunk_cap, cfg->top_k, ids,
-                                        scores_or_null, stream),
+                                        n_q, summaries, n_chunk_cap, cfg->top_k,
+                                        cfg->sink_chunks, ids, scores_or_null, stream),
                       "hga_route launch");
 }
 
@@ -174,7 +179,8 @@ hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, c
     return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                              (const uint16_t *)V, cfg->n_q_heads,
                                              cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
-                                             effective_scale(cfg), (uint16_t *)O, lse, stream),
+                                             cfg->sink_chunks, effective_scale(cfg),
+                                             (uint16_t *)O, lse, stream),
                       "hga_attend_fwd launch");
 }
 
@@ -207,25 +213,27 @@ hga_status hga_route_attend_fwd(const hga_config *cfg, const void *Q, const void
     if (!Q || !K || !V || !O || !lse || (cfg->top_k > 0 && (!ids || (need > 0 && !summaries))))
         return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
     const float scale = effective_scale(cfg);
-    if (cfg->top_k > 0 && need > hga::route_attend_max_candidates()) {
+    if (cfg->top_k > 0 && need - cfg->sink_chunks > hga::route_attend_max_candidates()) {
         // more candidates than the fused kernel keeps in LDS: the routing
         // kernel, then the attention kernel (the same ids, scores and outputs)
         st = hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads,
-                                          p0, n_q, summaries, n_chunk_cap, cfg->top_k, ids,
-                                          scores_or_null, stream),
+                                          p0, n_q, summaries, n_chunk_cap, cfg->top_k,
+                                          cfg->sink_chunks, ids, scores_or_null, stream),
                         "hga_route_attend_fwd route launch");
         if (st != HGA_OK) return st;
         return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                                  (const uint16_t *)V, cfg->n_q_heads,
                                                  cfg->n_kv_heads, T_cap, p0, n_q, ids,
-                                                 cfg->top_k, scale, (uint16_t *)O, lse, stream),
+                                                 cfg->top_k, cfg->sink_chunks, scale,
+                                                 (uint16_t *)O, lse, stream),
                           "hga_route_attend_fwd attend launch");
     }
     return hip_status(hga::launch_route_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                                    (const uint16_t *)V, cfg->n_q_heads,
                                                    cfg->n_kv_heads, T_cap, p0, n_q, summaries,
-                                                   n_chunk_cap, cfg->top_k, scale, ids,
-                                                   scores_or_null, (uint16_t *)O, lse, stream),
+                                                   n_chunk_cap, cfg->top_k, cfg->sink_chunks,
+                                                   scale, ids, scores_or_null, (uint16_t *)O,
+                                                   lse, stream),
                       "hga_route_attend_fwd launch");
 }
 
@@ -281,7 +289,8 @@ hga_status hga_route_groups(const hga_config *cfg, const void *Q, int64_t p0, in
     return hip_status(hga::launch_route_groups((const uint16_t *)Q, cfg->n_q_heads,
                                                cfg->n_kv_heads, p0, n_q, group_summaries,
                                                n_group_cap, chunk_ids, cfg->top_k, group_top_k,
-                                               group_ids, scores_or_null, stream),
+                                               cfg->sink_chunks, group_ids, scores_or_null,
+                                               stream),
                       "hga_route_groups launch");
 }
 
@@ -304,8 +313,9 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
     return hip_status(hga::launch_attend_fwd_groups((const uint16_t *)Q, (const uint16_t *)K,
                                                     (const uint16_t *)V, cfg->n_q_heads,
                                                     cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
-                                                    group_top_k, effective_scale(cfg),
-                                                    (uint16_t *)O, lse, stream),
+                                                    group_top_k, cfg->sink_chunks,
+                                                    effective_scale(cfg), (uint16_t *)O, lse,
+                                                    stream),
                       "hga_attend_fwd_groups launch");
 }
 
@@ -339,7 +349,8 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
     return hip_status(hga::launch_attend_bwd_groups((const uint16_t *)Q, (const uint16_t *)K,
                                                     (const uint16_t *)V, cfg->n_q_heads,
                                                     cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
-                                                    group_top_k, effective_scale(cfg), lse,
+                                                    group_top_k, cfg->sink_chunks,
+                                                    effective_scale(cfg), lse,
                                                     (const uint16_t *)dO, dQ, dK_active,
                                                     dV_active, workspace, stream),
                       "hga_attend_bwd_groups launch");
@@ -367,8 +378,8 @@ hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, 
         return fail(HGA_ERR_CAPACITY, "sink holds %zu words, %zu needed", sink_words,
                     hga::gather_sink_words(cfg->n_kv_heads, n_q));
     return hip_status(hga::launch_gather((const uint16_t *)K, (const uint16_t *)V,
-                                         cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k, sink,
-                                         stream),
+                                         cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
+                                         cfg->sink_chunks, sink, stream),
                       "hga_diag_gather launch");
 }
 
@@ -403,7 +414,8 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, c
     return hip_status(hga::launch_attend_bwd((const uint16_t *)Q, (const uint16_t *)K,
                                              (const uint16_t *)V, cfg->n_q_heads,
                                              cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
-                                             effective_scale(cfg), (const uint16_t *)O, lse,
+                                             cfg->sink_chunks, effective_scale(cfg),
+                                             (const uint16_t *)O, lse,
                                              (const uint16_t *)dO, dQ, dK_active, dV_active,
                                              workspace, stream),
                       "hga_attend_bwd launch");

@@ -14,6 +14,10 @@ constexpr int kC = 64;       // chunk length == query block length
 constexpr int kMaxTopK = 256;
 constexpr int kGroup = 8;                  // tokens per group (second routing level)
 constexpr int kMaxGroupTopK = kMaxTopK * (64 / kGroup);   // every group of kMaxTopK chunks
+constexpr int kMaxSink = HGA_MAX_SINK_CHUNKS;
+// tile list lengths: local + sink + routed units, chunk and group level
+constexpr int kChunkListMax = 1 + kMaxSink + kMaxTopK;
+constexpr int kGroupListMax = 1 + kMaxSink * (64 / kGroup) + kMaxGroupTopK;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -46,17 +50,19 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // router-made row (ascending, distinct) passes one neighbour check; only a
 // row with a repeat pays the quadratic pass. `list` holds k + 1 entries and
 // is read back by the same wave only.
-// first = row[lane] if lane < k, else -1: a caller may load it early, so the
-// load's latency overlaps the caller's other loads.
-__device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
-                                                int64_t local_chunk, int *list, int first)
+// One wave compacts the valid units of an id row (lo <= u < hi) into list,
+// in row order with repeats dropped, and returns their number. first =
+// row[lane] if lane < k, else -1: a caller may load it early, so the load's
+// latency overlaps the caller's other loads.
+__device__ __forceinline__ int build_unit_list(const int32_t *row, int k, int64_t lo,
+                                               int64_t hi, int *list, int first)
 {
     const int lane = threadIdx.x & 63;
     int cnt = 0;
     for (int base = 0; base < k; base += 64) {
         const int r = base + lane;
         const int c = base == 0 ? first : (r < k) ? row[r] : -1;
-        const bool ok = c >= 0 && (int64_t)c < local_chunk;
+        const bool ok = (int64_t)c >= lo && (int64_t)c < hi;
         const uint64_t m = __ballot(ok);
         if (ok) list[cnt + lanes_below(m)] = c;
         cnt += __popcll(m);
@@ -79,15 +85,26 @@ __device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
         }
         cnt = out;
     }
-    if (lane == 0) list[cnt] = (int)local_chunk;
-    return cnt + 1;
+    return cnt;
 }
 
-__device__ __forceinline__ int build_chunk_list(const int32_t *row, int k,
-                                                int64_t local_chunk, int *list)
+__device__ __forceinline__ int build_unit_list(const int32_t *row, int k, int64_t lo,
+                                               int64_t hi, int *list)
 {
     const int lane = threadIdx.x & 63;
-    return build_chunk_list(row, k, local_chunk, list, lane < k ? row[lane] : -1);
+    return build_unit_list(row, k, lo, hi, list, lane < k ? row[lane] : -1);
+}
+
+// The sink window in units of `unit` tokens for a block starting at P: the
+// units of the first min(s, P/C) chunks, written as 0, 1, ... by one wave.
+__device__ __forceinline__ int sink_units(int sink_chunks, int64_t P, int unit)
+{
+    const int64_t s = min((int64_t)sink_chunks, P / kC);
+    return (int)(s * (kC / unit));
+}
+__device__ __forceinline__ void write_sink_units(int *list, int n)
+{
+    for (int i = threadIdx.x & 63; i < n; i += 64) list[i] = i;
 }
 
 // Order-preserving map of a finite float to uint32 (larger float -> larger
@@ -108,24 +125,24 @@ hipError_t launch_summarize_groups(const uint16_t *K, int64_t Hkv, int64_t T_cap
                                    int64_t n_gcap, hipStream_t stream);
 
 hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
-                        int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                        int64_t n_q, const float *S, int64_t n_cap, int32_t k, int32_t sink,
                         int32_t *ids, float *scores, hipStream_t stream);
 
 hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                                int64_t n_q, const float *SG, int64_t n_gcap,
-                               const int32_t *chunk_ids, int32_t kc, int32_t m,
+                               const int32_t *chunk_ids, int32_t kc, int32_t m, int32_t sink,
                                int32_t *gids, float *scores, hipStream_t stream);
 
 hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, float scale,
+                             const int32_t *ids, int32_t k, int32_t sink, float scale,
                              uint16_t *O, float *lse, hipStream_t stream);
 
 hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     const uint16_t *V, int64_t Hq, int64_t Hkv,
                                     int64_t T_cap, int64_t p0, int64_t n_q,
-                                    const int32_t *gids, int32_t m, float scale,
+                                    const int32_t *gids, int32_t m, int32_t sink, float scale,
                                     uint16_t *O, float *lse, hipStream_t stream);
 // Routing and attention in one launch (ids and scores written as
 // launch_route would write them). Needs (p0 + n_q - C)/C <=
@@ -133,19 +150,19 @@ hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
 hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                    int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                                   float scale, int32_t *ids, float *scores, uint16_t *O,
-                                   float *lse, hipStream_t stream);
+                                   int32_t sink, float scale, int32_t *ids, float *scores,
+                                   uint16_t *O, float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
 // Gather-only diagnostic (diag.hip): sink holds gather_sink_words words.
 hipError_t launch_gather(const uint16_t *K, const uint16_t *V, int64_t Hkv, int64_t T_cap,
-                         int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, uint32_t *sink,
-                         hipStream_t stream);
+                         int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
+                         uint32_t *sink_out, hipStream_t stream);
 size_t gather_sink_words(int64_t Hkv, int64_t n_q);
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                     int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
-                                    int64_t n_q, const int32_t *gids, int32_t m, float scale,
-                                    const float *lse, const uint16_t *dO, float *dQ, float *dK,
-                                    float *dV, void *workspace, hipStream_t stream);
+                                    int64_t n_q, const int32_t *gids, int32_t m, int32_t sink,
+                                    float scale, const float *lse, const uint16_t *dO, float *dQ,
+                                    float *dK, float *dV, void *workspace, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
 
@@ -155,7 +172,7 @@ int64_t bwd_max_queries();
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, float scale,
+                             const int32_t *ids, int32_t k, int32_t sink, float scale,
                              const uint16_t *O, const float *lse,
                              const uint16_t *dO, float *dQ, float *dK,
                              float *dV, void *workspace, hipStream_t stream);

@@ -17,7 +17,7 @@ template <int G, int NI, bool kGroups>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
     const float *__restrict__ S, int64_t n_cap, int k,
-    const int32_t *__restrict__ chunk_ids, int kc,
+    const int32_t *__restrict__ chunk_ids, int kc, int c_lo,
     int32_t *__restrict__ ids, float *__restrict__ scores)
 {
     extern __shared__ uint32_t keys[];          // [candidates of this block]
@@ -31,23 +31,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const int64_t i = b * kC + row % kC;
         return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
     };
-    route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, chunk_ids, kc,
+    route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, g, b, p0, S, n_cap, k,
+                                                 chunk_ids, kc, c_lo,
                                     [&](int r, int id, float sc) __attribute__((always_inline)) {
                                         out[r] = id;
                                         if (sout) sout[r] = sc;
                                     });
 }
 
+struct RouteArgs {
+    const uint16_t *Q;
+    int64_t Hq, Hkv, p0, n_q;
+    const float *S;             // chunk or group summaries
+    int64_t n_cap;
+    int32_t k;                  // chunk budget, or the group budget
+    const int32_t *chunk_ids;   // group routing only
+    int32_t kc;
+    int32_t sink;               // sink window, chunks
+    int32_t *ids;
+    float *scores;
+};
+
 template <int G, int NI, bool kGroups>
-hipError_t launch_route_gn(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
-                           const float *S, int64_t n_cap, int32_t k, const int32_t *chunk_ids,
-                           int32_t kc, int32_t *ids, float *scores, size_t shmem,
-                           hipStream_t stream)
+hipError_t launch_route_gn(const RouteArgs &a, size_t shmem, hipStream_t stream)
 {
-    const int64_t n_blocks = n_q / kC;
-    hipLaunchKernelGGL((route_kernel<G, NI, kGroups>), dim3((unsigned)(n_blocks * Hkv)),
-                       dim3(kRouteThreads), shmem, stream, Q, n_q, Hkv, p0, S, n_cap, k,
-                       chunk_ids, kc, ids, scores);
+    const int64_t n_blocks = a.n_q / kC;
+    hipLaunchKernelGGL((route_kernel<G, NI, kGroups>), dim3((unsigned)(n_blocks * a.Hkv)),
+                       dim3(kRouteThreads), shmem, stream, a.Q, a.n_q, a.Hkv, a.p0, a.S,
+                       a.n_cap, a.k, a.chunk_ids, a.kc, (int)a.sink, a.ids, a.scores);
     return hipGetLastError();
 }
 
@@ -55,40 +66,29 @@ hipError_t launch_route_gn(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n
 // largest candidate count; beyond 2048 (chunk routing only) the LDS path
 // takes over.
 template <int G, bool kGroups>
-hipError_t launch_route_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
-                          const float *S, int64_t n_cap, int32_t k, const int32_t *chunk_ids,
-                          int32_t kc, int32_t *ids, float *scores, hipStream_t stream)
+hipError_t launch_route_g(const RouteArgs &a, hipStream_t stream)
 {
-    const int64_t max_chunks = (p0 + n_q - kC) / kC;
-    const int64_t max_eligible = kGroups ? (kC / kGroup) * (max_chunks < kc ? max_chunks : kc)
-                                         : max_chunks;
+    int64_t max_chunks = (a.p0 + a.n_q - kC) / kC - a.sink;
+    if (max_chunks < 0) max_chunks = 0;
+    const int64_t max_eligible =
+        kGroups ? (kC / kGroup) * (max_chunks < a.kc ? max_chunks : a.kc) : max_chunks;
     // chunk routing keeps the keys; group routing also sorts up to kc ids there
-    int64_t slots = max_eligible > kc ? max_eligible : (kGroups ? kc : max_eligible);
+    int64_t slots = max_eligible > a.kc ? max_eligible : (kGroups ? a.kc : max_eligible);
     const size_t shmem = (size_t)(slots > 0 ? slots : 1) * sizeof(uint32_t);
-    if (max_eligible <= 4 * 64)
-        return launch_route_gn<G, 4, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
-                                              scores, shmem, stream);
-    if (max_eligible <= 8 * 64)
-        return launch_route_gn<G, 8, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
-                                              scores, shmem, stream);
-    if (max_eligible <= 16 * 64)
-        return launch_route_gn<G, 16, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids,
-                                               scores, shmem, stream);
-    return launch_route_gn<G, kMaxRegKeys, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids,
-                                                    kc, ids, scores, shmem, stream);
+    if (max_eligible <= 4 * 64) return launch_route_gn<G, 4, kGroups>(a, shmem, stream);
+    if (max_eligible <= 8 * 64) return launch_route_gn<G, 8, kGroups>(a, shmem, stream);
+    if (max_eligible <= 16 * 64) return launch_route_gn<G, 16, kGroups>(a, shmem, stream);
+    return launch_route_gn<G, kMaxRegKeys, kGroups>(a, shmem, stream);
 }
 
 template <bool kGroups>
-hipError_t launch_route_any(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
-                            int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                            const int32_t *chunk_ids, int32_t kc, int32_t *ids, float *scores,
-                            hipStream_t stream)
+hipError_t launch_route_any(const RouteArgs &a, hipStream_t stream)
 {
-    switch (Hq / Hkv) {
-    case 1: return launch_route_g<1, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
-    case 2: return launch_route_g<2, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
-    case 4: return launch_route_g<4, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
-    case 8: return launch_route_g<8, kGroups>(Q, Hkv, p0, n_q, S, n_cap, k, chunk_ids, kc, ids, scores, stream);
+    switch (a.Hq / a.Hkv) {
+    case 1: return launch_route_g<1, kGroups>(a, stream);
+    case 2: return launch_route_g<2, kGroups>(a, stream);
+    case 4: return launch_route_g<4, kGroups>(a, stream);
+    case 8: return launch_route_g<8, kGroups>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -96,22 +96,22 @@ hipError_t launch_route_any(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t 
 }  // namespace
 
 hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
-                        int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                        int64_t n_q, const float *S, int64_t n_cap, int32_t k, int32_t sink,
                         int32_t *ids, float *scores, hipStream_t stream)
 {
     if (n_q == 0 || k == 0) return hipSuccess;
-    return launch_route_any<false>(Q, Hq, Hkv, p0, n_q, S, n_cap, k, nullptr, 0, ids, scores,
-                                   stream);
+    const RouteArgs a{Q, Hq, Hkv, p0, n_q, S, n_cap, k, nullptr, 0, sink, ids, scores};
+    return launch_route_any<false>(a, stream);
 }
 
 hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                                int64_t n_q, const float *SG, int64_t n_gcap,
-                               const int32_t *chunk_ids, int32_t kc, int32_t m,
+                               const int32_t *chunk_ids, int32_t kc, int32_t m, int32_t sink,
                                int32_t *gids, float *scores, hipStream_t stream)
 {
     if (n_q == 0 || m == 0) return hipSuccess;
-    return launch_route_any<true>(Q, Hq, Hkv, p0, n_q, SG, n_gcap, m, chunk_ids, kc, gids,
-                                  scores, stream);
+    const RouteArgs a{Q, Hq, Hkv, p0, n_q, SG, n_gcap, m, chunk_ids, kc, sink, gids, scores};
+    return launch_route_any<true>(a, stream);
 }
 
 }  // namespace hga

@@ -208,19 +208,19 @@ __device__ __forceinline__ int select_top_k_reg(const uint32_t *keys, int nE, in
 }
 
 
-// The distinct valid chunks (0 <= c < limit) of a chunk row, ascending, into
-// chl; returns their number. A router-made row (ascending, distinct) passes
-// one neighbour check; any other row has its repeats dropped (first kept) and
-// is rank-sorted through tmp (k entries). One wave calls it.
-__device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64_t limit,
-                                                int *chl, int *tmp)
+// The distinct valid chunks (lo <= c < limit) of a chunk row, ascending,
+// into chl; returns their number. A router-made row (ascending, distinct)
+// passes one neighbour check; any other row has its repeats dropped (first
+// kept) and is rank-sorted through tmp (k entries). One wave calls it.
+__device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64_t lo,
+                                                int64_t limit, int *chl, int *tmp)
 {
     const int lane = threadIdx.x & 63;
     int cnt = 0;
     for (int base = 0; base < k; base += 64) {
         const int r = base + lane;
         const int c = (r < k) ? row[r] : -1;
-        const bool ok = c >= 0 && (int64_t)c < limit;
+        const bool ok = (int64_t)c >= lo && (int64_t)c < limit;
         const uint64_t m = __ballot(ok);
         if (ok) chl[cnt + lanes_below(m)] = c;
         cnt += __popcll(m);
@@ -248,10 +248,6 @@ __device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64
     return n;
 }
 
-// kGroups = false: chunk routing, candidates every chunk c < P/C, rows of S.
-// kGroups = true: group routing (second level), candidates the 8 groups of
-// each distinct valid chunk of chunk_ids[g][b], in ascending group order, rows
-// of the group summaries S; k is then the group budget.
 // LDS the router uses besides the candidate keys.
 struct RouteLds {
     float part[16][kD];
@@ -272,10 +268,12 @@ struct RouteLds {
 // emit(r, id, score) in ascending order, then (r, -1, -inf) up to k; the
 // return value (their number) is meaningful in wave 0.
 //
-// kGroups = false: chunk routing, candidates every chunk c < P/C, rows of S.
+// kGroups = false: chunk routing, candidates every chunk c with c_lo <= c <
+// P/C (c_lo = the sink window's chunk count), rows of S.
 // kGroups = true: group routing (second level), candidates the 8 groups of
-// each distinct valid chunk of chunk_ids[g][b], in ascending group order, rows
-// of the group summaries S; k is then the group budget.
+// each distinct valid chunk (c_lo <= c < P/C) of chunk_ids[g][b], in
+// ascending group order, rows of the group summaries S; k is then the group
+// budget.
 // kBatch: summary rows per lane in flight; kScoreWaves: waves that score
 // (the first kScoreWaves of the workgroup). Both only distribute the
 // candidates over lanes: each score's arithmetic, and so every score, is the
@@ -288,7 +286,7 @@ template <int G, int NI, bool kGroups, int kBatch, int kScoreWaves, typename QRo
 __device__ __forceinline__ int route_block(
     RouteLds &sh, uint32_t *keys, QRow q_row, int64_t n_q, int64_t g,
     int64_t b, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
-    const int32_t *__restrict__ chunk_ids, int kc, Emit emit)
+    const int32_t *__restrict__ chunk_ids, int kc, int c_lo, Emit emit)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -299,12 +297,12 @@ __device__ __forceinline__ int route_block(
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
     int *chl = sh.chl;
-    int nE = (int)(P / kC);
+    int nE = (int)max((int64_t)0, P / kC - c_lo);
     if (kGroups) {
         // 0. the block's distinct valid routed chunks, ascending
         if (wave == 0) {
-            const int n = sorted_chunk_set(chunk_ids + (g * n_blocks + b) * kc, kc, P / kC,
-                                           chl, (int *)keys);
+            const int n = sorted_chunk_set(chunk_ids + (g * n_blocks + b) * kc, kc, c_lo,
+                                           P / kC, chl, (int *)keys);
             if (lane == 0) sh.n_ch = n;
         }
         __syncthreads();
@@ -312,7 +310,7 @@ __device__ __forceinline__ int route_block(
     }
     // summary row of candidate c (its chunk, or its group)
     auto row_of = [&](int c) __attribute__((always_inline)) {
-        return kGroups ? chl[c >> 3] * (kC / kGroup) + (c & 7) : c;
+        return kGroups ? chl[c >> 3] * (kC / kGroup) + (c & 7) : c + c_lo;
     };
 
     // Every load that does not depend on qbar is issued first: all of this
@@ -424,7 +422,7 @@ __device__ __forceinline__ int route_block(
     const int n_sel = wave_select(sh.cand_key, m, k, sh.chosen);
     for (int r = lane; r < k; r += 64) {
         if (r < n_sel)
-            emit(r, sh.cand_pos[sh.chosen[r]], key_to_score(sh.cand_key[sh.chosen[r]]));
+            emit(r, row_of(sh.cand_pos[sh.chosen[r]]), key_to_score(sh.cand_key[sh.chosen[r]]));
         else
             emit(r, -1, -INFINITY);
     }

@@ -33,14 +33,15 @@ class hga_config(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("q_block", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("sink_chunks", ctypes.c_int32)]
 
 
 def make_config(n_q_heads: int, n_kv_heads: int, top_k: int, *, head_dim: int = 128,
                 chunk: int = 64, q_block: int = 64, softmax_scale: float = 0.0,
-                dtype: int = HGA_BF16) -> hga_config:
+                dtype: int = HGA_BF16, sink_chunks: int = 0) -> hga_config:
     return hga_config(n_q_heads, n_kv_heads, head_dim, chunk, q_block, top_k,
-                      softmax_scale, dtype)
+                      softmax_scale, dtype, sink_chunks)
 
 
 class HGAError(RuntimeError):

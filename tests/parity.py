@@ -36,24 +36,26 @@ def from_dev(t: torch.Tensor) -> np.ndarray:
 
 
 def check_ids(gpu_ids: np.ndarray, ref_ids: np.ndarray, sigma: np.ndarray, p0: int,
-              C: int = 64, Bq: int = 64, where: str = "") -> int:
-    """Returns the number of (head, block) rows whose sets differ within the gap."""
+              C: int = 64, Bq: int = 64, where: str = "", sink_chunks: int = 0) -> int:
+    """Returns the number of (head, block) rows whose sets differ within the gap.
+    With a sink window the candidates are the chunks sink_chunks <= c < P/C."""
     assert gpu_ids.shape == ref_ids.shape, (gpu_ids.shape, ref_ids.shape)
     Hkv, nb, k = gpu_ids.shape
     near_ties = 0
+    lo = sink_chunks
     for g in range(Hkv):
         for b in range(nb):
             a, r = gpu_ids[g, b], ref_ids[g, b]
             nE = (p0 + b * Bq) // C
             na, nr = int((a >= 0).sum()), int((r >= 0).sum())
             ctx = f"{where} head {g} block {b}: gpu {a.tolist()} oracle {r.tolist()}"
-            assert na == nr == min(k, nE), ctx
+            assert na == nr == min(k, max(0, nE - lo)), ctx
             assert np.all(a[na:] == -1), ctx
             assert np.all(np.diff(a[:na]) > 0), ctx
-            assert na == 0 or (a[0] >= 0 and a[na - 1] < nE), ctx
+            assert na == 0 or (a[0] >= lo and a[na - 1] < nE), ctx
             if np.array_equal(a, r):
                 continue
-            sig = sigma[g, b, :nE]
+            sig = sigma[g, b, lo:nE]
             M = np.max(np.abs(sig))
             kth = np.sort(sig)[::-1][nr - 1]
             for c in set(a[:na].tolist()) ^ set(r[:nr].tolist()):
@@ -93,16 +95,17 @@ def summary_bound(K: np.ndarray, c_begin: int, c_end: int, C: int = 64) -> np.nd
     return (C - 1) * 2.0 ** -24 * out * 1.0001 + 2.0 ** -24 * out
 
 
-def group_candidates(chunk_row: np.ndarray, P: int, C: int = 64, U: int = 8) -> np.ndarray:
+def group_candidates(chunk_row: np.ndarray, P: int, C: int = 64, U: int = 8,
+                     sink_chunks: int = 0) -> np.ndarray:
     """Candidate groups of one block: the U-token groups of the distinct chunk
-    ids c of its routed row with 0 <= c < P/C, ascending."""
-    ch = sorted({int(c) for c in chunk_row if 0 <= c < P // C})
+    ids c of its routed row with sink_chunks <= c < P/C, ascending."""
+    ch = sorted({int(c) for c in chunk_row if sink_chunks <= c < P // C})
     return np.array([c * (C // U) + j for c in ch for j in range(C // U)], dtype=np.int64)
 
 
 def check_group_ids(gpu_gids: np.ndarray, ref_gids: np.ndarray, sigma: np.ndarray,
                     chunk_ids: np.ndarray, p0: int, C: int = 64, Bq: int = 64, U: int = 8,
-                    where: str = "") -> int:
+                    where: str = "", sink_chunks: int = 0) -> int:
     """The id rule of check_ids at the group level: the candidates of a block
     are the groups of its routed chunks (group_candidates), M is the largest
     |score| among them. Returns the number of rows that differ within the gap."""
@@ -112,7 +115,7 @@ def check_group_ids(gpu_gids: np.ndarray, ref_gids: np.ndarray, sigma: np.ndarra
     for g in range(Hkv):
         for b in range(nb):
             a, r = gpu_gids[g, b], ref_gids[g, b]
-            cand = group_candidates(chunk_ids[g, b], p0 + b * Bq, C, U)
+            cand = group_candidates(chunk_ids[g, b], p0 + b * Bq, C, U, sink_chunks)
             na, nr = int((a >= 0).sum()), int((r >= 0).sum())
             ctx = f"{where} head {g} block {b}: gpu {a.tolist()} oracle {r.tolist()}"
             assert na == nr == min(m, cand.size), ctx

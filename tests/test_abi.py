@@ -58,6 +58,8 @@ def _fwd(cfg, p0=14336, n_q=2048, T=16384, ids=FAKE, O=FAKE):
     (dict(top_k=-1), hga.HGA_ERR_INVALID_ARG, "top_k"),
     (dict(dtype=1), hga.HGA_ERR_UNSUPPORTED, "dtype"),
     (dict(softmax_scale=float("nan")), hga.HGA_ERR_INVALID_ARG, "finite"),
+    (dict(sink_chunks=-1), hga.HGA_ERR_INVALID_ARG, "sink_chunks"),
+    (dict(sink_chunks=65), hga.HGA_ERR_UNSUPPORTED, "sink_chunks"),
 ])
 def test_config_checks(kw, status, needle):
     cfg = _cfg(**kw)
