@@ -60,6 +60,9 @@ def _load():
                                       _i64, _i64, _i64, _i64, _i64, _i32p, _i64,
                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
                                       _f64p, _f64p, _f64p, _i64]
+    lib.oracle_attend_decode.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
+                                         _i64, _i64, _i64, _i32p, _i64, ctypes.c_double,
+                                         _i64, _f64p, _f64p]
     _lib = lib
     return lib
 
@@ -194,3 +197,31 @@ def attend_bwd(Q, K, V, dO, ids, p0: int, C: int = 64, Bq: int = 64,
     _load().oracle_attend_bwd(Q, K, V, dO, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k,
                               float(scale), p1, p2, dQ, dK, dV, sink)
     return dQ, dK, dV
+
+
+def route_decode(Q, S, p0: int, k: int, Hkv: int, C: int = 64, want_scores=False,
+                 sink: int = 0):
+    """Routing of a decode step, one token at a time: token i (position
+    p0 + i) routes on the mean of its own G query heads over the closed chunks
+    before its open chunk -- the block router with blocks of one query.
+    Returns ids [Hkv][n_q][k] (and sigma [Hkv][n_q][n_cap])."""
+    return route(Q, S, p0, k, Hkv, C, 1, want_scores=want_scores, sink=sink)
+
+
+def attend_decode(Q, K, V, ids, p0: int, C: int = 64, scale: float | None = None,
+                  sink: int = 0):
+    """Exact attention of a decode step: token i at p = p0 + i attends the
+    sink window, its routed chunks before its open chunk, and its open chunk
+    up to p. ids [Hkv][n_q][k]. Returns (O [Hq][n_q][D], lse [Hq][n_q])."""
+    Q, K, V = _f32(Q), _f32(K), _f32(V)
+    Hq, n_q, D = Q.shape
+    Hkv, T, _ = K.shape
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    assert ids.shape[:2] == (Hkv, n_q) and sink % C == 0 and sink >= 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = np.full((Hq, n_q, D), np.nan)
+    lse = np.full((Hq, n_q), np.nan)
+    _load().oracle_attend_decode(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, ids, ids.shape[2],
+                                 float(scale), sink, O, lse)
+    return O, lse

@@ -474,3 +474,68 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
     }
     free(Delta); free(Obuf); free(lse);
 }
+
+/* ------------------------------------------------------------- attend decode
+ * Routed generation (technical summary 2.1 applied to one token at a time; the
+ * pages note the method also serves generation). Token i of a decode step
+ * sits at position p = p0 + i (p0 need not be a multiple of C); its local
+ * window is the part of its own, still open chunk up to p, and it routes on
+ * its own (ids [Hkv][n_q][k], e.g. oracle_route with Bq = 1):
+ *     Pc   = C * floor(p / C)                      start of the open chunk
+ *     A(p) = [0, min(sink, Pc))  U  union_{c in ids[g][i], sink <= cC, c < Pc/C}
+ *            [cC, cC + C)  U  [Pc, p]
+ * and O, lse as in oracle_attend_fwd. For a block of 64 queries starting a
+ * chunk this is the prefill definition itself.
+ */
+void oracle_attend_decode(const float *Q, const float *K, const float *V,
+                          int64_t Hq, int64_t Hkv, int64_t D, int64_t T,
+                          int64_t p0, int64_t n_q, int64_t C,
+                          const int32_t *ids, int64_t k, double scale, int64_t sink,
+                          double *O, double *lse)
+{
+    int64_t G = Hq / Hkv;
+    int64_t n_chunks = T / C;
+#pragma omp parallel
+    {
+        int64_t *pos = (int64_t *)malloc((size_t)(T + 1) * sizeof(int64_t));
+        double *z = (double *)malloc((size_t)(T + 1) * sizeof(double));
+        double *acc = (double *)malloc((size_t)D * sizeof(double));
+        unsigned char *seen = (unsigned char *)malloc((size_t)n_chunks + 1);
+#pragma omp for schedule(dynamic)
+        for (int64_t row = 0; row < Hq * n_q; ++row) {
+            int64_t h = row / n_q, i = row % n_q, g = h / G;
+            int64_t p = p0 + i, Pc = C * (p / C);
+            int64_t n = 0;
+            for (int64_t t = 0; t < sink && t < Pc; ++t) pos[n++] = t;
+            memset(seen, 0, (size_t)n_chunks + 1);
+            const int32_t *row_ids = ids + (g * n_q + i) * k;
+            for (int64_t r = 0; r < k; ++r) {
+                int64_t c = row_ids[r];
+                if (c < 0 || c >= Pc / C || c * C < sink || seen[c]) continue;
+                seen[c] = 1;
+            }
+            for (int64_t c = 0; c < n_chunks; ++c)
+                if (seen[c])
+                    for (int64_t t = c * C; t < c * C + C; ++t) pos[n++] = t;
+            for (int64_t t = Pc; t <= p; ++t) pos[n++] = t;
+
+            const float *q = Q + row * D;
+            double m = -INFINITY;
+            for (int64_t a = 0; a < n; ++a) {
+                z[a] = scale * dot_fd(q, K + (g * T + pos[a]) * D, D);
+                if (z[a] > m) m = z[a];
+            }
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                double e = exp(z[a] - m);
+                l += e;
+                const float *vj = V + (g * T + pos[a]) * D;
+                for (int64_t d = 0; d < D; ++d) acc[d] += e * (double)vj[d];
+            }
+            for (int64_t d = 0; d < D; ++d) O[row * D + d] = acc[d] / l;
+            lse[row] = m + log(l);
+        }
+        free(seen); free(acc); free(z); free(pos);
+    }
+}

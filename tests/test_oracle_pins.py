@@ -701,3 +701,88 @@ def test_route_groups_ignores_chunks_inside_the_sink():
     M = _mask_with_sink(g_sink, Hq, Hkv, n_q, p0, T, 8, 64, s * 64)
     O_ref, lse_ref = _sdpa_masked(x["Q"], x["K"], x["V"], M, 1 / math.sqrt(D))
     np.testing.assert_allclose(O, O_ref, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------- decode
+# (one token at a time: the token routes on its own G query heads over the
+# closed chunks before its open chunk, and attends the sink, its routed chunks
+# and its open chunk up to itself)
+
+def _decode_mask(ids, Hq, Hkv, n_q, p0, T, C, sink):
+    G = Hq // Hkv
+    M = np.zeros((Hq, n_q, T), dtype=bool)
+    for h in range(Hq):
+        for i in range(n_q):
+            p = p0 + i
+            Pc = C * (p // C)
+            M[h, i, :min(sink, Pc)] = True
+            for c in ids[h // G, i]:
+                if 0 <= c < Pc // C and c * C >= sink:
+                    M[h, i, c * C:(c + 1) * C] = True
+            M[h, i, Pc:p + 1] = True
+    return M
+
+
+@pytest.mark.parametrize("p0,s", [(197, 0), (250, 2), (128, 1), (17, 2)])
+def test_decode_attention_matches_masked_sdpa(p0, s):
+    Hq, Hkv, D, T, n_q, C, k = 4, 2, 16, 256, 6, 8, 3
+    x = _tiny(90 + p0, Hq, Hkv, D, T, 8, C)
+    Q = x["Q"][:, :n_q]
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route_decode(Q, S, p0, k, Hkv, C, sink=s * C)
+    # caller-made entries: a token's own open chunk (future keys) and a chunk
+    # inside the sink add nothing
+    ids[0, 0, 0] = (p0 // C)
+    ids[1, n_q - 1, 1] = 0
+    O, lse = oracle.attend_decode(Q, x["K"], x["V"], ids, p0, C, sink=s * C)
+    M = _decode_mask(ids, Hq, Hkv, n_q, p0, T, C, s * C)
+    O_ref, lse_ref = _sdpa_masked(Q, x["K"], x["V"], M, 1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_at_a_chunk_start_is_prefill_with_one_query_blocks():
+    Hq, Hkv, D, T, C, k = 4, 2, 16, 256, 8, 4
+    x = _tiny(95, Hq, Hkv, D, T, 8, C)
+    p0, n_q = 160, 1                      # p0 % C == 0
+    Q = x["Q"][:, :n_q]
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route_decode(Q, S, p0, k, Hkv, C)
+    O1, l1 = oracle.attend_decode(Q, x["K"], x["V"], ids, p0, C)
+    O2, l2 = oracle.attend_fwd(Q, x["K"], x["V"], ids, p0, C, 1)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_decode_with_every_chunk_is_dense_causal():
+    Hq, Hkv, D, T, C = 2, 1, 16, 128, 8
+    x = _tiny(96, Hq, Hkv, D, T, 8, C)
+    p0, n_q = 101, 5
+    Q = x["Q"][:, :n_q]
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route_decode(Q, S, p0, T // C, Hkv, C)
+    O, _ = oracle.attend_decode(Q, x["K"], x["V"], ids, p0, C)
+    q = torch.from_numpy(Q.astype(np.float64))
+    kk = torch.from_numpy(np.repeat(x["K"].astype(np.float64), Hq, 0))
+    vv = torch.from_numpy(np.repeat(x["V"].astype(np.float64), Hq, 0))
+    causal = torch.from_numpy(np.arange(T)[None, :] <= (p0 + np.arange(n_q))[:, None])
+    O_ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, attn_mask=causal,
+                                                             scale=1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_decode_routing_finds_a_planted_chunk_per_token():
+    # chunk 5 is the direction of token 2's mean query: token 2 (and any token
+    # past chunk 5) picks it at k = 1; a token whose open chunk is chunk 5 or
+    # earlier cannot (it is not closed for it)
+    Hq, Hkv, D, T, C = 4, 1, 16, 256, 8
+    x = _tiny(97, Hq, Hkv, D, T, 8, C, bf16=False)
+    Q = x["Q"][:, :3].copy()
+    K = x["K"].copy()
+    qbar = Q[:, 2].mean(axis=0)
+    K[0, 5 * C:6 * C] = 40.0 * qbar / np.linalg.norm(qbar)
+    S = oracle.summarize(K, C, 0, T // C)
+    ids = oracle.route_decode(Q, S, 200, 1, Hkv, C)
+    assert ids[0, 2, 0] == 5
+    ids_early = oracle.route_decode(Q, S, 44, 1, Hkv, C)       # open chunk 5: not a candidate
+    assert ids_early[0, 2, 0] != 5
