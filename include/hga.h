@@ -275,6 +275,50 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Routed generation (decode): a step of n_q new tokens at positions p0 ..
+ * p0+n_q-1, one token at a time (technical summary 2.1 applied per token; the
+ * pages note the method also serves generation). Positions need not be
+ * multiples of C. Token p's open chunk starts at Pc = C*floor(p/C); the
+ * chunks before it are closed, and their summaries must exist (append a
+ * chunk's summary with hga_summarize once its last token is in K).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * hga_route_decode -- hga_route with one-token blocks: for token i (p = p0+i)
+ * and kv head g, qbar = mean of Q[h][i] over the G heads of g (fp32),
+ * candidates the chunks s <= c < Pc/C (s = cfg->sink_chunks), and
+ * ids[g][i][:] the min(k, Pc/C - s) of highest score, ties to the lower id,
+ * ascending, then -1.
+ *   Q        device bf16 [Hq][n_q][D]
+ *   ids      device int32 [Hkv][n_q][k];  scores_or_null as for hga_route
+ *   summaries: (p0 + n_q - 1)/C <= n_chunks_valid <= n_chunk_cap, else
+ *            HGA_ERR_CAPACITY
+ */
+hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                            const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
+                            int32_t *ids, float *scores_or_null, hipStream_t stream);
+
+/* Device workspace hga_attend_decode needs for n_q tokens (0 on bad args). */
+size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t n_q);
+
+/*
+ * hga_attend_decode -- exact attention of the step's tokens: token p attends
+ *     A(p) = [0, min(sC, Pc))  U  union_{c in ids[g][i], s <= c < Pc/C} [cC, cC+C)
+ *            U  [Pc, p]
+ * with O and lse as in hga_attend_fwd (ids rows are sets; entries outside the
+ * range add nothing). The K/V of the step's own tokens must already be in K
+ * and V.
+ *   Q, O   device bf16 [Hq][n_q][D];  K, V device bf16 [Hkv][T_cap][D]
+ *   ids    device int32 [Hkv][n_q][k];  lse device f32 [Hq][n_q]
+ *   p0 + n_q <= T_cap, else HGA_ERR_INVALID_ARG
+ *   workspace  at least hga_decode_workspace_bytes(cfg, n_q) bytes, else
+ *            HGA_ERR_CAPACITY; calls that share it must not overlap in time.
+ */
+hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K, const void *V,
+                             int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids, void *O,
+                             float *lse, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostic (not a step of the method).
  * ---------------------------------------------------------------------- */
 

@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libhga.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["hga_api.cpp", "summarize.hip", "route.hip", "attend_fwd.hip", "attend_bwd.hip",
-           "diag.hip"]
+           "diag.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,297 @@
+// decode.hip -- routed generation: a decode step of n_q tokens at positions
+// p0 .. p0+n_q-1 (arXiv 2607.15105, gist.science technical summary 2.1 applied
+// one token at a time; the pages note that the method also serves
+// generation). Token p routes on its own G query heads over the closed chunks
+// before its open chunk, and attends the sink window, its routed chunks and
+// its open chunk up to itself.
+//
+//   route_decode_kernel   the router (route_block) with one-token blocks: one
+//                         256-thread workgroup per (token, kv head).
+//   decode_partial_kernel split-K attention: the tiles of a (token, kv head)
+//                         -- sink chunks, routed chunks, the open chunk's
+//                         prefix -- are dealt kDecTiles at a time to
+//                         n_split workgroups; each loads its tiles into LDS at
+//                         once, scores them on the vector ALUs (G query rows
+//                         are too few for the matrix cores) and writes, per
+//                         head, the running max (log2 units), the sum of
+//                         exponentials and the unnormalised output.
+//   decode_combine_kernel merges the partials of a (token, head) in split
+//                         order: O (bf16) and lse.
+// At batch 1 the step reads (k + sink + 1) K/V tiles of 32 KiB per (token, kv
+// head) once: HBM bound, so the split spreads those reads over many CUs.
+#include "route_core.h"
+
+namespace hga {
+namespace {
+
+template <int G, int NI>
+__global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
+    const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
+    const float *__restrict__ S, int64_t n_cap, int k, int sink,
+    int32_t *__restrict__ ids, float *__restrict__ scores)
+{
+    extern __shared__ uint32_t keys[];          // [candidates of this token]
+    __shared__ RouteLds sh;
+    const int64_t g = blockIdx.x % Hkv;
+    const int64_t i = blockIdx.x / Hkv;        // token
+    int32_t *out = ids + (g * n_q + i) * k;
+    float *sout = scores ? scores + (g * n_q + i) * k : nullptr;
+    auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {   // row: head in group
+        return *(const u32x4 *)(Q + ((g * G + row) * n_q + i) * kD + dseg * 8);
+    };
+    auto emit = [&](int r, int id, float sc) __attribute__((always_inline)) {
+        out[r] = id;
+        if (sout) sout[r] = sc;
+    };
+    route_block<G, NI, false, 16, kRouteWaves, decltype(q_row), decltype(emit), 1>(
+        sh, keys, q_row, n_q, g, i, p0, S, n_cap, k, nullptr, 0, sink, emit);
+}
+
+constexpr int kDecThreads = 256;
+constexpr int kDecTiles = 2;                // tiles per split workgroup
+constexpr int kDecStride = kD + 8;          // bf16 per LDS row (272 B)
+constexpr int kPartFloats = 2 + kD;         // max (log2 units), sum, output
+
+// Workgroup (token i, kv head g, split j): tiles j*kDecTiles .. +kDecTiles of
+// the token's list [sink chunks, routed chunks, open chunk]. Wave w serves
+// heads w, w + 4 (G = 8) of the group; lane l holds key l of a tile for the
+// scores and output dims 2l, 2l + 1 for P.V.
+template <int G>
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int64_t T_cap, int64_t p0,
+    const int32_t *__restrict__ ids, int k, int sink, float scale_log2, int n_split,
+    float *__restrict__ part)
+{
+    constexpr int HPW = G > 4 ? 2 : 1;          // heads per wave
+    __shared__ int list[kChunkListMax];
+    __shared__ int list_n;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kDecTiles][kC * kDecStride];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[kDecTiles][kC * kDecStride];
+    __shared__ float qs[G][kD];
+    __shared__ float ps[4][HPW][kC];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t g = blockIdx.x % Hkv;
+    const int64_t rest = blockIdx.x / Hkv;
+    const int j = (int)(rest % n_split);
+    const int64_t i = rest / n_split;
+    const int64_t p = p0 + i;
+    const int64_t Pc = kC * (p / kC);           // start of the open chunk
+    if (wave == 0) {
+        const int ns = sink_units(sink, Pc, kC);
+        write_sink_units(list, ns);
+        const int n = build_unit_list(ids + (g * n_q + i) * k, k, sink, Pc / kC, list + ns);
+        if (lane == 0) {
+            list[ns + n] = (int)(Pc / kC);
+            list_n = ns + n + 1;
+        }
+    }
+    for (int e = tid; e < G * kD; e += kDecThreads) {
+        const uint16_t b = Q[((g * G + e / kD) * n_q + i) * kD + e % kD];
+        qs[e / kD][e % kD] = __uint_as_float((uint32_t)b << 16);
+    }
+    __syncthreads();
+    const int n_tiles = list_n;
+    const int t0 = j * kDecTiles;
+    const int my_tiles = max(0, min(kDecTiles, n_tiles - t0));
+
+    // All of this workgroup's K and V rows are loaded at once: thread t moves
+    // rows t/16 + 16*r, d = 8*(t%16) .. +8; rows of the open chunk past p are
+    // written as zeros (their scores are masked, and zeros keep P.V finite).
+    const uint16_t *Kg = K + g * T_cap * kD;
+    const uint16_t *Vg = V + g * T_cap * kD;
+    for (int u = 0; u < my_tiles; ++u) {
+        const int t = t0 + u;
+        const int64_t c = list[t];
+        const int valid = (t == n_tiles - 1) ? (int)(p - Pc + 1) : kC;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = (tid >> 4) + 16 * r;
+            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (row < valid) {
+                const int64_t off = (c * kC + row) * kD + (tid & 15) * 8;
+                kv = *(const u32x4 *)(Kg + off);
+                vv = *(const u32x4 *)(Vg + off);
+            }
+            *(u32x4 *)(&Ks[u][row * kDecStride + (tid & 15) * 8]) = kv;
+            *(u32x4 *)(&Vs[u][row * kDecStride + (tid & 15) * 8]) = vv;
+        }
+    }
+    __syncthreads();
+
+    float m_run[HPW], l_run[HPW], o0[HPW], o1[HPW];
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) { m_run[e] = -INFINITY; l_run[e] = 0.f; o0[e] = 0.f; o1[e] = 0.f; }
+    const bool serves = wave < G;               // G < 4 leaves waves idle
+    for (int u = 0; u < my_tiles && serves; ++u) {
+        const int t = t0 + u;
+        const int valid = (t == n_tiles - 1) ? (int)(p - Pc + 1) : kC;
+        const uint16_t *kr = &Ks[u][lane * kDecStride];
+#pragma unroll
+        for (int e = 0; e < HPW; ++e) {
+            const int h = wave + 4 * e;
+            float z = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < kD; d += 8) {
+                const u32x4 w = *(const u32x4 *)(kr + d);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    z = fmaf(qs[h][d + 2 * q], bf16_lo(w[q]), z);
+                    z = fmaf(qs[h][d + 2 * q + 1], bf16_hi(w[q]), z);
+                }
+            }
+            z = lane < valid ? z * scale_log2 : -INFINITY;
+            float mt = z;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+            const float m_new = fmaxf(m_run[e], mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[e] - m_new);
+            const float pz = __builtin_amdgcn_exp2f(z - m_new);
+            float sum = pz;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+            m_run[e] = m_new;
+            l_run[e] = l_run[e] * alpha + sum;
+            ps[wave][e][lane] = pz;
+            o0[e] *= alpha;
+            o1[e] *= alpha;
+        }
+        // (a wave reads only the probabilities it wrote: no barrier needed)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+#pragma unroll
+        for (int e = 0; e < HPW; ++e) {
+            const uint16_t *vc = &Vs[u][2 * lane];
+            float a0 = 0.f, a1 = 0.f;
+            for (int key = 0; key < kC; ++key) {
+                const float pk = ps[wave][e][key];
+                const uint32_t w = *(const uint32_t *)(vc + key * kDecStride);
+                a0 = fmaf(pk, bf16_lo(w), a0);
+                a1 = fmaf(pk, bf16_hi(w), a1);
+            }
+            o0[e] += a0;
+            o1[e] += a1;
+        }
+    }
+    if (!serves) return;
+#pragma unroll
+    for (int e = 0; e < HPW; ++e) {
+        const int h = wave + 4 * e;
+        float *dst = part + ((((i * Hkv + g) * n_split + j) * G) + h) * kPartFloats;
+        if (lane == 0) {
+            dst[0] = m_run[e];
+            dst[1] = l_run[e];
+        }
+        dst[2 + 2 * lane] = o0[e];
+        dst[3 + 2 * lane] = o1[e];
+    }
+}
+
+// One workgroup of kD threads per (token, query head): the splits' partials
+// merged in split order.
+template <int G>
+__global__ __launch_bounds__(kD) void decode_combine_kernel(
+    const float *__restrict__ part, int64_t n_q, int64_t Hkv, int n_split,
+    uint16_t *__restrict__ O, float *__restrict__ lse)
+{
+    const int d = threadIdx.x;
+    const int64_t h = blockIdx.x % (Hkv * G);
+    const int64_t i = blockIdx.x / (Hkv * G);
+    const int64_t g = h / G, hh = h % G;
+    const float *base = part + ((i * Hkv + g) * n_split * G + hh) * kPartFloats;
+    float M = -INFINITY;
+    for (int j = 0; j < n_split; ++j) M = fmaxf(M, base[(int64_t)j * G * kPartFloats]);
+    float L = 0.f, acc = 0.f;
+    for (int j = 0; j < n_split; ++j) {
+        const float *pj = base + (int64_t)j * G * kPartFloats;
+        const float w = __builtin_amdgcn_exp2f(pj[0] - M);   // 0 for an empty split
+        L = fmaf(pj[1], w, L);
+        acc = fmaf(pj[2 + d], w, acc);
+    }
+    O[(h * n_q + i) * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
+    if (d == 0) lse[h * n_q + i] = (M + __log2f(L)) * 0.69314718055994530942f;
+}
+
+template <int G>
+hipError_t launch_route_decode_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
+                                 const float *S, int64_t n_cap, int32_t k, int32_t sink,
+                                 int32_t *ids, float *scores, hipStream_t stream)
+{
+    int64_t max_eligible = (p0 + n_q - 1) / kC - sink;
+    if (max_eligible < 0) max_eligible = 0;
+    const size_t shmem = (size_t)(max_eligible > 0 ? max_eligible : 1) * sizeof(uint32_t);
+    const dim3 grid((unsigned)(n_q * Hkv)), block(kRouteThreads);
+#define HGA_ROUTE_DEC(NI)                                                                   \
+    hipLaunchKernelGGL((route_decode_kernel<G, NI>), grid, block, shmem, stream, Q, n_q, Hkv, \
+                       p0, S, n_cap, k, (int)sink, ids, scores)
+    if (max_eligible <= 4 * 64) HGA_ROUTE_DEC(4);
+    else if (max_eligible <= 8 * 64) HGA_ROUTE_DEC(8);
+    else if (max_eligible <= 16 * 64) HGA_ROUTE_DEC(16);
+    else HGA_ROUTE_DEC(32);
+#undef HGA_ROUTE_DEC
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_attend_decode_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                  int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
+                                  const int32_t *ids,
+                                  int32_t k, int32_t sink, float scale, uint16_t *O,
+                                  float *lse, float *part, hipStream_t stream)
+{
+    const int n_split = decode_splits(k, sink);
+    hipLaunchKernelGGL((decode_partial_kernel<G>), dim3((unsigned)(n_q * Hkv * n_split)),
+                       dim3(kDecThreads), 0, stream, Q, K, V, n_q, Hkv, T_cap, p0, ids, k,
+                       (int)sink, scale * 1.44269504088896340736f, n_split, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<G>), dim3((unsigned)(n_q * Hkv * G)), dim3(kD), 0,
+                       stream, part, n_q, Hkv, n_split, O, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_splits(int32_t k, int32_t sink)
+{
+    return (sink + k + 1 + kDecTiles - 1) / kDecTiles;
+}
+
+size_t decode_workspace_bytes(int64_t Hq, int64_t n_q, int32_t k, int32_t sink)
+{
+    return (size_t)n_q * (size_t)Hq * (size_t)decode_splits(k, sink) * kPartFloats *
+           sizeof(float);
+}
+
+hipError_t launch_route_decode(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
+                               int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                               int32_t sink, int32_t *ids, float *scores, hipStream_t stream)
+{
+    if (n_q == 0 || k == 0) return hipSuccess;
+    switch (Hq / Hkv) {
+    case 1: return launch_route_decode_g<1>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
+    case 2: return launch_route_decode_g<2>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
+    case 4: return launch_route_decode_g<4>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
+    case 8: return launch_route_decode_g<8>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_attend_decode(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
+                                float scale, uint16_t *O, float *lse, void *workspace,
+                                hipStream_t stream)
+{
+    if (n_q == 0) return hipSuccess;
+    float *part = (float *)workspace;
+    switch (Hq / Hkv) {
+    case 1: return launch_attend_decode_g<1>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, part, stream);
+    case 2: return launch_attend_decode_g<2>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, part, stream);
+    case 4: return launch_attend_decode_g<4>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, part, stream);
+    case 8: return launch_attend_decode_g<8>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, part, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hga

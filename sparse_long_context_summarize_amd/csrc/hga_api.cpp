@@ -356,6 +356,71 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
                       "hga_attend_bwd_groups launch");
 }
 
+hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                            const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
+                            int32_t *ids, float *scores_or_null, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    if (p0 < 0 || n_q < 0 || n_chunks_valid < 0 || n_chunk_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
+    if (n_chunks_valid > n_chunk_cap)
+        return fail(HGA_ERR_CAPACITY, "n_chunks_valid (%lld) exceeds n_chunk_cap (%lld)",
+                    (long long)n_chunks_valid, (long long)n_chunk_cap);
+    if (n_q == 0 || cfg->top_k == 0) return HGA_OK;
+    // the last token's closed chunks (those before its open chunk)
+    const int64_t need = (p0 + n_q - 1) / hga::kC;
+    if (need > n_chunks_valid)
+        return fail(HGA_ERR_CAPACITY, "the last token needs %lld summaries, %lld valid",
+                    (long long)need, (long long)n_chunks_valid);
+    if (need - cfg->sink_chunks > kMaxEligible)
+        return fail(HGA_ERR_UNSUPPORTED, "more than %lld candidate chunks per token",
+                    (long long)kMaxEligible);
+    if (!Q || !ids || (need > 0 && !summaries))
+        return fail(HGA_ERR_INVALID_ARG, "Q, summaries or ids is NULL");
+    return hip_status(hga::launch_route_decode((const uint16_t *)Q, cfg->n_q_heads,
+                                               cfg->n_kv_heads, p0, n_q, summaries, n_chunk_cap,
+                                               cfg->top_k, cfg->sink_chunks, ids,
+                                               scores_or_null, stream),
+                      "hga_route_decode launch");
+}
+
+size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t n_q)
+{
+    if (check_config(cfg) != HGA_OK || n_q < 0) return 0;
+    return hga::decode_workspace_bytes(cfg->n_q_heads, n_q, cfg->top_k, cfg->sink_chunks);
+}
+
+hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K, const void *V,
+                             int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids, void *O,
+                             float *lse, void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    if (p0 < 0 || n_q < 0 || T_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
+    if (p0 + n_q > T_cap)
+        return fail(HGA_ERR_INVALID_ARG, "p0 + n_q (%lld) exceeds T_cap (%lld)",
+                    (long long)(p0 + n_q), (long long)T_cap);
+    if (n_q == 0) return HGA_OK;
+    if (!Q || !K || !V || !O || !lse || (cfg->top_k > 0 && !ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const size_t need = hga::decode_workspace_bytes(cfg->n_q_heads, n_q, cfg->top_k,
+                                                    cfg->sink_chunks);
+    if (!workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    return hip_status(hga::launch_attend_decode((const uint16_t *)Q, (const uint16_t *)K,
+                                                (const uint16_t *)V, cfg->n_q_heads,
+                                                cfg->n_kv_heads, T_cap, p0, n_q, ids,
+                                                cfg->top_k, cfg->sink_chunks,
+                                                effective_scale(cfg), (uint16_t *)O, lse,
+                                                workspace, stream),
+                      "hga_attend_decode launch");
+}
+
 size_t hga_diag_gather_sink_words(const hga_config *cfg, int64_t n_q)
 {
     if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;

@@ -278,11 +278,14 @@ struct RouteLds {
 // (the first kScoreWaves of the workgroup). Both only distribute the
 // candidates over lanes: each score's arithmetic, and so every score, is the
 // same whichever lanes compute it.
-// q_row(r, dseg): the 8 bf16 of query row r (0 .. G*64-1: head g*G + r/64,
-// query r%64 of the block) at d = 8*dseg .. +8, from wherever the caller
-// holds them (the values, not their source, fix the result).
+// q_row(r, dseg): the 8 bf16 of query row r (0 .. G*kBq-1: head g*G +
+// r/kBq, query r%kBq of the block) at d = 8*dseg .. +8, from wherever the
+// caller holds them (the values, not their source, fix the result).
+// kBq = 64: query blocks of 64 starting at p0 + 64*b. kBq = 1 (decode): block
+// b is the single token at p0 + b, and its candidates end at the start of its
+// own open chunk, P = 64*floor((p0 + b)/64).
 template <int G, int NI, bool kGroups, int kBatch, int kScoreWaves, typename QRow,
-          typename Emit>
+          typename Emit, int kBq = kC>
 __device__ __forceinline__ int route_block(
     RouteLds &sh, uint32_t *keys, QRow q_row, int64_t n_q, int64_t g,
     int64_t b, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
@@ -294,8 +297,8 @@ __device__ __forceinline__ int route_block(
     // below, and the selection inside them, run on scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool act = wave < kRouteWaves;
-    const int64_t n_blocks = n_q / kC;
-    const int64_t P = p0 + b * kC;
+    const int64_t n_blocks = n_q / kBq;
+    const int64_t P = kBq == kC ? p0 + b * kC : kC * ((p0 + b) / kC);
     int *chl = sh.chl;
     int nE = (int)max((int64_t)0, P / kC - c_lo);
     if (kGroups) {
@@ -335,15 +338,23 @@ __device__ __forceinline__ int route_block(
     // sums rows r0, r0 + 16, ... at d = 8*dseg .. +8.
     if (act) {
         const int dseg = tid & 15, r0 = tid >> 4;
-        u32x4 w[G * 4];
+        constexpr int kRows = G * kBq, kPer = (kRows + 15) / 16;
+        u32x4 w[kPer];
 #pragma unroll
-        for (int m = 0; m < G * 4; ++m) w[m] = q_row(r0 + 16 * m, dseg);
+        for (int m = 0; m < kPer; ++m) {
+            if constexpr (kRows % 16 == 0) {
+                w[m] = q_row(r0 + 16 * m, dseg);
+            } else {
+                const u32x4 z = {0u, 0u, 0u, 0u};   // bf16 zeros
+                w[m] = (r0 + 16 * m < kRows) ? q_row(r0 + 16 * m, dseg) : z;
+            }
+        }
         if (wave * 4 < nE) load_batch(wave * 4);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int m = 0; m < G * 4; ++m)
+        for (int m = 0; m < kPer; ++m)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 acc[2 * q] += bf16_lo(w[m][q]);
@@ -359,7 +370,7 @@ __device__ __forceinline__ int route_block(
         float s = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s += sh.part[r][tid];
-        sh.qbar[tid] = s * (1.0f / (float)(G * kC));   // a power of two: exact
+        sh.qbar[tid] = s * (1.0f / (float)(G * kBq));  // a power of two: exact
     }
     __syncthreads();
 

@@ -24,7 +24,8 @@ HGA_BF16 = 0
 EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
-            "hga_attend_bwd_groups", "hga_diag_gather_sink_words", "hga_diag_gather",
+            "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
+            "hga_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
             "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
 
@@ -81,6 +82,11 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
+    L.hga_route_decode.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp]
+    L.hga_decode_workspace_bytes.argtypes = [_cfgp, _i64]
+    L.hga_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.hga_attend_decode.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
     L.hga_diag_gather_sink_words.argtypes = [_cfgp, _i64]
     L.hga_diag_gather_sink_words.restype = ctypes.c_size_t
     L.hga_diag_gather.argtypes = [_cfgp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t,
@@ -91,7 +97,8 @@ def lib() -> ctypes.CDLL:
     for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
                "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
-               "hga_attend_bwd_groups", "hga_diag_gather"):
+               "hga_attend_bwd_groups", "hga_diag_gather", "hga_route_decode",
+               "hga_attend_decode"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
@@ -241,6 +248,27 @@ def _m_attend_bwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, d
             ws_bytes, _stream(stream))
 
 
+def _m_route_decode(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids,
+                    scores=None, stream=None):
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _stream(stream))
+
+
+def _m_attend_decode(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, workspace, stream=None):
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+            _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
+            _dev(lse, "lse", torch.float32), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=None):
     if K.shape != V.shape:
         raise ValueError("K and V shapes differ")
@@ -255,7 +283,8 @@ _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
             "hga_attend_fwd_groups": _m_attend_fwd_groups,
             "hga_attend_bwd_groups": _m_attend_bwd_groups,
-            "hga_diag_gather": _m_diag_gather}
+            "hga_diag_gather": _m_diag_gather, "hga_route_decode": _m_route_decode,
+            "hga_attend_decode": _m_attend_decode}
 
 
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
@@ -335,6 +364,26 @@ def hga_attend_bwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: 
     _check("hga_attend_bwd_groups", lib().hga_attend_bwd_groups(
         *_m_attend_bwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, dO, dQ, dK, dV, workspace,
                               stream)))
+
+
+def hga_route_decode(cfg: hga_config, Q: torch.Tensor, p0: int, summaries: torch.Tensor,
+                     n_chunks_valid: int, ids: torch.Tensor, scores: torch.Tensor | None = None,
+                     stream=None) -> None:
+    """Routing of a decode step, one token at a time (ids [Hkv][n_q][k])."""
+    _check("hga_route_decode", lib().hga_route_decode(
+        *_m_route_decode(cfg, Q, p0, summaries, n_chunks_valid, ids, scores, stream)))
+
+
+def hga_decode_workspace_bytes(cfg: hga_config, n_q: int) -> int:
+    return int(lib().hga_decode_workspace_bytes(ctypes.byref(cfg), n_q))
+
+
+def hga_attend_decode(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                      p0: int, ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
+                      workspace: torch.Tensor, stream=None) -> None:
+    """Attention of a decode step (split over the routed chunks, then merged)."""
+    _check("hga_attend_decode", lib().hga_attend_decode(
+        *_m_attend_decode(cfg, Q, K, V, p0, ids, O, lse, workspace, stream)))
 
 
 def hga_diag_gather_sink_words(cfg: hga_config, n_q: int) -> int:

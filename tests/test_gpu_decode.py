@@ -1,0 +1,138 @@
+"""GPU parity of routed decode (hga_route_decode, hga_attend_decode) against
+the CPU oracle: a step of n_q tokens at positions p0 .. p0+n_q-1, each routing
+on its own query heads over the closed chunks before its open chunk and
+attending the sink window, its chunks and its open chunk up to itself."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_close, check_ids, from_dev, to_dev_bf16
+from sparse_long_context_summarize_amd import hga, inputs
+
+pytestmark = pytest.mark.gpu
+
+C = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+    torch.cuda.init()
+    yield
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def decode(x, p0, n_q, k, s=0, ids_override=None):
+    """x: Q [Hq][>=n_q][D] (the step's queries are its first n_q rows), K/V
+    [Hkv][T][D] holding every position up to p0 + n_q - 1."""
+    Q = x["Q"][:, :n_q]
+    Hq, _, D = Q.shape
+    Hkv, T, _ = x["K"].shape
+    cfg = hga.make_config(Hq, Hkv, k, sink_chunks=s)
+    Qd, K, V = to_dev_bf16(Q), to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    n_closed = (p0 + n_q - 1) // C
+    S = torch.full((Hkv, max(n_closed, 1), D), float("nan"), device="cuda")
+    hga.hga_summarize(cfg, K, 0, n_closed * C, S)
+    ids = torch.full((Hkv, n_q, k), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((Hkv, n_q, k), float("nan"), device="cuda")
+    hga.hga_route_decode(cfg, Qd, p0, S, n_closed, ids, sc)
+    if ids_override is not None:
+        ids = torch.from_numpy(np.ascontiguousarray(ids_override, dtype=np.int32)).cuda()
+        cfg = hga.make_config(Hq, Hkv, ids.shape[2], sink_chunks=s)
+    O = torch.full((Hq, n_q, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Hq, n_q), float("nan"), device="cuda")
+    ws = torch.full((hga.hga_decode_workspace_bytes(cfg, n_q),), 255, dtype=torch.uint8,
+                    device="cuda")
+    hga.hga_attend_decode(cfg, Qd, K, V, p0, ids, O, lse, ws)
+    torch.cuda.synchronize()
+    return dict(ids=ids.cpu().numpy(), scores=from_dev(sc), O=from_dev(O), lse=from_dev(lse),
+                S=from_dev(S), Q=Q, n_closed=n_closed)
+
+
+def check(x, p0, n_q, k, s, res, where, routed=True):
+    Hkv = x["K"].shape[0]
+    if routed and res["n_closed"] > 0:
+        S_ref = oracle.summarize(x["K"], C, 0, res["n_closed"])
+        ids_ref, sig = oracle.route_decode(res["Q"], S_ref, p0, k, Hkv, want_scores=True,
+                                           sink=s * C)
+        check_ids(res["ids"], ids_ref, sig, p0, C=C, Bq=1, where=where, sink_chunks=s)
+    O_ref, lse_ref = oracle.attend_decode(res["Q"], x["K"], x["V"], res["ids"], p0, sink=s * C)
+    st = check_close(f"{where} O", res["O"], O_ref)
+    check_close(f"{where} lse", res["lse"], lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+    log(f"{where}: O {st}")
+
+
+@pytest.mark.parametrize("p0,n_q", [(1597, 8), (1600, 1), (1663, 1), (0, 3), (60, 8)])
+def test_tiny_positions(p0, n_q):
+    w = inputs.TINY
+    x = inputs.generate(w, bf16=True)          # T = 2048 holds every position used
+    res = decode(x, p0, n_q, 4)
+    check(x, p0, n_q, 4, 0, res, f"tiny p0={p0} n_q={n_q}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (8, 2), (8, 1), (16, 8)])
+@pytest.mark.parametrize("k,s", [(3, 0), (7, 2)])
+def test_head_layouts(Hq, Hkv, k, s):
+    T = 2048
+    x = inputs.small_random(600 + Hq + k, Hq, Hkv, 128, T, 8, bf16=True)
+    res = decode(x, T - 8, 8, k, s)
+    check(x, T - 8, 8, k, s, res, f"Hq={Hq} Hkv={Hkv} k={k} s={s}")
+
+
+def test_layer16k_step():
+    w = inputs.LAYER16K
+    x = inputs.generate(w)
+    res = decode(x, w.T - 8, 8, w.k)
+    check(x, w.T - 8, 8, w.k, 0, res, "16K decode, 8 tokens")
+
+
+def test_layer128k_single_token():
+    w = inputs.LAYER128K
+    x = inputs.generate(w)
+    res = decode(x, w.T - 1, 1, w.k)
+    check(x, w.T - 1, 1, w.k, 0, res, "128K decode, 1 token")
+
+
+def test_more_than_2048_candidates():
+    T, p0 = 64 * 2201, 64 * 2200 + 15          # 2200 closed chunks before the open one
+    x = inputs.small_random(610, 4, 1, 128, T, 2, bf16=True)
+    res = decode(x, p0, 2, 40)
+    check(x, p0, 2, 40, 0, res, "2200 candidates")
+
+
+def test_largest_budget_and_sink():
+    T, p0 = 64 * 301, 64 * 300 + 1
+    x = inputs.small_random(611, 4, 2, 128, T, 4, bf16=True)
+    res = decode(x, p0, 4, 256, s=3)
+    check(x, p0, 4, 256, 3, res, "k=256 sink 3")
+
+
+def test_messy_id_rows():
+    """Rows are sets: repeats, order, -1, ids at or past the open chunk, and
+    sink chunks add nothing."""
+    T, p0, n_q, k = 2048, 1590, 6, 9           # open chunks 24 and 24/25
+    x = inputs.small_random(612, 4, 1, 128, T, n_q, bf16=True)
+    rows = np.array([[[3, 3, 24, -1, 0, 23, 7, 7, 1],
+                      [24, 25, 99, -5, 2, 2, 2, 2, 2],
+                      [-1] * 9,
+                      [23, 22, 21, 20, 19, 18, 17, 16, 15],
+                      [0, 1, 2, 3, 4, 5, 6, 7, 8],
+                      [25, 24, 23, 1 << 30, 12, 12, 11, 10, 9]]], np.int32)
+    res = decode(x, p0, n_q, k, s=2, ids_override=rows)
+    check(x, p0, n_q, k, 2, res, "messy rows", routed=False)
+
+
+def test_routed_scores_and_determinism():
+    w = inputs.LAYER16K
+    x = inputs.generate(w)
+    a = decode(x, w.T - 8, 8, w.k)
+    b = decode(x, w.T - 8, 8, w.k)
+    for name in ("ids", "scores", "O", "lse"):
+        np.testing.assert_array_equal(a[name], b[name], err_msg=name)
+    assert np.all(np.isneginf(a["scores"][a["ids"] < 0]))
