@@ -310,6 +310,7 @@ def extra_timings(torch, hga, inputs, dev):
                      device=dev)
     res.update(segloop_timing(torch, hga, inputs, dev))
     res.update(group_timings(torch, hga, inputs, dev))
+    res.update(decode_timings(torch, hga, inputs, dev))
     res.update(attend_timings(torch, hga, inputs, dev))
     try:
         times = []
@@ -461,6 +462,60 @@ def group_timings(torch, hga, inputs, dev):
         "groups16k_bwd_algorithmic_gflop": fl_bwd / 1e9,
         "groups16k_bwd_tflops": fl_bwd / (ms_bwd * 1e-3) / 1e12,
     })
+    return res
+
+
+def decode_timings(torch, hga, inputs, dev):
+    """Routed decode at batch 1: one token after the 128K-history workload's
+    last position (k = 32) and 8 tokens after the 16K layer's (k = 16), each
+    call and the step (route + attend) HIP-event timed (median of 10).
+    Algorithmic bytes: the summaries each token scores, its routed and open
+    chunks' K and V (bf16), Q read and O written."""
+    res = {}
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    for w, n_q, tag in ((inputs.LAYER128K, 1, "decode128k_1tok"),
+                        (inputs.LAYER16K, 8, "decode16k_8tok")):
+        x = inputs.generate(w)
+        K, V = up(x["K"]), up(x["V"])
+        Q = up(np.ascontiguousarray(x["Q"][:, :n_q]))
+        p0 = w.T - n_q
+        cfg = hga.make_config(w.Hq, w.Hkv, w.k)
+        n_closed = (p0 + n_q - 1) // C
+        S = torch.empty((w.Hkv, n_closed, w.D), device=dev)
+        hga.hga_summarize(cfg, K, 0, n_closed * C, S)
+        ids = torch.empty((w.Hkv, n_q, w.k), dtype=torch.int32, device=dev)
+        O = torch.empty((w.Hq, n_q, w.D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.Hq, n_q), device=dev)
+        ws = torch.empty(hga.hga_decode_workspace_bytes(cfg, p0, n_q), dtype=torch.uint8,
+                         device=dev)
+        route = hga.prepare("hga_route_decode", cfg, Q, p0, S, n_closed, ids, ws)
+        attend = hga.prepare("hga_attend_decode", cfg, Q, K, V, p0, ids, O, lse, ws)
+
+        def step():
+            route()
+            attend()
+
+        t_route = _median_ms(torch, route)
+        t_att = _median_ms(torch, attend)
+        t_step = _median_ms(torch, step)
+        toks = p0 + np.arange(n_q)
+        n_sum = float(sum(t // C for t in toks)) * w.Hkv
+        n_tiles = float((ids.cpu().numpy() >= 0).sum() + w.Hkv * n_q)
+        route_bytes = n_sum * w.D * 4 + w.Hq * n_q * w.D * 2
+        att_bytes = n_tiles * C * w.D * 2 * 2 + w.Hq * n_q * w.D * 2 * 2
+        res.update({
+            f"{tag}_route_us": t_route * 1e3,
+            f"{tag}_attend_us": t_att * 1e3,
+            f"{tag}_step_us": t_step * 1e3,
+            f"{tag}_tokens_per_s": n_q / (t_step * 1e-3),
+            f"{tag}_algorithmic_MB": (route_bytes + att_bytes) / 1e6,
+            f"{tag}_attend_GBps": att_bytes / (t_att * 1e-3) / 1e9,
+            f"{tag}_step_GBps": (route_bytes + att_bytes) / (t_step * 1e-3) / 1e9,
+        })
+        del K, V, S
     return res
 
 

@@ -293,13 +293,20 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
  *   ids      device int32 [Hkv][n_q][k];  scores_or_null as for hga_route
  *   summaries: (p0 + n_q - 1)/C <= n_chunks_valid <= n_chunk_cap, else
  *            HGA_ERR_CAPACITY
+ *   workspace  device scratch (the candidates' scores), at least
+ *            hga_decode_workspace_bytes(cfg, p0, n_q) bytes, else
+ *            HGA_ERR_CAPACITY; owned by the caller, contents on entry
+ *            ignored and on return unspecified; calls that share it must not
+ *            overlap in time (the same buffer may serve hga_attend_decode).
  */
 hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
                             const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
-                            int32_t *ids, float *scores_or_null, hipStream_t stream);
+                            int32_t *ids, float *scores_or_null, void *workspace,
+                            size_t ws_bytes, hipStream_t stream);
 
-/* Device workspace hga_attend_decode needs for n_q tokens (0 on bad args). */
-size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t n_q);
+/* Device workspace that hga_route_decode and hga_attend_decode need for a
+ * step of n_q tokens at p0 (one size serves both; 0 on bad arguments). */
+size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t p0, int64_t n_q);
 
 /*
  * hga_attend_decode -- exact attention of the step's tokens: token p attends
@@ -311,8 +318,10 @@ size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t n_q);
  *   Q, O   device bf16 [Hq][n_q][D];  K, V device bf16 [Hkv][T_cap][D]
  *   ids    device int32 [Hkv][n_q][k];  lse device f32 [Hq][n_q]
  *   p0 + n_q <= T_cap, else HGA_ERR_INVALID_ARG
- *   workspace  at least hga_decode_workspace_bytes(cfg, n_q) bytes, else
- *            HGA_ERR_CAPACITY; calls that share it must not overlap in time.
+ *   workspace  device scratch (the per-split partial results), at least
+ *            hga_decode_workspace_bytes(cfg, p0, n_q) bytes, else
+ *            HGA_ERR_CAPACITY; owned by the caller, contents on entry ignored;
+ *            calls that share it must not overlap in time.
  */
 hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K, const void *V,
                              int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids, void *O,

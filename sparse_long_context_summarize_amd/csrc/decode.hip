@@ -5,8 +5,14 @@
 // before its open chunk, and attends the sink window, its routed chunks and
 // its open chunk up to itself.
 //
-//   route_decode_kernel   the router (route_block) with one-token blocks: one
-//                         256-thread workgroup per (token, kv head).
+//   decode_score_kernel   routing, step 1: the token's mean query (over its G
+//                         heads) scored against the summaries of its candidate
+//                         chunks (s <= c < Pc/C), 256 candidates per
+//                         workgroup so that one token's thousands of summary
+//                         rows are read by many CUs at once; order-preserving
+//                         keys go to the workspace.
+//   decode_select_kernel  routing, step 2: the top-k by (score desc, id asc)
+//                         over those keys, with the router's selection code.
 //   decode_partial_kernel split-K attention: the tiles of a (token, kv head)
 //                         -- sink chunks, routed chunks, the open chunk's
 //                         prefix -- are dealt kDecTiles at a time to
@@ -24,27 +30,131 @@
 namespace hga {
 namespace {
 
-template <int G, int NI>
-__global__ __launch_bounds__(kRouteThreads) void route_decode_kernel(
-    const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
-    const float *__restrict__ S, int64_t n_cap, int k, int sink,
-    int32_t *__restrict__ ids, float *__restrict__ scores)
+constexpr int kScoreBlock = 256;            // candidates per scoring workgroup
+
+// Candidates of token p: chunks s .. Pc/C - 1 (none if the sink covers them).
+__device__ __forceinline__ int decode_candidates(int64_t p, int sink)
 {
-    extern __shared__ uint32_t keys[];          // [candidates of this token]
-    __shared__ RouteLds sh;
+    return (int)max((int64_t)0, p / kC - sink);
+}
+
+// Workgroup (token i, kv head g, block blk): candidates blk*256 .. +256.
+template <int G>
+__global__ __launch_bounds__(kRouteThreads) void decode_score_kernel(
+    const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
+    const float *__restrict__ S, int64_t n_cap, int sink, int n_blk, int64_t kcap,
+    uint32_t *__restrict__ keys)
+{
+    __shared__ float qbar[kD];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t g = blockIdx.x % Hkv;
-    const int64_t i = blockIdx.x / Hkv;        // token
+    const int64_t rest = blockIdx.x / Hkv;
+    const int blk = (int)(rest % n_blk);
+    const int64_t i = rest / n_blk;
+    const int nE = decode_candidates(p0 + i, sink);
+    const int c0 = blk * kScoreBlock;
+    if (c0 >= nE) return;                       // uniform across the workgroup
+
+    // this lane's 16 summary rows first (they do not depend on the mean):
+    // chunk c0 + 16*u + 4*wave + sub, 8 dims per lane
+    const int sdseg = lane & 15, sub = lane >> 4;
+    const float *Sg = S + (g * n_cap + sink) * kD + sdseg * 8;
+    f32x4 slo[16], shi[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int c = min(c0 + 16 * u + 4 * wave + sub, nE - 1);   // in bounds; unused past nE
+        slo[u] = *(const f32x4 *)(Sg + (int64_t)c * kD);
+        shi[u] = *(const f32x4 *)(Sg + (int64_t)c * kD + 4);
+    }
+    if (tid < kD) {                             // mean over the G heads, in head order
+        float a = 0.f;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const uint16_t b = Q[((g * G + h) * n_q + i) * kD + tid];
+            a += __uint_as_float((uint32_t)b << 16);
+        }
+        qbar[tid] = a * (1.0f / (float)G);      // a power of two: exact
+    }
+    __syncthreads();
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = qbar[sdseg * 8 + e];
+    uint32_t *kout = keys + (i * Hkv + g) * kcap;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        float sc = qv[0] * slo[u][0];
+        sc = fmaf(qv[1], slo[u][1], sc);
+        sc = fmaf(qv[2], slo[u][2], sc);
+        sc = fmaf(qv[3], slo[u][3], sc);
+        sc = fmaf(qv[4], shi[u][0], sc);
+        sc = fmaf(qv[5], shi[u][1], sc);
+        sc = fmaf(qv[6], shi[u][2], sc);
+        sc = fmaf(qv[7], shi[u][3], sc);
+        sc = row16_sum(sc);
+        const int c = c0 + 16 * u + 4 * wave + sub;
+        if (sdseg == 0 && c < nE) kout[c] = score_key(sc);
+    }
+}
+
+constexpr int kSelWaves = 8;                // selection workgroup: 512 threads
+
+// Final stage of a two-stage selection: wave 0 over the kSelWaves * k
+// survivors (holes hold key 0, below every score's key), NI * 64 of them.
+template <int NI, typename IdOf, typename Emit>
+__device__ __forceinline__ void select_survivors(const uint32_t *cand_key, int k, IdOf id_of,
+                                                 Emit emit)
+{
+    select_top_k_reg<NI>(cand_key, kSelWaves * k, k, id_of, emit);
+}
+
+// Workgroup (token i, kv head g): top-k of the token's keys; ids are chunk
+// ids (candidate index + s), ascending, -1 padded. Up to 256 candidates one
+// wave selects; beyond that each of the 8 waves selects the top k of its
+// share (NI * 64 candidates at most) and wave 0 selects among the survivors,
+// kept in candidate order so that ties still go to the lower id.
+template <int NI>
+__global__ __launch_bounds__(kSelWaves * 64) void decode_select_kernel(
+    int64_t n_q, int64_t Hkv, int64_t p0, int k, int sink, int64_t kcap,
+    const uint32_t *__restrict__ keys, int32_t *__restrict__ ids, float *__restrict__ scores)
+{
+    __shared__ uint32_t cand_key[kSelWaves * kMaxTopK];
+    __shared__ int cand_pos[kSelWaves * kMaxTopK];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t g = blockIdx.x % Hkv;
+    const int64_t i = blockIdx.x / Hkv;
+    const int nE = decode_candidates(p0 + i, sink);
+    const uint32_t *kin = keys + (i * Hkv + g) * kcap;
     int32_t *out = ids + (g * n_q + i) * k;
     float *sout = scores ? scores + (g * n_q + i) * k : nullptr;
-    auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {   // row: head in group
-        return *(const u32x4 *)(Q + ((g * G + row) * n_q + i) * kD + dseg * 8);
-    };
     auto emit = [&](int r, int id, float sc) __attribute__((always_inline)) {
         out[r] = id;
         if (sout) sout[r] = sc;
     };
-    route_block<G, NI, false, 16, kRouteWaves, decltype(q_row), decltype(emit), 1>(
-        sh, keys, q_row, n_q, g, i, p0, S, n_cap, k, nullptr, 0, sink, emit);
+    if (nE <= 4 * 64) {
+        auto id_of = [&](int c) __attribute__((always_inline)) { return c + sink; };
+        if (wave == 0) select_top_k_reg<4>(kin, nE, k, id_of, emit);
+        return;
+    }
+    const int per = (nE + kSelWaves - 1) / kSelWaves;   // <= NI * 64 (host-chosen NI)
+    const int lo = min(nE, wave * per);
+    const int hi = min(nE, lo + per);
+    {
+        auto id_of = [&](int c) __attribute__((always_inline)) { return c + lo; };
+        auto keep = [&](int r, int pos, float sc) __attribute__((always_inline)) {
+            cand_key[wave * k + r] = pos >= 0 ? score_key(sc) : 0u;
+            cand_pos[wave * k + r] = pos;
+        };
+        select_top_k_reg<NI>(kin + lo, hi - lo, k, id_of, keep);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    auto id_of = [&](int c) __attribute__((always_inline)) { return cand_pos[c] + sink; };
+    if (k <= 32) select_survivors<4>(cand_key, k, id_of, emit);
+    else if (k <= 64) select_survivors<8>(cand_key, k, id_of, emit);
+    else if (k <= 128) select_survivors<16>(cand_key, k, id_of, emit);
+    else select_survivors<32>(cand_key, k, id_of, emit);
 }
 
 constexpr int kDecThreads = 256;
@@ -188,47 +298,74 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
 }
 
 // One workgroup of kD threads per (token, query head): the splits' partials
-// merged in split order.
+// merged in split order (every split's max and sum loaded at once first).
+constexpr int kMaxSplits = (kMaxSink + kMaxTopK + 1 + 1) / 2;
+
 template <int G>
 __global__ __launch_bounds__(kD) void decode_combine_kernel(
     const float *__restrict__ part, int64_t n_q, int64_t Hkv, int n_split,
     uint16_t *__restrict__ O, float *__restrict__ lse)
 {
+    __shared__ float ms[kMaxSplits], ws[kMaxSplits];
+    __shared__ float M_s, L_s;
     const int d = threadIdx.x;
     const int64_t h = blockIdx.x % (Hkv * G);
     const int64_t i = blockIdx.x / (Hkv * G);
     const int64_t g = h / G, hh = h % G;
     const float *base = part + ((i * Hkv + g) * n_split * G + hh) * kPartFloats;
-    float M = -INFINITY;
-    for (int j = 0; j < n_split; ++j) M = fmaxf(M, base[(int64_t)j * G * kPartFloats]);
-    float L = 0.f, acc = 0.f;
-    for (int j = 0; j < n_split; ++j) {
-        const float *pj = base + (int64_t)j * G * kPartFloats;
-        const float w = __builtin_amdgcn_exp2f(pj[0] - M);   // 0 for an empty split
-        L = fmaf(pj[1], w, L);
-        acc = fmaf(pj[2 + d], w, acc);
+    const int64_t step = (int64_t)G * kPartFloats;
+    for (int j = d; j < n_split; j += kD) {
+        ms[j] = base[j * step];
+        ws[j] = base[j * step + 1];
     }
-    O[(h * n_q + i) * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
-    if (d == 0) lse[h * n_q + i] = (M + __log2f(L)) * 0.69314718055994530942f;
+    __syncthreads();
+    if (d == 0) {
+        float M = -INFINITY;
+        for (int j = 0; j < n_split; ++j) M = fmaxf(M, ms[j]);
+        float L = 0.f;
+        for (int j = 0; j < n_split; ++j) {
+            const float w = __builtin_amdgcn_exp2f(ms[j] - M);   // 0 for an empty split
+            L = fmaf(ws[j], w, L);
+            ms[j] = w;
+        }
+        M_s = M;
+        L_s = L;
+    }
+    __syncthreads();
+    float acc = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < n_split; ++j) acc = fmaf(base[j * step + 2 + d], ms[j], acc);
+    O[(h * n_q + i) * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)(acc / L_s));
+    if (d == 0) lse[h * n_q + i] = (M_s + __log2f(L_s)) * 0.69314718055994530942f;
 }
 
 template <int G>
 hipError_t launch_route_decode_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int64_t n_q,
                                  const float *S, int64_t n_cap, int32_t k, int32_t sink,
-                                 int32_t *ids, float *scores, hipStream_t stream)
+                                 int32_t *ids, float *scores, uint32_t *keys,
+                                 hipStream_t stream)
 {
-    int64_t max_eligible = (p0 + n_q - 1) / kC - sink;
-    if (max_eligible < 0) max_eligible = 0;
-    const size_t shmem = (size_t)(max_eligible > 0 ? max_eligible : 1) * sizeof(uint32_t);
-    const dim3 grid((unsigned)(n_q * Hkv)), block(kRouteThreads);
-#define HGA_ROUTE_DEC(NI)                                                                   \
-    hipLaunchKernelGGL((route_decode_kernel<G, NI>), grid, block, shmem, stream, Q, n_q, Hkv, \
-                       p0, S, n_cap, k, (int)sink, ids, scores)
-    if (max_eligible <= 4 * 64) HGA_ROUTE_DEC(4);
-    else if (max_eligible <= 8 * 64) HGA_ROUTE_DEC(8);
-    else if (max_eligible <= 16 * 64) HGA_ROUTE_DEC(16);
-    else HGA_ROUTE_DEC(32);
-#undef HGA_ROUTE_DEC
+    const int64_t kcap = decode_key_capacity(p0, n_q, sink);
+    if (kcap > 0) {
+        const int n_blk = (int)((kcap + kScoreBlock - 1) / kScoreBlock);
+        hipLaunchKernelGGL((decode_score_kernel<G>), dim3((unsigned)(n_q * Hkv * n_blk)),
+                           dim3(kRouteThreads), 0, stream, Q, n_q, Hkv, p0, S, n_cap,
+                           (int)sink, n_blk, kcap, keys);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(n_q * Hkv)), block(kSelWaves * 64);
+#define HGA_SELECT_DEC(NI)                                                                  \
+    hipLaunchKernelGGL((decode_select_kernel<NI>), grid, block, 0, stream, n_q, Hkv, p0, k,  \
+                       (int)sink, kcap, keys, ids, scores)
+    // each wave's share of the most candidates any token has
+    const int64_t per = (kcap + kSelWaves - 1) / kSelWaves;
+    if (per <= 4 * 64) HGA_SELECT_DEC(4);
+    else if (per <= 8 * 64) HGA_SELECT_DEC(8);
+    else if (per <= 16 * 64) HGA_SELECT_DEC(16);
+    else if (per <= 32 * 64) HGA_SELECT_DEC(32);
+    else HGA_SELECT_DEC(48);
+#undef HGA_SELECT_DEC
     return hipGetLastError();
 }
 
@@ -257,22 +394,37 @@ int decode_splits(int32_t k, int32_t sink)
     return (sink + k + 1 + kDecTiles - 1) / kDecTiles;
 }
 
-size_t decode_workspace_bytes(int64_t Hq, int64_t n_q, int32_t k, int32_t sink)
+int64_t decode_key_capacity(int64_t p0, int64_t n_q, int32_t sink)
 {
-    return (size_t)n_q * (size_t)Hq * (size_t)decode_splits(k, sink) * kPartFloats *
-           sizeof(float);
+    if (n_q <= 0) return 0;
+    const int64_t c = (p0 + n_q - 1) / kC - sink;   // the last token has the most candidates
+    return c > 0 ? c : 0;
+}
+
+size_t decode_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t p0, int64_t n_q, int32_t k,
+                              int32_t sink)
+{
+    // the router's keys and the attention's partials are used one call after
+    // the other: one buffer serves both
+    const size_t keys = (size_t)n_q * (size_t)Hkv * (size_t)decode_key_capacity(p0, n_q, sink) *
+                        sizeof(uint32_t);
+    const size_t parts = (size_t)n_q * (size_t)Hq * (size_t)decode_splits(k, sink) *
+                         kPartFloats * sizeof(float);
+    return keys > parts ? keys : parts;
 }
 
 hipError_t launch_route_decode(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                                int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                               int32_t sink, int32_t *ids, float *scores, hipStream_t stream)
+                               int32_t sink, int32_t *ids, float *scores, void *workspace,
+                               hipStream_t stream)
 {
     if (n_q == 0 || k == 0) return hipSuccess;
+    uint32_t *keys = (uint32_t *)workspace;
     switch (Hq / Hkv) {
-    case 1: return launch_route_decode_g<1>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
-    case 2: return launch_route_decode_g<2>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
-    case 4: return launch_route_decode_g<4>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
-    case 8: return launch_route_decode_g<8>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, stream);
+    case 1: return launch_route_decode_g<1>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, keys, stream);
+    case 2: return launch_route_decode_g<2>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, keys, stream);
+    case 4: return launch_route_decode_g<4>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, keys, stream);
+    case 8: return launch_route_decode_g<8>(Q, Hkv, p0, n_q, S, n_cap, k, sink, ids, scores, keys, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -358,7 +358,8 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
 
 hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
                             const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
-                            int32_t *ids, float *scores_or_null, hipStream_t stream)
+                            int32_t *ids, float *scores_or_null, void *workspace,
+                            size_t ws_bytes, hipStream_t stream)
 {
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
@@ -379,17 +380,23 @@ hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, in
                     (long long)kMaxEligible);
     if (!Q || !ids || (need > 0 && !summaries))
         return fail(HGA_ERR_INVALID_ARG, "Q, summaries or ids is NULL");
+    const size_t ws_need = hga::decode_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, p0, n_q,
+                                                       cfg->top_k, cfg->sink_chunks);
+    if (!workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < ws_need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, ws_need);
     return hip_status(hga::launch_route_decode((const uint16_t *)Q, cfg->n_q_heads,
                                                cfg->n_kv_heads, p0, n_q, summaries, n_chunk_cap,
                                                cfg->top_k, cfg->sink_chunks, ids,
-                                               scores_or_null, stream),
+                                               scores_or_null, workspace, stream),
                       "hga_route_decode launch");
 }
 
-size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t n_q)
+size_t hga_decode_workspace_bytes(const hga_config *cfg, int64_t p0, int64_t n_q)
 {
-    if (check_config(cfg) != HGA_OK || n_q < 0) return 0;
-    return hga::decode_workspace_bytes(cfg->n_q_heads, n_q, cfg->top_k, cfg->sink_chunks);
+    if (check_config(cfg) != HGA_OK || p0 < 0 || n_q < 0) return 0;
+    return hga::decode_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, p0, n_q, cfg->top_k,
+                                       cfg->sink_chunks);
 }
 
 hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K, const void *V,
@@ -407,8 +414,8 @@ hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K
     if (n_q == 0) return HGA_OK;
     if (!Q || !K || !V || !O || !lse || (cfg->top_k > 0 && !ids))
         return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
-    const size_t need = hga::decode_workspace_bytes(cfg->n_q_heads, n_q, cfg->top_k,
-                                                    cfg->sink_chunks);
+    const size_t need = hga::decode_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, p0, n_q,
+                                                    cfg->top_k, cfg->sink_chunks);
     if (!workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < need)
         return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);

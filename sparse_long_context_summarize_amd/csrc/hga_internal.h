@@ -153,14 +153,18 @@ hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const u
                                    int32_t sink, float scale, int32_t *ids, float *scores,
                                    uint16_t *O, float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
-// Routed decode (decode.hip): the partials of decode_splits(k, sink) split
-// workgroups per (token, kv head) live in a workspace of
-// decode_workspace_bytes.
+// Routed decode (decode.hip). One workspace of decode_workspace_bytes serves
+// the router (the keys of up to decode_key_capacity candidates per token and
+// kv head) and then the attention (the partials of decode_splits(k, sink)
+// split workgroups per token and kv head).
 int decode_splits(int32_t k, int32_t sink);
-size_t decode_workspace_bytes(int64_t Hq, int64_t n_q, int32_t k, int32_t sink);
+int64_t decode_key_capacity(int64_t p0, int64_t n_q, int32_t sink);
+size_t decode_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t p0, int64_t n_q, int32_t k,
+                              int32_t sink);
 hipError_t launch_route_decode(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                                int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                               int32_t sink, int32_t *ids, float *scores, hipStream_t stream);
+                               int32_t sink, int32_t *ids, float *scores, void *workspace,
+                               hipStream_t stream);
 hipError_t launch_attend_decode(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                 int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                 int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,

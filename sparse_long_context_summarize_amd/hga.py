@@ -82,8 +82,9 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
-    L.hga_route_decode.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp]
-    L.hga_decode_workspace_bytes.argtypes = [_cfgp, _i64]
+    L.hga_route_decode.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+                                   ctypes.c_size_t, _vp]
+    L.hga_decode_workspace_bytes.argtypes = [_cfgp, _i64, _i64]
     L.hga_decode_workspace_bytes.restype = ctypes.c_size_t
     L.hga_attend_decode.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
@@ -248,20 +249,25 @@ def _m_attend_bwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, d
             ws_bytes, _stream(stream))
 
 
+def _workspace(workspace):
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def _m_route_decode(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids,
-                    scores=None, stream=None):
+                    workspace, scores=None, stream=None):
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
             _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
-            _stream(stream))
+            *_workspace(workspace), _stream(stream))
 
 
 def _m_attend_decode(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, workspace, stream=None):
     if K.shape != V.shape:
         raise ValueError("K and V shapes differ")
-    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
-            or not workspace.is_contiguous():
-        raise ValueError("workspace must be contiguous GPU memory")
+    _workspace(workspace)
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
             _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
@@ -367,15 +373,16 @@ def hga_attend_bwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: 
 
 
 def hga_route_decode(cfg: hga_config, Q: torch.Tensor, p0: int, summaries: torch.Tensor,
-                     n_chunks_valid: int, ids: torch.Tensor, scores: torch.Tensor | None = None,
-                     stream=None) -> None:
+                     n_chunks_valid: int, ids: torch.Tensor, workspace: torch.Tensor,
+                     scores: torch.Tensor | None = None, stream=None) -> None:
     """Routing of a decode step, one token at a time (ids [Hkv][n_q][k])."""
     _check("hga_route_decode", lib().hga_route_decode(
-        *_m_route_decode(cfg, Q, p0, summaries, n_chunks_valid, ids, scores, stream)))
+        *_m_route_decode(cfg, Q, p0, summaries, n_chunks_valid, ids, workspace, scores,
+                         stream)))
 
 
-def hga_decode_workspace_bytes(cfg: hga_config, n_q: int) -> int:
-    return int(lib().hga_decode_workspace_bytes(ctypes.byref(cfg), n_q))
+def hga_decode_workspace_bytes(cfg: hga_config, p0: int, n_q: int) -> int:
+    return int(lib().hga_decode_workspace_bytes(ctypes.byref(cfg), p0, n_q))
 
 
 def hga_attend_decode(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

@@ -203,3 +203,39 @@ def test_route_attend_checks():
     cfg0 = _cfg(top_k=0)
     assert f(ctypes.byref(cfg0), FAKE, FAKE, FAKE, 16384, 14336, 0, None, 0, 0, None, None,
              FAKE, FAKE, None) == hga.HGA_OK
+
+
+def test_decode_checks():
+    L = hga.lib()
+    cfg = _cfg(top_k=32)
+    # router keys: one per candidate (chunks before the last token's open
+    # chunk) per token and kv head; attention partials: 130 floats per split
+    # (two routed units a split) per token and query head; one size serves both
+    p0, n_q = 131071, 1
+    keys = n_q * 8 * (p0 // 64) * 4
+    parts = n_q * 32 * ((32 + 1 + 1) // 2) * 130 * 4
+    assert hga.hga_decode_workspace_bytes(cfg, p0, n_q) == max(keys, parts)
+    assert hga.hga_decode_workspace_bytes(cfg, 100, 1) == parts
+    assert hga.hga_decode_workspace_bytes(_cfg(top_k=32, sink_chunks=4), 64 * 10, 1) == \
+        1 * 32 * ((4 + 32 + 1 + 1) // 2) * 130 * 4
+    assert hga.hga_decode_workspace_bytes(cfg, -1, 1) == 0
+    assert hga.hga_decode_workspace_bytes(_cfg(head_dim=64), p0, 1) == 0
+    need = hga.hga_decode_workspace_bytes(cfg, p0, n_q)
+    n_closed = p0 // 64
+
+    def route(ws, ws_bytes, n_valid=n_closed, n_cap=n_closed):
+        return L.hga_route_decode(ctypes.byref(cfg), FAKE, p0, n_q, FAKE, n_cap, n_valid,
+                                  FAKE, None, ws, ws_bytes, None)
+
+    assert route(FAKE, need - 1) == hga.HGA_ERR_CAPACITY
+    assert "workspace" in hga.hga_last_error()
+    assert route(None, need) == hga.HGA_ERR_INVALID_ARG
+    assert route(FAKE, need, n_valid=n_closed - 1) == hga.HGA_ERR_CAPACITY
+    assert route(FAKE, need, n_valid=n_closed + 1) == hga.HGA_ERR_CAPACITY   # above the cap
+
+    def attend(ws_bytes, T=p0 + n_q):
+        return L.hga_attend_decode(ctypes.byref(cfg), FAKE, FAKE, FAKE, T, p0, n_q, FAKE,
+                                   FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert attend(need - 1) == hga.HGA_ERR_CAPACITY
+    assert attend(need, T=p0) == hga.HGA_ERR_INVALID_ARG

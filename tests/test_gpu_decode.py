@@ -41,14 +41,16 @@ def decode(x, p0, n_q, k, s=0, ids_override=None):
     hga.hga_summarize(cfg, K, 0, n_closed * C, S)
     ids = torch.full((Hkv, n_q, k), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((Hkv, n_q, k), float("nan"), device="cuda")
-    hga.hga_route_decode(cfg, Qd, p0, S, n_closed, ids, sc)
+    ws = torch.full((hga.hga_decode_workspace_bytes(cfg, p0, n_q),), 255, dtype=torch.uint8,
+                    device="cuda")
+    hga.hga_route_decode(cfg, Qd, p0, S, n_closed, ids, ws, sc)
     if ids_override is not None:
         ids = torch.from_numpy(np.ascontiguousarray(ids_override, dtype=np.int32)).cuda()
         cfg = hga.make_config(Hq, Hkv, ids.shape[2], sink_chunks=s)
+        ws = torch.full((hga.hga_decode_workspace_bytes(cfg, p0, n_q),), 255,
+                        dtype=torch.uint8, device="cuda")
     O = torch.full((Hq, n_q, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((Hq, n_q), float("nan"), device="cuda")
-    ws = torch.full((hga.hga_decode_workspace_bytes(cfg, n_q),), 255, dtype=torch.uint8,
-                    device="cuda")
     hga.hga_attend_decode(cfg, Qd, K, V, p0, ids, O, lse, ws)
     torch.cuda.synchronize()
     return dict(ids=ids.cpu().numpy(), scores=from_dev(sc), O=from_dev(O), lse=from_dev(lse),
@@ -104,6 +106,14 @@ def test_more_than_2048_candidates():
     x = inputs.small_random(610, 4, 1, 128, T, 2, bf16=True)
     res = decode(x, p0, 2, 40)
     check(x, p0, 2, 40, 0, res, "2200 candidates")
+
+
+def test_two_stage_selection_with_many_candidates():
+    """5000 candidates: eight shares of 625 selected apart, then merged."""
+    T, p0 = 64 * 5001, 64 * 5000 + 40
+    x = inputs.small_random(613, 2, 1, 128, T, 3, bf16=True)
+    res = decode(x, p0, 3, 100, s=1)
+    check(x, p0, 3, 100, 1, res, "5000 candidates, k=100")
 
 
 def test_largest_budget_and_sink():
