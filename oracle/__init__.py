@@ -49,17 +49,19 @@ def _load():
     lib.oracle_get_threads.restype = ctypes.c_int
     lib.oracle_summarize.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _f64p, _i64]
     lib.oracle_route.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
-                                 _f64p, _i64, _i64, _i32p, ctypes.c_void_p, _i64]
+                                 _f64p, _i64, _i64, _i32p, ctypes.c_void_p, _i64,
+                                 _i64, ctypes.c_void_p, _i64]
     lib.oracle_route_groups.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                         _i64, _f64p, _i64, _i32p, _i64, _i64, _i32p,
                                         ctypes.c_void_p, _i64]
     lib.oracle_attend_fwd.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _i32p, _i64,
-                                      ctypes.c_double, ctypes.c_void_p, _f64p, _f64p, _i64]
+                                      ctypes.c_double, ctypes.c_void_p, _f64p, _f64p, _i64,
+                                      _i64]
     lib.oracle_attend_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _i64, _i32p, _i64,
                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
-                                      _f64p, _f64p, _f64p, _i64]
+                                      _f64p, _f64p, _f64p, _i64, _i64]
     lib.oracle_attend_decode.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
                                          _i64, _i64, _i64, _i32p, _i64, ctypes.c_double,
                                          _i64, _f64p, _f64p]
@@ -104,12 +106,17 @@ def summarize(K, C: int, c_begin: int, c_end: int, out=None, n_cap: int | None =
 
 
 def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_scores=False,
-          sink: int = 0):
+          sink: int = 0, per_q_head: bool = False, prev_block: bool = False, Q_prev=None):
     """Per (kv head, block) top-k chunk ids, ascending, -1 padded. Candidates
     are the closed chunks before the block that lie past the first ``sink``
     tokens (the sink window, attended by every block; a multiple of C).
 
-    Returns ids [Hkv][n_blocks][k] int32 (and sigma [Hkv][n_blocks][n_cap]
+    per_q_head: one routing unit per query head (ids [Hq][n_blocks][k]).
+    prev_block: strictly causal routing -- block b scores with the queries of
+    the block before it; Q_prev [Hq][Bq][D] holds the Bq queries before p0
+    (None only when p0 == 0).
+
+    Returns ids [units][n_blocks][k] int32 (and sigma [units][n_blocks][n_cap]
     float64, NaN for ineligible chunks, if want_scores)."""
     Q = _f32(Q)
     Hq, n_q, D = Q.shape
@@ -117,11 +124,20 @@ def route(Q, S, p0: int, k: int, Hkv: int, C: int = 64, Bq: int = 64, want_score
     assert S.shape[0] == Hkv and S.shape[2] == D
     n_cap = S.shape[1]
     n_blocks = n_q // Bq
-    ids = np.empty((Hkv, n_blocks, k), dtype=np.int32)
-    sig = np.empty((Hkv, n_blocks, n_cap)) if want_scores else None
+    units = Hq if per_q_head else Hkv
+    ids = np.empty((units, n_blocks, k), dtype=np.int32)
+    sig = np.empty((units, n_blocks, n_cap)) if want_scores else None
     assert sink % C == 0 and sink >= 0
+    qp = None
+    if prev_block and Q_prev is not None:
+        qp = _f32(Q_prev)
+        assert qp.shape == (Hq, Bq, D)
+    assert not prev_block or qp is not None or p0 == 0
     _load().oracle_route(Q, Hq, Hkv, n_q, D, p0, C, Bq, S, n_cap, k, ids,
-                         sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None, sink)
+                         sig.ctypes.data_as(ctypes.c_void_p) if want_scores else None, sink,
+                         int(per_q_head),
+                         qp.ctypes.data_as(ctypes.c_void_p) if qp is not None else None,
+                         int(prev_block))
     return (ids, sig) if want_scores else ids
 
 
@@ -153,10 +169,11 @@ def route_groups(Q, SG, p0: int, chunk_ids, m: int, Hkv: int, C: int = 64, Bq: i
 
 
 def attend_fwd(Q, K, V, ids, p0: int, C: int = 64, Bq: int = 64, scale: float | None = None,
-               unit_mask=None, sink: int = 0):
+               unit_mask=None, sink: int = 0, per_q_head: bool = False):
     """Exact attention over the first ``sink`` tokens (the sink window; a
     multiple of C), the routed units and the causal local block. ids count
-    units of C tokens: chunks (C = 64) or groups (C = 8, with Bq = 64).
+    units of C tokens: chunks (C = 64) or groups (C = 8, with Bq = 64); one
+    row per (kv head, block), or per (query head, block) with per_q_head.
 
     Returns (O [Hq][n_q][D], lse [Hq][n_q]) float64; rows of units excluded by
     ``unit_mask`` ([Hq][n_blocks]) are NaN."""
@@ -171,16 +188,18 @@ def attend_fwd(Q, K, V, ids, p0: int, C: int = 64, Bq: int = 64, scale: float | 
     lse = np.full((Hq, n_q), np.nan)
     m, mp = _mask_ptr(unit_mask)
     assert sink % C == 0 and sink >= 0
+    assert ids.shape[:2] == ((Hq if per_q_head else Hkv), n_q // Bq)
     _load().oracle_attend_fwd(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k,
-                              float(scale), mp, O, lse, sink)
+                              float(scale), mp, O, lse, sink, int(per_q_head))
     return O, lse
 
 
 def attend_bwd(Q, K, V, dO, ids, p0: int, C: int = 64, Bq: int = 64,
-               scale: float | None = None, dq_mask=None, dkv_mask=None, sink: int = 0):
+               scale: float | None = None, dq_mask=None, dkv_mask=None, sink: int = 0,
+               per_q_head: bool = False):
     """Gradients of sum(O * dO): dQ [Hq][n_q][D], and dK, dV [Hkv][n_q][D] for
     the active keys p0 .. p0+n_q-1 only (history detached); the attended set
-    as in attend_fwd, sink window included."""
+    as in attend_fwd, sink window and id-row granularity included."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
     Hq, n_q, D = Q.shape
     Hkv, T, _ = K.shape
@@ -194,8 +213,9 @@ def attend_bwd(Q, K, V, dO, ids, p0: int, C: int = 64, Bq: int = 64,
     m1, p1 = _mask_ptr(dq_mask)
     m2, p2 = _mask_ptr(dkv_mask)
     assert sink % C == 0 and sink >= 0
+    assert ids.shape[:2] == ((Hq if per_q_head else Hkv), n_q // Bq)
     _load().oracle_attend_bwd(Q, K, V, dO, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k,
-                              float(scale), p1, p2, dQ, dK, dV, sink)
+                              float(scale), p1, p2, dQ, dK, dV, sink, int(per_q_head))
     return dQ, dK, dV
 
 

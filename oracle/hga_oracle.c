@@ -107,6 +107,20 @@ void oracle_summarize(const float *K, int64_t Hkv, int64_t T, int64_t D,
  *     write them in ascending id order, pad with -1.
  * ids is [Hkv][n_blocks][k]. If sigma_out is not NULL it receives
  * sigma_c for every c < n_cap as [Hkv][n_blocks][n_cap] (NaN for c not in E).
+ *
+ * Two routing variants (the pages fix neither the head granularity of the
+ * query block's score nor a causal form of it; both are readings of this
+ * repository, next to the default above):
+ *   per_q_head != 0  one routing unit per query head h instead of per kv
+ *                    head: qbar is the mean over the Bq queries of head h
+ *                    alone, scored against the summaries of its kv head
+ *                    h / G; ids (and sigma_out) are then [Hq][n_blocks][...].
+ *   prev_block != 0  strictly causal routing: block b scores with the queries
+ *                    of the block before it (positions P - Bq .. P - 1): rows
+ *                    (b-1)*Bq .. b*Bq - 1 of Q for b >= 1, and the Bq rows of
+ *                    Q_prev ([Hq][Bq][D], the queries just before p0) for
+ *                    b = 0; Q_prev may be NULL when p0 = 0 (block 0 then has
+ *                    no candidates). The candidates are unchanged.
  */
 typedef struct { double sigma; int64_t c; } scored_chunk;
 
@@ -128,26 +142,44 @@ static int by_id_asc(const void *pa, const void *pb)
 void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
                   int64_t D, int64_t p0, int64_t C, int64_t Bq,
                   const double *S, int64_t n_cap, int64_t k,
-                  int32_t *ids, double *sigma_out, int64_t sink)
+                  int32_t *ids, double *sigma_out, int64_t sink,
+                  int64_t per_q_head, const float *Q_prev, int64_t prev_block)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
+    int64_t n_units = per_q_head ? Hq : Hkv;        /* routing units per block */
+    int64_t heads = per_q_head ? 1 : G;             /* query heads per unit */
 #pragma omp parallel for schedule(dynamic)
-    for (int64_t u = 0; u < Hkv * n_blocks; ++u) {
+    for (int64_t u = 0; u < n_units * n_blocks; ++u) {
         int64_t g = u / n_blocks, b = u % n_blocks;
+        int64_t kv = per_q_head ? g / G : g;        /* summaries of this kv head */
         int64_t P = p0 + b * Bq;
         int64_t c_hi = P / C;               /* chunks c with (c+1)*C <= P */
         if (c_hi > n_cap) c_hi = n_cap;
         int64_t c_lo = (sink + C - 1) / C;  /* first chunk past the sink */
         int64_t nE = c_hi > c_lo ? c_hi - c_lo : 0;
 
+        /* the Bq query rows this block scores with: its own, or the block's
+           before it (from Q_prev for the first block) */
+        const float *Qr = Q;
+        int64_t r_n = n_q, r_first = b * Bq;
+        if (prev_block) {
+            if (b > 0) {
+                r_first = (b - 1) * Bq;
+            } else {
+                Qr = Q_prev;
+                r_n = Bq;
+                r_first = 0;
+            }
+        }
         double *qbar = (double *)malloc((size_t)D * sizeof(double));
         for (int64_t d = 0; d < D; ++d) {
             double sum = 0.0;
-            for (int64_t h = g * G; h < g * G + G; ++h)
-                for (int64_t i = b * Bq; i < b * Bq + Bq; ++i)
-                    sum += (double)Q[(h * n_q + i) * D + d];
-            qbar[d] = sum / (double)(G * Bq);
+            if (Qr)
+                for (int64_t h = g * heads; h < g * heads + heads; ++h)
+                    for (int64_t i = r_first; i < r_first + Bq; ++i)
+                        sum += (double)Qr[(h * r_n + i) * D + d];
+            qbar[d] = sum / (double)(heads * Bq);
         }
 
         scored_chunk *cand = (scored_chunk *)malloc((size_t)(nE > 0 ? nE : 1) * sizeof(scored_chunk));
@@ -155,7 +187,7 @@ void oracle_route(const float *Q, int64_t Hq, int64_t Hkv, int64_t n_q,
             int64_t c = c_lo + e;
             double sigma = 0.0;
             for (int64_t d = 0; d < D; ++d)
-                sigma += qbar[d] * S[(g * n_cap + c) * D + d];
+                sigma += qbar[d] * S[(kv * n_cap + c) * D + d];
             cand[e].sigma = sigma;
             cand[e].c = c;
         }
@@ -322,12 +354,16 @@ static double dot_fd(const float *a, const float *b, int64_t D)
  *     lse[h][i] = m + ln l
  * unit_mask ([Hq][n_blocks], may be NULL) limits the work to chosen
  * (head, block) units; other rows of O/lse are left untouched.
+ * per_q_head != 0: ids is [Hq][n_blocks][k] and query head h attends the
+ * chunks of its own row ids[h][b] (per-query-head routing); otherwise row
+ * ids[h / G][b] serves all G heads of a kv head.
  */
 void oracle_attend_fwd(const float *Q, const float *K, const float *V,
                        int64_t Hq, int64_t Hkv, int64_t D, int64_t T,
                        int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
                        const int32_t *ids, int64_t k, double scale,
-                       const uint8_t *unit_mask, double *O, double *lse, int64_t sink)
+                       const uint8_t *unit_mask, double *O, double *lse, int64_t sink,
+                       int64_t per_q_head)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -344,7 +380,7 @@ void oracle_attend_fwd(const float *Q, const float *K, const float *V,
             int64_t b = i / Bq, g = h / G;
             if (unit_mask && !unit_mask[h * n_blocks + b]) continue;
             int64_t P = p0 + b * Bq, p = p0 + i;
-            const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
+            const int32_t *ids_gb = ids + ((per_q_head ? h : g) * n_blocks + b) * k;
             int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks, sink);
             const float *q = Q + (h * n_q + i) * D;
 
@@ -381,6 +417,7 @@ void oracle_attend_fwd(const float *Q, const float *K, const float *V,
  * dQ is [Hq][n_q][D]; dK, dV are [Hkv][n_q][D] indexed by j - p0.
  * dq_mask ([Hq][n_blocks]) and dkv_mask ([Hkv][n_q/C]) may be NULL; masked-out
  * rows are left untouched. lse and O are recomputed here from Q, K, V.
+ * per_q_head: the id rows as in oracle_attend_fwd.
  */
 void oracle_attend_bwd(const float *Q, const float *K, const float *V,
                        const float *dO,
@@ -388,7 +425,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
                        int64_t p0, int64_t n_q, int64_t C, int64_t Bq,
                        const int32_t *ids, int64_t k, double scale,
                        const uint8_t *dq_mask, const uint8_t *dkv_mask,
-                       double *dQ, double *dK, double *dV, int64_t sink)
+                       double *dQ, double *dK, double *dV, int64_t sink, int64_t per_q_head)
 {
     int64_t G = Hq / Hkv;
     int64_t n_blocks = n_q / Bq;
@@ -399,7 +436,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
 
     /* pass 1: lse, O and Delta for every active query */
     oracle_attend_fwd(Q, K, V, Hq, Hkv, D, T, p0, n_q, C, Bq, ids, k, scale,
-                      NULL, Obuf, lse, sink);
+                      NULL, Obuf, lse, sink, per_q_head);
 #pragma omp parallel for schedule(static)
     for (int64_t row = 0; row < Hq * n_q; ++row) {
         double s = 0.0;
@@ -420,7 +457,7 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
             int64_t b = i / Bq, g = h / G;
             if (dq_mask && !dq_mask[h * n_blocks + b]) continue;
             int64_t P = p0 + b * Bq, p = p0 + i;
-            const int32_t *ids_gb = ids + (g * n_blocks + b) * k;
+            const int32_t *ids_gb = ids + ((per_q_head ? h : g) * n_blocks + b) * k;
             int64_t n = attended_positions(ids_gb, k, C, P, p, pos, seen, n_chunks, sink);
             const float *q = Q + row * D;
             const float *go = dO + row * D;
@@ -452,7 +489,8 @@ void oracle_attend_bwd(const float *Q, const float *K, const float *V,
             for (int64_t h = g * G; h < g * G + G; ++h) {
                 for (int64_t i = 0; i < n_q; ++i) {
                     int64_t b = i / Bq, P = p0 + b * Bq, p = p0 + i;
-                    if (!is_attended(ids + (g * n_blocks + b) * k, k, C, P, p, j, sink))
+                    const int64_t row_u = per_q_head ? h : g;
+                    if (!is_attended(ids + (row_u * n_blocks + b) * k, k, C, P, p, j, sink))
                         continue;
                     int64_t row = h * n_q + i;
                     const float *q = Q + row * D;

@@ -786,3 +786,212 @@ def test_decode_routing_finds_a_planted_chunk_per_token():
     assert ids[0, 2, 0] == 5
     ids_early = oracle.route_decode(Q, S, 44, 1, Hkv, C)       # open chunk 5: not a candidate
     assert ids_early[0, 2, 0] != 5
+
+
+# ------------------------------------------------------ routing variants
+# Per-query-head routing (one routing unit per query head rather than per kv
+# head) and strictly causal routing (block b scores with the queries of the
+# block before it). The pages define neither; these pins fix the readings.
+
+def _mask_per_head(ids, Hq, n_q, p0, T, C, Bq, sink=0):
+    """Attend-mask [Hq][n_q][T] with head h reading its own id row ids[h]."""
+    M = np.zeros((Hq, n_q, T), dtype=bool)
+    for h in range(Hq):
+        for i in range(n_q):
+            b = i // Bq
+            P = p0 + b * Bq
+            M[h, i, :min(sink, P)] = True
+            for c in ids[h, b]:
+                if 0 <= c < P // C:
+                    M[h, i, c * C:(c + 1) * C] = True
+            M[h, i, P:p0 + i + 1] = True
+    return M
+
+
+def _brute_route(Qr_blocks, S_heads, P_list, k, C, sink=0):
+    """Exhaustive top-k: Qr_blocks[u][b] are the query rows unit u scores
+    with in block b, S_heads[u] its summaries [n_cap][D]."""
+    U, nb = len(Qr_blocks), len(P_list)
+    ids = np.full((U, nb, k), -1, np.int32)
+    for u in range(U):
+        for b, P in enumerate(P_list):
+            qbar = np.asarray(Qr_blocks[u][b], np.float64).mean(axis=0)
+            cand = np.arange(sink // C, P // C)
+            if cand.size == 0:
+                continue
+            sig = S_heads[u][cand] @ qbar
+            order = np.lexsort((cand, -sig))[:k]
+            ids[u, b, :order.size] = np.sort(cand[order])
+    return ids
+
+
+def test_per_head_route_score_equals_mean_pairwise_logit():
+    x = _tiny(seed=90, Hq=4, Hkv=2, D=16, T=256, n_q=64, C=8)
+    C = Bq = 8
+    p0, G = 256 - 64, 2
+    S = oracle.summarize(x["K"], C, 0, 256 // C)
+    ids, sig = oracle.route(x["Q"], S, p0, 5, 2, C, Bq, want_scores=True, per_q_head=True)
+    assert ids.shape == (4, 8, 5)
+    Q = x["Q"].astype(np.float64)
+    K = x["K"].astype(np.float64)
+    for h in range(4):
+        for b in range(64 // Bq):
+            P = p0 + b * Bq
+            q = Q[h, b * Bq:(b + 1) * Bq]
+            for c in range(256 // C):
+                if c < P // C:
+                    pair = (q @ K[h // G, c * C:(c + 1) * C].T).mean()
+                    assert abs(sig[h, b, c] - pair) <= 1e-12 * max(1.0, abs(pair))
+                else:
+                    assert np.isnan(sig[h, b, c])
+
+
+def test_per_head_scores_average_to_the_kv_head_score():
+    x = _tiny(seed=91, Hq=8, Hkv=2, D=16, T=512, n_q=128, C=8)
+    C, Bq, p0 = 8, 16, 512 - 128
+    S = oracle.summarize(x["K"], C, 0, 512 // C)
+    _, sh = oracle.route(x["Q"], S, p0, 4, 2, C, Bq, want_scores=True, per_q_head=True)
+    _, sg = oracle.route(x["Q"], S, p0, 4, 2, C, Bq, want_scores=True)
+    avg = sh.reshape(2, 4, *sh.shape[1:]).mean(axis=1)
+    ok = ~np.isnan(sg)
+    assert np.array_equal(ok, ~np.isnan(avg))
+    np.testing.assert_allclose(avg[ok], sg[ok], rtol=1e-12, atol=1e-14)
+    # one query head per kv head: the two granularities coincide
+    x1 = _tiny(seed=92, Hq=2, Hkv=2, D=16, T=512, n_q=128, C=8)
+    S1 = oracle.summarize(x1["K"], C, 0, 512 // C)
+    a, sa = oracle.route(x1["Q"], S1, p0, 6, 2, C, Bq, want_scores=True, per_q_head=True)
+    b, sb = oracle.route(x1["Q"], S1, p0, 6, 2, C, Bq, want_scores=True)
+    assert np.array_equal(a, b)
+    assert np.array_equal(np.isnan(sa), np.isnan(sb))
+
+
+@pytest.mark.parametrize("sink", [0, 16])
+def test_per_head_selection_is_the_exhaustive_top_k(sink):
+    x = _tiny(seed=93, Hq=4, Hkv=1, D=16, T=512, n_q=128, C=8)
+    C, Bq, p0, k = 8, 16, 512 - 128, 7
+    S = oracle.summarize(x["K"], C, 0, 512 // C)
+    ids = oracle.route(x["Q"], S, p0, k, 1, C, Bq, per_q_head=True, sink=sink)
+    Q = x["Q"].astype(np.float64)
+    rows = [[Q[h, b * Bq:(b + 1) * Bq] for b in range(128 // Bq)] for h in range(4)]
+    want = _brute_route(rows, [S[0]] * 4, [p0 + b * Bq for b in range(128 // Bq)], k, C,
+                        sink)
+    assert np.array_equal(ids, want)
+
+
+def test_per_head_routing_serves_each_head_its_own_chunk():
+    # head 0's queries point along e0, head 1's along e1; chunk 2 holds e0 keys,
+    # chunk 5 holds e1 keys. Per query head, each head takes its own chunk; per
+    # kv head both heads share the stronger of the two.
+    D, C = 4, 8
+    T = 8 * C
+    K = np.zeros((1, T, D), np.float32)
+    K[0, 2 * C:3 * C, 0] = 1.0
+    K[0, 5 * C:6 * C, 1] = 2.0
+    Q = np.zeros((2, C, D), np.float32)
+    Q[0, :, 0] = 1.0
+    Q[1, :, 1] = 1.0
+    S = oracle.summarize(K, C, 0, 8)
+    per_head = oracle.route(Q, S, 7 * C, 1, 1, C, C, per_q_head=True)
+    assert per_head[:, 0, 0].tolist() == [2, 5]
+    assert oracle.route(Q, S, 7 * C, 1, 1, C, C)[0, 0, 0] == 5
+
+
+@pytest.mark.parametrize("sink", [0, 16])
+def test_per_head_attention_matches_masked_sdpa(sink):
+    Hq, Hkv, D, T, n_q, C, Bq = 4, 2, 16, 256, 64, 8, 16
+    x = _tiny(94, Hq, Hkv, D, T, n_q, C)
+    p0 = T - n_q
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(x["Q"], S, p0, 4, Hkv, C, Bq, per_q_head=True, sink=sink)
+    assert not np.array_equal(ids[0], ids[1])           # the heads do differ
+    O, lse = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0, C, Bq, sink=sink,
+                               per_q_head=True)
+    M = _mask_per_head(ids, Hq, n_q, p0, T, C, Bq, sink)
+    O_ref, lse_ref = _sdpa_masked(x["Q"], x["K"], x["V"], M, 1 / math.sqrt(D))
+    np.testing.assert_allclose(O, O_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-10, atol=1e-12)
+    # rows repeated over the heads of a kv head give the shared-row result
+    idk = oracle.route(x["Q"], S, p0, 4, Hkv, C, Bq, sink=sink)
+    O1, l1 = oracle.attend_fwd(x["Q"], x["K"], x["V"], np.repeat(idk, Hq // Hkv, axis=0), p0,
+                               C, Bq, sink=sink, per_q_head=True)
+    O2, l2 = oracle.attend_fwd(x["Q"], x["K"], x["V"], idk, p0, C, Bq, sink=sink)
+    assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+def test_per_head_backward_matches_autograd():
+    Hq, Hkv, D, T, n_q, C, Bq = 4, 2, 16, 256, 64, 8, 16
+    x = _tiny(95, Hq, Hkv, D, T, n_q, C, with_dO=True)
+    p0, s = T - n_q, 8
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(x["Q"], S, p0, 3, Hkv, C, Bq, per_q_head=True, sink=s)
+    dQ, dK, dV = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], ids, p0, C, Bq, sink=s,
+                                   per_q_head=True)
+    M = _mask_per_head(ids, Hq, n_q, p0, T, C, Bq, s)
+    G = Hq // Hkv
+    q = torch.tensor(x["Q"], dtype=torch.float64, requires_grad=True)
+    kk = torch.tensor(x["K"], dtype=torch.float64, requires_grad=True)
+    vv = torch.tensor(x["V"], dtype=torch.float64, requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q, kk.repeat_interleave(G, 0), vv.repeat_interleave(G, 0),
+        attn_mask=torch.from_numpy(M), scale=1 / math.sqrt(D))
+    (out * torch.from_numpy(x["dO"].astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(dQ, q.grad.numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dK, kk.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(dV, vv.grad.numpy()[:, p0:], rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("per_q_head,sink", [(False, 0), (True, 0), (False, 16), (True, 8)])
+def test_prev_block_route_is_the_top_k_of_the_previous_queries(per_q_head, sink):
+    Hq, Hkv, D, T, n_q, C, Bq = 4, 2, 16, 512, 128, 8, 16
+    x = _tiny(96, Hq, Hkv, D, T, n_q + Bq, C)
+    Q_prev, Q = x["Q"][:, :Bq], x["Q"][:, Bq:]
+    p0, k = T - n_q, 5
+    S = oracle.summarize(x["K"], C, 0, T // C)
+    ids = oracle.route(Q, S, p0, k, Hkv, C, Bq, per_q_head=per_q_head, prev_block=True,
+                       Q_prev=Q_prev, sink=sink)
+    G = Hq // Hkv
+    allq = x["Q"].astype(np.float64)          # rows: the Bq queries before p0, then Q
+    nb = n_q // Bq
+    heads = [[h] for h in range(Hq)] if per_q_head else \
+        [list(range(g * G, g * G + G)) for g in range(Hkv)]
+    rows = [[allq[hs, b * Bq:(b + 1) * Bq].reshape(-1, D) for b in range(nb)] for hs in heads]
+    S_u = [S[hs[0] // G] for hs in heads]
+    want = _brute_route(rows, S_u, [p0 + b * Bq for b in range(nb)], k, C, sink)
+    assert np.array_equal(ids, want)
+
+
+def test_prev_block_route_never_sees_its_own_block():
+    # A block's own queries (and any later ones) leave its ids unchanged under
+    # strictly causal routing; the default routing does see them.
+    D, C = 4, 8
+    T = 8 * C
+    K = np.zeros((1, T, D), np.float32)
+    K[0, 0:C, 0] = 1.0
+    K[0, C:2 * C, 1] = 1.0
+    Q = np.zeros((1, 3 * C, D), np.float32)
+    Q[0, :, 0] = 1.0
+    Q_prev = np.zeros((1, C, D), np.float32)
+    Q_prev[0, :, 0] = 1.0
+    S = oracle.summarize(K, C, 0, 8)
+    p0 = 4 * C
+    base = oracle.route(Q, S, p0, 1, 1, C, C, prev_block=True, Q_prev=Q_prev)
+    assert base[0, :, 0].tolist() == [0, 0, 0]
+    Q2 = Q.copy()
+    Q2[0, C:, 1] = 100.0                     # blocks 1 and 2 now point at chunk 1
+    own = oracle.route(Q2, S, p0, 1, 1, C, C)
+    assert own[0, :, 0].tolist() == [0, 1, 1]
+    prev = oracle.route(Q2, S, p0, 1, 1, C, C, prev_block=True, Q_prev=Q_prev)
+    assert prev[0, :, 0].tolist() == [0, 0, 1]   # only block 2 sees block 1's change
+    Qp2 = Q_prev.copy()
+    Qp2[0, :, 1] = 100.0                     # the queries before p0 steer block 0 only
+    prev2 = oracle.route(Q, S, p0, 1, 1, C, C, prev_block=True, Q_prev=Qp2)
+    assert prev2[0, :, 0].tolist() == [1, 0, 0]
+
+
+def test_prev_block_route_at_sequence_start_needs_no_previous_queries():
+    x = _tiny(97, 2, 1, 16, 128, 128, 8)
+    S = oracle.summarize(x["K"], 8, 0, 16)
+    ids = oracle.route(x["Q"], S, 0, 3, 1, 8, 16, prev_block=True)
+    assert np.all(ids[0, 0] == -1)           # block 0 has no candidates
+    for b in range(1, 8):                    # later blocks: min(k, P/C) of them
+        assert (ids[0, b] >= 0).sum() == min(3, (16 * b) // 8)
