@@ -64,6 +64,7 @@ typedef struct hga_config {
     float softmax_scale;    /* <= 0 selects 1/sqrt(head_dim)                   */
     int32_t dtype;          /* HGA_BF16                                        */
     int32_t sink_chunks;    /* s: 0 .. HGA_MAX_SINK_CHUNKS; see below          */
+    int32_t route_heads;    /* HGA_ROUTE_PER_KV_HEAD (0) or _PER_Q_HEAD; below */
 } hga_config;
 
 /*
@@ -77,6 +78,27 @@ typedef struct hga_config {
  * method without a sink.
  */
 #define HGA_MAX_SINK_CHUNKS 64
+
+/*
+ * Routing granularity (technical summary 2.1 has the query block score the
+ * chunk summaries but does not say over which heads). A routing unit owns
+ * one id row per query block:
+ *   HGA_ROUTE_PER_KV_HEAD  a unit is a kv head g: the block's mean query is
+ *                          taken over the G query heads that share g, and all
+ *                          G heads attend the chunks of row ids[g][b]
+ *                          (U = Hkv units).
+ *   HGA_ROUTE_PER_Q_HEAD   a unit is a query head h: its own block mean,
+ *                          scored against the summaries of its kv head h/G,
+ *                          and head h attends the chunks of row ids[h][b]
+ *                          (U = Hq units; the G heads of a kv head no longer
+ *                          share the gathered chunks).
+ * hga_route, hga_route_causal, hga_attend_fwd, hga_route_attend_fwd and
+ * hga_attend_bwd take either; the group-level, decode and diagnostic entry
+ * points take HGA_ROUTE_PER_KV_HEAD only (else HGA_ERR_UNSUPPORTED). Any
+ * other value is HGA_ERR_INVALID_ARG.
+ */
+#define HGA_ROUTE_PER_KV_HEAD 0
+#define HGA_ROUTE_PER_Q_HEAD 1
 
 /*
  * hga_summarize -- append chunk summaries (technical summary 2.1, chunk
@@ -99,21 +121,22 @@ hga_status hga_summarize(const hga_config *cfg, const void *K, int64_t T_cap,
 /*
  * hga_route -- per query block top-k chunk ids (technical summary 2.1: the
  * current query block scores the resident summaries and keeps the most
- * relevant earlier chunks; the selection carries no gradient). For kv head g
- * and block b, first query position P = p0 + b*Bq:
- *     qbar    = mean of Q[h][i] over the G heads of group g and the Bq
- *               queries of block b (fp32)
+ * relevant earlier chunks; the selection carries no gradient). For routing
+ * unit u (kv head g = u, or query head u of kv head g = u/G; see
+ * cfg->route_heads) and block b, first query position P = p0 + b*Bq:
+ *     qbar    = mean of Q[h][i] over the query heads h of unit u (the G heads
+ *               of g, or head u alone) and the Bq queries of block b (fp32)
  *     score_c = qbar . summaries[g][c]     for every chunk s <= c < P/C (fp32;
  *               s = cfg->sink_chunks, see hga_config)
- *     ids[g][b][:] = the min(k, P/C - s) chunks of highest score, ties to
+ *     ids[u][b][:] = the min(k, P/C - s) chunks of highest score, ties to
  *               the lower chunk id, written in ascending id order, then -1.
  *   Q              device bf16 [Hq][n_q][D]
  *   summaries      device f32 [Hkv][n_chunk_cap][D]; rows 0 .. n_chunks_valid-1
  *                  must hold summaries. Needs (p0 + n_q - Bq)/C <= n_chunks_valid
  *                  <= n_chunk_cap, else HGA_ERR_CAPACITY. Only rows c < P/C are
  *                  read for block b.
- *   ids            device int32 [Hkv][n_q/Bq][k]
- *   scores_or_null device f32 [Hkv][n_q/Bq][k] or NULL: the fp32 score of each
+ *   ids            device int32 [U][n_q/Bq][k]  (U = Hkv, or Hq per query head)
+ *   scores_or_null device f32 [U][n_q/Bq][k] or NULL: the fp32 score of each
  *                  written id, -INFINITY beside a -1.
  */
 hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
@@ -122,11 +145,30 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
                      hipStream_t stream);
 
 /*
+ * hga_route_causal -- strictly causal routing. hga_route's block mean takes
+ * in the block's own later queries, so a query's chunk set depends on
+ * queries after it (the causal leakage inside a chunk that the pages name as
+ * a limitation; they define no fix). Here block b instead scores with the
+ * mean of the Bq queries just before it, positions P - Bq .. P - 1: the rows
+ * of block b - 1 of Q for b >= 1, and Q_prev for b = 0. Candidates, tie rule,
+ * output layout and errors are hga_route's; the attention entry points take
+ * these ids unchanged.
+ *   Q_prev   device bf16 [Hq][Bq][D]: the queries at positions p0 - Bq ..
+ *            p0 - 1 (the previous segment's last block); may be NULL when
+ *            p0 = 0 (block 0 then has no candidates), else HGA_ERR_INVALID_ARG
+ */
+hga_status hga_route_causal(const hga_config *cfg, const void *Q, const void *Q_prev,
+                            int64_t p0, int64_t n_q, const float *summaries,
+                            int64_t n_chunk_cap, int64_t n_chunks_valid, int32_t *ids,
+                            float *scores_or_null, hipStream_t stream);
+
+/*
  * hga_attend_fwd -- exact-token attention over the routed chunks and the
  * causal local block (technical summary 2.1: only the exact K/V of the
  * selected units enter attention; summaries never act as values). For query
- * i (position p = p0 + i, block b, head h, kv head g = h/G):
- *     A(i) = [0, min(sC, P))  U  union_{c in ids[g][b], s <= c < P/C} [cC, cC+C)
+ * i (position p = p0 + i, block b, head h, kv head g = h/G, routing unit u =
+ * g, or h with HGA_ROUTE_PER_Q_HEAD):
+ *     A(i) = [0, min(sC, P))  U  union_{c in ids[u][b], s <= c < P/C} [cC, cC+C)
  *            U  [P, p]                 (s = cfg->sink_chunks, the sink window)
  *     z_j  = scale * Q[h][i] . K[g][j]
  *     O[h][i]   = sum_{j in A(i)} softmax(z)_j V[g][j]      (bf16, RNE)
@@ -137,7 +179,7 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
  * once (rows as hga_route writes them, ascending and distinct, need no
  * de-duplication work).
  *   Q, O   device bf16 [Hq][n_q][D];   K, V device bf16 [Hkv][T_cap][D]
- *   ids    device int32 [Hkv][n_q/Bq][k];   lse device f32 [Hq][n_q]
+ *   ids    device int32 [U][n_q/Bq][k] (U as for hga_route); lse device f32 [Hq][n_q]
  *   p0     multiple of C; n_q multiple of Bq; p0 + n_q <= T_cap
  */
 hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
@@ -175,8 +217,9 @@ size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
  *     dQ_i = scale * sum_{j in A(i)} dS_ij K_j
  *     dK_j = scale * sum_{(h,i): j in A(i)} dS_ij Q_i     p0 <= j < p0+n_q
  *     dV_j =         sum_{(h,i): j in A(i)} P_ij dO_i     p0 <= j < p0+n_q
- * (sums over the G query heads that share kv head g; A(i) and the ids rule as
- * for hga_attend_fwd, a set per row). lse is the output of
+ * (sums over the G query heads that share kv head g, each head with its own
+ * A(i); A(i) and the ids rule as for hga_attend_fwd, a set per row, id rows
+ * per cfg->route_heads). lse is the output of
  * hga_attend_fwd for the same arguments. Delta is recomputed in fp32 from P
  * and dP rather than taken as dO . O, because the bf16 rounding of O would
  * reach dS undamped wherever attention concentrates on a few keys; O is

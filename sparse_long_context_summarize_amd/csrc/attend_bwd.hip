@@ -166,8 +166,9 @@ void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
-    int64_t n_q, int64_t Hkv, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids,
-    int k, int sink, float scale_log2, float scale, float *__restrict__ dQ)
+    int64_t n_q, int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0,
+    const int32_t *__restrict__ ids, int k, int sink, float scale_log2, float scale,
+    float *__restrict__ dQ)
 {
     constexpr int HW = G < 4 ? G : 4;
     constexpr int NHG = G / HW;
@@ -180,15 +181,17 @@ void bwd_dq_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
+    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
+    const int64_t rest0 = blockIdx.x / Hkv;
+    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id row
+    const int64_t rest = rest0 / kv_div;
     const int hg = (int)(rest % NHG);
     const int64_t b = rest / NHG;
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
     const int64_t local_chunk = P / kC;
-    const uint16_t *Kg = K + g * T_cap * kD;
-    const uint16_t *Vg = V + g * T_cap * kD;
+    const uint16_t *Kg = K + gkv * T_cap * kD;
+    const uint16_t *Vg = V + gkv * T_cap * kD;
 
     // the sink window's units, the routed units (past the sink, before P,
     // repeats dropped), then the local chunk
@@ -202,7 +205,7 @@ void bwd_dq_kernel(
             list_n = ns + n + 1;
         }
     }
-    // the dkdv kernel that follows counts finished workgroups per (kv head, chunk)
+    // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
     __syncthreads();
     const int n_units = list_n - 1;
@@ -412,8 +415,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, int64_t n_q,
-    int64_t Hkv, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k, int sink,
-    float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV,
+    int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k,
+    int sink, float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV,
     float *__restrict__ part, int *__restrict__ counters)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];
@@ -426,8 +429,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
+    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
+    const int64_t rest0 = blockIdx.x / Hkv;
+    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id rows
+    const int64_t rest = rest0 / kv_div;
     const int split = (int)(rest % kSplit);
     const int64_t a = rest / kSplit;             // active chunk = its own query block
     const int64_t n_blocks = n_q / kC;
@@ -510,8 +515,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     bf16x8 kb[8], vb[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        kb[ks] = *(const bf16x8 *)(K + (g * T_cap + key_row) * kD + 16 * ks + 8 * half);
-        vb[ks] = *(const bf16x8 *)(V + (g * T_cap + key_row) * kD + 16 * ks + 8 * half);
+        kb[ks] = *(const bf16x8 *)(K + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
+        vb[ks] = *(const bf16x8 *)(V + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
     }
 
     auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
@@ -724,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
     // Several workgroups share this chunk: store the partial, count, and let
     // the last one add the partials in workgroup order 0, 1, ... .
-    const int64_t part_stride = Hkv * n_q * kD;          // floats per (split, tensor)
+    const int64_t part_stride = Hkv * kv_div * n_q * kD;   // floats per (split, tensor)
     if (qh == 0) {
         float *pk = part + (int64_t)(2 * split) * part_stride + out_row * kD;
         float *pv = part + (int64_t)(2 * split + 1) * part_stride + out_row * kD;
@@ -768,9 +773,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
 }
 
+// Per-query-head routing: dK, dV of kv head g are the sums over its query
+// heads of each head's own contribution (dkdv ran per head into dKu, dVu
+// [Hq][n_q][D]); added in head order.
+__global__ __launch_bounds__(256) void sum_heads_kernel(
+    const float *__restrict__ dKu, const float *__restrict__ dVu, int64_t n_vec, int G,
+    int64_t per_head, float *__restrict__ dK, float *__restrict__ dV)
+{
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index in dK
+    if (v >= n_vec) return;
+    const int64_t g = v / per_head, r = v % per_head;
+    const f32x4 *sk = (const f32x4 *)dKu + g * G * per_head + r;
+    const f32x4 *sv = (const f32x4 *)dVu + g * G * per_head + r;
+    f32x4 ak = sk[0], av = sv[0];
+    for (int hh = 1; hh < G; ++hh) {
+        const f32x4 xk = sk[hh * per_head], xv = sv[hh * per_head];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { ak[e] += xk[e]; av[e] += xv[e]; }
+    }
+    ((f32x4 *)dK)[v] = ak;
+    ((f32x4 *)dV)[v] = av;
+}
+
+// G: query heads per routing unit (1 with per-query-head routing, where
+// kv_div = query heads per kv head and dK/dV are then the per-head buffers).
 template <int G, int kUnit>
 hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
-                        int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
+                        int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, int64_t n_q,
                         const int32_t *ids, int32_t k, int32_t sink, float scale, const float *lse,
                         const uint16_t *dO, float *dQ, float *dK, float *dV,
                         float *delta, int *counters, float *part, hipStream_t stream)
@@ -778,39 +807,45 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * NHG)), dim3(kDqThreads),
-                       0, stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, T_cap, p0, ids,
-                       k, (int)sink, scale_log2, scale, dQ);
+    hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>),
+                       dim3((unsigned)(n_blocks * Hkv * kv_div * NHG)), dim3(kDqThreads), 0,
+                       stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, kv_div, T_cap, p0,
+                       ids, k, (int)sink, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>), dim3((unsigned)(n_blocks * Hkv * kSplit)),
-                       dim3(kThreads), 0, stream, Q, K, V, dO, lse, delta, n_q, Hkv, T_cap, p0,
-                       ids, k, (int)sink, scale_log2, scale, dK, dV, part, counters);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>),
+                       dim3((unsigned)(n_blocks * Hkv * kv_div * kSplit)), dim3(kThreads), 0,
+                       stream, Q, K, V, dO, lse, delta, n_q, Hkv, kv_div, T_cap, p0, ids, k,
+                       (int)sink, scale_log2, scale, dK, dV, part, counters);
     return hipGetLastError();
 }
 
-// Workspace layout: Delta [Hq][n_q] f32 | counters [Hkv][n_q/C] int32 (padded
-// to 256 B) | partial sums [kSplit][dK, dV][Hkv][n_q][D] f32.
+// Workspace layout (U routing units: Hkv, or Hq with per-query-head routing):
+// Delta [Hq][n_q] f32 | counters [U][n_q/C] int32 | partial sums
+// [kSplit][dK, dV][U][n_q][D] f32 | per-query-head routing only: each head's
+// dK and dV, [2][Hq][n_q][D] f32. Every part starts on a 256-byte boundary.
 struct BwdWorkspace {
-    size_t delta_off, counter_off, part_off, total;
+    size_t delta_off, counter_off, part_off, head_off, total;
 };
 
-BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q)
+BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int64_t U = per_q_head ? Hq : Hkv;
     BwdWorkspace w;
     w.delta_off = 0;
     w.counter_off = up((size_t)(Hq * n_q) * sizeof(float));
-    w.part_off = w.counter_off + up((size_t)(Hkv * (n_q / kC)) * sizeof(int));
-    w.total = w.part_off + (size_t)kSplit * 2 * (size_t)(Hkv * n_q * kD) * sizeof(float);
+    w.part_off = w.counter_off + up((size_t)(U * (n_q / kC)) * sizeof(int));
+    w.head_off = w.part_off + (size_t)kSplit * 2 * (size_t)(U * n_q * kD) * sizeof(float);
+    w.total = w.head_off + (per_q_head ? 2 * (size_t)(Hq * n_q * kD) * sizeof(float) : 0);
     return w;
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q)
+size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
 {
-    return bwd_layout(Hq, Hkv, n_q).total;
+    return bwd_layout(Hq, Hkv, n_q, per_q_head).total;
 }
 
 int64_t bwd_max_queries() { return (int64_t)kMaxBlocksDkdv * kC; }
@@ -820,21 +855,34 @@ namespace {
 template <int kUnit>
 hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                            int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
-                           const int32_t *ids, int32_t k, int32_t sink, float scale,
-                           const float *lse, const uint16_t *dO, float *dQ, float *dK, float *dV,
-                           void *workspace, hipStream_t stream)
+                           const int32_t *ids, int32_t k, int32_t sink, bool per_q_head,
+                           float scale, const float *lse, const uint16_t *dO, float *dQ,
+                           float *dK, float *dV, void *workspace, hipStream_t stream)
 {
     if (n_q == 0) return hipSuccess;
-    const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q);
+    const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q, per_q_head);
     uint8_t *ws = (uint8_t *)workspace;
     float *delta = (float *)(ws + w.delta_off);
     int *counters = (int *)(ws + w.counter_off);
     float *part = (float *)(ws + w.part_off);
-    switch (Hq / Hkv) {
-    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    const int G = (int)(Hq / Hkv);
+    if (per_q_head) {
+        float *dKu = (float *)(ws + w.head_off);
+        float *dVu = dKu + Hq * n_q * kD;
+        hipError_t e = launch_bwd_g<1, kUnit>(Q, K, V, Hkv, G, T_cap, p0, n_q, ids, k, sink,
+                                              scale, lse, dO, dQ, dKu, dVu, delta, counters,
+                                              part, stream);
+        if (e != hipSuccess) return e;
+        const int64_t per_head = n_q * kD / 4, n_vec = Hkv * per_head;
+        hipLaunchKernelGGL(sum_heads_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256),
+                           0, stream, dKu, dVu, n_vec, G, per_head, dK, dV);
+        return hipGetLastError();
+    }
+    switch (G) {
+    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -844,13 +892,13 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                              int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                              int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
-                             float scale, const uint16_t *O, const float *lse,
+                             bool per_q_head, float scale, const uint16_t *O, const float *lse,
                              const uint16_t *dO, float *dQ, float *dK, float *dV,
                              void *workspace, hipStream_t stream)
 {
     (void)O;    // Delta is recomputed from P and dP (see the dq kernel)
-    return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, scale, lse, dO,
-                               dQ, dK, dV, workspace, stream);
+    return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, per_q_head,
+                               scale, lse, dO, dQ, dK, dV, workspace, stream);
 }
 
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
@@ -859,8 +907,8 @@ hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const 
                                     float scale, const float *lse, const uint16_t *dO, float *dQ,
                                     float *dK, float *dV, void *workspace, hipStream_t stream)
 {
-    return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, sink, scale, lse,
-                                   dO, dQ, dK, dV, workspace, stream);
+    return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, sink, false,
+                                   scale, lse, dO, dQ, dK, dV, workspace, stream);
 }
 
 }  // namespace hga

@@ -36,6 +36,10 @@
 // Workgroup w serves kv head w % Hkv: with 8 kv heads every block of one head
 // runs on the same XCD, where neighbouring blocks' overlapping chunk choices
 // hit that XCD's L2.
+//
+// Per-query-head routing (one id row per query head) runs the G = 1 kernel
+// with kv_div = query heads per kv head: each query head is then its own
+// unit, reading its own id row and its kv head's K and V.
 #include "route_core.h"
 
 #include <type_traits>
@@ -175,7 +179,7 @@ template <int G, int kUnit, int kRouteNI>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int64_t T_cap,
+    const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int kv_div, int64_t T_cap,
     int64_t p0, int32_t *__restrict__ ids, int k, int sink, float scale_log2,
     uint16_t *__restrict__ O, float *__restrict__ lse,
     const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores)
@@ -192,15 +196,17 @@ void attend_fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
+    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
+    const int64_t rest0 = blockIdx.x / Hkv;
+    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id row
+    const int64_t rest = rest0 / kv_div;
     const int hg = (int)(rest % NHG);
     const int64_t b = rest / NHG;
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
     const int64_t local_chunk = P / kC;
-    const uint16_t *Kg = K + g * T_cap * kD;
-    const uint16_t *Vg = V + g * T_cap * kD;
+    const uint16_t *Kg = K + gkv * T_cap * kD;
+    const uint16_t *Vg = V + gkv * T_cap * kD;
 
     // Group A = waves 0-3, group B = waves 4-7: wave w computes head
     // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
@@ -276,7 +282,7 @@ void attend_fwd_kernel(
         float *sc_row = (scores && wr) ? scores + (g * n_blocks + b) * k : nullptr;
         constexpr int kBatchR = G >= 8 ? 4 : 8;
         const int n_sel = route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
-            sh, keys, q_row, n_q, g, b, p0, S, n_cap, k, nullptr, 0, sink,
+            sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, k, nullptr, 0, sink,
             [&](int r, int id, float sc) __attribute__((always_inline)) {
                 list[1 + n_sink + r] = id;
                 if (wr) {
@@ -539,6 +545,7 @@ void attend_fwd_kernel(
 
 struct FwdArgs {
     const uint16_t *Q, *K, *V;
+    bool per_q_head;         // one id row per query head
     int64_t Hq, Hkv, T_cap, p0, n_q;
     int32_t *ids;
     int32_t k;
@@ -557,10 +564,11 @@ hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = a.n_q / kC;
     const float scale_log2 = a.scale * 1.44269504088896340736f;
+    const int kv_div = a.per_q_head ? (int)(a.Hq / a.Hkv) : 1;
     hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit, kRouteNI>),
-                       dim3((unsigned)(n_blocks * a.Hkv * NHG)), dim3(kThreads), 0, stream,
-                       a.Q, a.K, a.V, a.n_q, a.Hkv, a.T_cap, a.p0, a.ids, a.k, (int)a.sink,
-                       scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
+                       dim3((unsigned)(n_blocks * a.Hkv * kv_div * NHG)), dim3(kThreads), 0,
+                       stream, a.Q, a.K, a.V, a.n_q, a.Hkv, kv_div, a.T_cap, a.p0, a.ids, a.k,
+                       (int)a.sink, scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
     return hipGetLastError();
 }
 
@@ -568,7 +576,7 @@ template <int kUnit, int kRouteNI>
 hipError_t launch_unit(const FwdArgs &a, hipStream_t stream)
 {
     if (a.n_q == 0) return hipSuccess;
-    switch (a.Hq / a.Hkv) {
+    switch (a.per_q_head ? 1 : a.Hq / a.Hkv) {       // query heads per unit
     case 1: return launch_g<1, kUnit, kRouteNI>(a, stream);
     case 2: return launch_g<2, kUnit, kRouteNI>(a, stream);
     case 4: return launch_g<4, kUnit, kRouteNI>(a, stream);
@@ -582,11 +590,11 @@ hipError_t launch_unit(const FwdArgs &a, hipStream_t stream)
 hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, int32_t sink, float scale,
-                             uint16_t *O, float *lse, hipStream_t stream)
+                             const int32_t *ids, int32_t k, int32_t sink, bool per_q_head,
+                             float scale, uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(ids), k, sink,
-                    scale, O, lse, nullptr, 0, nullptr};
+    const FwdArgs a{Q, K, V, per_q_head, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(ids),
+                    k, sink, scale, O, lse, nullptr, 0, nullptr};
     return launch_unit<kC, 0>(a, stream);
 }
 
@@ -596,8 +604,8 @@ hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     const int32_t *gids, int32_t m, int32_t sink, float scale,
                                     uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(gids), m, sink,
-                    scale, O, lse, nullptr, 0, nullptr};
+    const FwdArgs a{Q, K, V, false, Hq, Hkv, T_cap, p0, n_q, const_cast<int32_t *>(gids), m,
+                    sink, scale, O, lse, nullptr, 0, nullptr};
     return launch_unit<kGroup, 0>(a, stream);
 }
 
@@ -609,11 +617,11 @@ int64_t route_attend_max_candidates()
 hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                    int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                                   int32_t sink, float scale, int32_t *ids, float *scores,
-                                   uint16_t *O, float *lse, hipStream_t stream)
+                                   int32_t sink, bool per_q_head, float scale, int32_t *ids,
+                                   float *scores, uint16_t *O, float *lse, hipStream_t stream)
 {
-    const FwdArgs a{Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse, S, n_cap,
-                    scores};
+    const FwdArgs a{Q, K, V, per_q_head, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, scale, O, lse,
+                    S, n_cap, scores};
     if (k == 0) return launch_unit<kC, 0>(a, stream);
     // keys per lane of the router's register selection: the smallest class
     // that holds the largest candidate count (beyond 2048 the LDS path)

@@ -61,8 +61,22 @@ hga_status check_config(const hga_config *cfg)
     if (cfg->sink_chunks > HGA_MAX_SINK_CHUNKS)
         return fail(HGA_ERR_UNSUPPORTED, "sink_chunks must be at most %d (got %d)",
                     HGA_MAX_SINK_CHUNKS, cfg->sink_chunks);
+    if (cfg->route_heads != HGA_ROUTE_PER_KV_HEAD && cfg->route_heads != HGA_ROUTE_PER_Q_HEAD)
+        return fail(HGA_ERR_INVALID_ARG, "route_heads must be HGA_ROUTE_PER_KV_HEAD or "
+                    "HGA_ROUTE_PER_Q_HEAD (got %d)", cfg->route_heads);
     return HGA_OK;
 }
+
+// The entry points that only know one id row per kv head.
+hga_status check_kv_head_routing(const hga_config *cfg, const char *what)
+{
+    if (cfg->route_heads != HGA_ROUTE_PER_KV_HEAD)
+        return fail(HGA_ERR_UNSUPPORTED, "%s supports route_heads = HGA_ROUTE_PER_KV_HEAD only",
+                    what);
+    return HGA_OK;
+}
+
+bool per_q_head(const hga_config *cfg) { return cfg->route_heads == HGA_ROUTE_PER_Q_HEAD; }
 
 float effective_scale(const hga_config *cfg)
 {
@@ -134,9 +148,11 @@ hga_status hga_summarize(const hga_config *cfg, const void *K, int64_t T_cap,
                       "hga_summarize launch");
 }
 
-hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
-                     const float *summaries, int64_t n_chunk_cap, int64_t n_chunks_valid,
-                     int32_t *ids, float *scores_or_null, hipStream_t stream)
+static hga_status route_common(const hga_config *cfg, const void *Q, const void *Q_prev,
+                               bool prev_block, int64_t p0, int64_t n_q,
+                               const float *summaries, int64_t n_chunk_cap,
+                               int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                               hipStream_t stream, const char *what)
 {
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
@@ -158,10 +174,32 @@ hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n
                     (long long)kMaxEligible);
     if (!Q || !ids || (need > 0 && !summaries))
         return fail(HGA_ERR_INVALID_ARG, "Q, summaries or ids is NULL");
+    if (prev_block && p0 > 0 && !Q_prev)
+        return fail(HGA_ERR_INVALID_ARG, "Q_prev is NULL with p0 = %lld > 0", (long long)p0);
     return hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads, p0,
                                         n_q, summaries, n_chunk_cap, cfg->top_k,
-                                        cfg->sink_chunks, ids, scores_or_null, stream),
-                      "hga_route launch");
+                                        cfg->sink_chunks, per_q_head(cfg), prev_block,
+                                        (const uint16_t *)Q_prev, ids, scores_or_null, stream),
+                      what);
+}
+
+hga_status hga_route(const hga_config *cfg, const void *Q, int64_t p0, int64_t n_q,
+                     const float *summaries, int64_t n_chunk_cap,
+                     int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                     hipStream_t stream)
+{
+    return route_common(cfg, Q, nullptr, false, p0, n_q, summaries, n_chunk_cap,
+                        n_chunks_valid, ids, scores_or_null, stream, "hga_route launch");
+}
+
+hga_status hga_route_causal(const hga_config *cfg, const void *Q, const void *Q_prev,
+                            int64_t p0, int64_t n_q, const float *summaries,
+                            int64_t n_chunk_cap, int64_t n_chunks_valid, int32_t *ids,
+                            float *scores_or_null, hipStream_t stream)
+{
+    return route_common(cfg, Q, p0 > 0 ? Q_prev : nullptr, true, p0, n_q, summaries,
+                        n_chunk_cap, n_chunks_valid, ids, scores_or_null, stream,
+                        "hga_route_causal launch");
 }
 
 hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, const void *V,
@@ -179,8 +217,8 @@ hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K, c
     return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                              (const uint16_t *)V, cfg->n_q_heads,
                                              cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
-                                             cfg->sink_chunks, effective_scale(cfg),
-                                             (uint16_t *)O, lse, stream),
+                                             cfg->sink_chunks, per_q_head(cfg),
+                                             effective_scale(cfg), (uint16_t *)O, lse, stream),
                       "hga_attend_fwd launch");
 }
 
@@ -218,22 +256,23 @@ hga_status hga_route_attend_fwd(const hga_config *cfg, const void *Q, const void
         // kernel, then the attention kernel (the same ids, scores and outputs)
         st = hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads,
                                           p0, n_q, summaries, n_chunk_cap, cfg->top_k,
-                                          cfg->sink_chunks, ids, scores_or_null, stream),
+                                          cfg->sink_chunks, per_q_head(cfg), false, nullptr,
+                                          ids, scores_or_null, stream),
                         "hga_route_attend_fwd route launch");
         if (st != HGA_OK) return st;
         return hip_status(hga::launch_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                                  (const uint16_t *)V, cfg->n_q_heads,
                                                  cfg->n_kv_heads, T_cap, p0, n_q, ids,
-                                                 cfg->top_k, cfg->sink_chunks, scale,
-                                                 (uint16_t *)O, lse, stream),
+                                                 cfg->top_k, cfg->sink_chunks, per_q_head(cfg),
+                                                 scale, (uint16_t *)O, lse, stream),
                           "hga_route_attend_fwd attend launch");
     }
     return hip_status(hga::launch_route_attend_fwd((const uint16_t *)Q, (const uint16_t *)K,
                                                    (const uint16_t *)V, cfg->n_q_heads,
                                                    cfg->n_kv_heads, T_cap, p0, n_q, summaries,
                                                    n_chunk_cap, cfg->top_k, cfg->sink_chunks,
-                                                   scale, ids, scores_or_null, (uint16_t *)O,
-                                                   lse, stream),
+                                                   per_q_head(cfg), scale, ids, scores_or_null,
+                                                   (uint16_t *)O, lse, stream),
                       "hga_route_attend_fwd launch");
 }
 
@@ -272,6 +311,8 @@ hga_status hga_route_groups(const hga_config *cfg, const void *Q, int64_t p0, in
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_route_groups");
+    if (st != HGA_OK) return st;
     st = check_segment(p0, n_q, 0, false);
     if (st != HGA_OK) return st;
     if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
@@ -302,6 +343,8 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_attend_fwd_groups");
+    if (st != HGA_OK) return st;
     st = check_segment(p0, n_q, T_cap, true);
     if (st != HGA_OK) return st;
     if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
@@ -329,6 +372,8 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_attend_bwd_groups");
+    if (st != HGA_OK) return st;
     st = check_segment(p0, n_q, T_cap, true);
     if (st != HGA_OK) return st;
     if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
@@ -341,7 +386,7 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
     if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
         (group_top_k > 0 && !group_ids))
         return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
-    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q, false);
     if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < need)
         return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
@@ -363,6 +408,8 @@ hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, in
 {
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_route_decode");
     if (st != HGA_OK) return st;
     if (p0 < 0 || n_q < 0 || n_chunks_valid < 0 || n_chunk_cap < 0)
         return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
@@ -406,6 +453,8 @@ hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_attend_decode");
+    if (st != HGA_OK) return st;
     if (p0 < 0 || n_q < 0 || T_cap < 0)
         return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
     if (p0 + n_q > T_cap)
@@ -441,6 +490,8 @@ hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, 
     g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_diag_gather");
+    if (st != HGA_OK) return st;
     st = check_segment(p0, n_q, T_cap, true);
     if (st != HGA_OK) return st;
     if (n_q == 0) return HGA_OK;
@@ -458,7 +509,7 @@ hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, 
 size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)
 {
     if (check_config(cfg) != HGA_OK || n_q < 0 || n_q % hga::kC != 0) return 0;
-    return hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+    return hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q, per_q_head(cfg));
 }
 
 hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, const void *V,
@@ -479,15 +530,16 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, c
     if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
         (cfg->top_k > 0 && !ids))
         return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
-    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q);
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q,
+                                                 per_q_head(cfg));
     if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
     if (ws_bytes < need)
         return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
     return hip_status(hga::launch_attend_bwd((const uint16_t *)Q, (const uint16_t *)K,
                                              (const uint16_t *)V, cfg->n_q_heads,
                                              cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
-                                             cfg->sink_chunks, effective_scale(cfg),
-                                             (const uint16_t *)O, lse,
+                                             cfg->sink_chunks, per_q_head(cfg),
+                                             effective_scale(cfg), (const uint16_t *)O, lse,
                                              (const uint16_t *)dO, dQ, dK_active, dV_active,
                                              workspace, stream),
                       "hga_attend_bwd launch");

@@ -124,8 +124,13 @@ hipError_t launch_summarize_groups(const uint16_t *K, int64_t Hkv, int64_t T_cap
                                    int64_t c_begin, int64_t c_end, float *SG,
                                    int64_t n_gcap, hipStream_t stream);
 
+// per_q_head: one routing unit (id row) per query head instead of per kv
+// head. prev_block: strictly causal routing (block b scores with block b-1's
+// queries; Q_prev [Hq][C][D] holds the C queries before p0, used by block 0,
+// and may be null when p0 == 0).
 hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                         int64_t n_q, const float *S, int64_t n_cap, int32_t k, int32_t sink,
+                        bool per_q_head, bool prev_block, const uint16_t *Q_prev,
                         int32_t *ids, float *scores, hipStream_t stream);
 
 hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
@@ -136,8 +141,8 @@ hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64
 hipError_t launch_attend_fwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, int32_t sink, float scale,
-                             uint16_t *O, float *lse, hipStream_t stream);
+                             const int32_t *ids, int32_t k, int32_t sink, bool per_q_head,
+                             float scale, uint16_t *O, float *lse, hipStream_t stream);
 
 hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
                                     const uint16_t *V, int64_t Hq, int64_t Hkv,
@@ -150,8 +155,8 @@ hipError_t launch_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
 hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                    int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                    int64_t n_q, const float *S, int64_t n_cap, int32_t k,
-                                   int32_t sink, float scale, int32_t *ids, float *scores,
-                                   uint16_t *O, float *lse, hipStream_t stream);
+                                   int32_t sink, bool per_q_head, float scale, int32_t *ids,
+                                   float *scores, uint16_t *O, float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
 // Routed decode (decode.hip). One workspace of decode_workspace_bytes serves
 // the router (the keys of up to decode_key_capacity candidates per token and
@@ -181,7 +186,7 @@ hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const 
                                     float scale, const float *lse, const uint16_t *dO, float *dQ,
                                     float *dK, float *dV, void *workspace, hipStream_t stream);
 
-size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q);
+size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head);
 
 // Largest active segment (queries) the backward's key-major pass can list.
 int64_t bwd_max_queries();
@@ -189,8 +194,8 @@ int64_t bwd_max_queries();
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,
                              int64_t T_cap, int64_t p0, int64_t n_q,
-                             const int32_t *ids, int32_t k, int32_t sink, float scale,
-                             const uint16_t *O, const float *lse,
+                             const int32_t *ids, int32_t k, int32_t sink, bool per_q_head,
+                             float scale, const uint16_t *O, const float *lse,
                              const uint16_t *dO, float *dQ, float *dK,
                              float *dV, void *workspace, hipStream_t stream);
 

@@ -4,34 +4,50 @@
 // earlier chunks; the chosen chunks' 8-token groups are ranked the same way
 // by their own summaries; no gradient flows through the choice).
 //
-// One 256-thread workgroup per (query block b, kv head g) runs route_block
-// (route_core.h). Workgroup w serves kv head w % Hkv: with 8 kv heads the
-// blocks of one head land on one XCD and share its L2 copy of that head's
-// summaries.
+// One 256-thread workgroup per (query block b, routing unit) runs route_block
+// (route_core.h). A routing unit is a kv head (its G query heads share one
+// id row) or, with per-query-head routing, one query head (kv_div = G query
+// heads per kv head, each its own unit scored against its kv head's
+// summaries). Workgroup w serves kv head w % Hkv: with 8 kv heads the blocks
+// of one head land on one XCD and share its L2 copy of that head's summaries.
+// kPrev: strictly causal routing, where block b scores with the queries of
+// block b - 1 (Q_prev, the 64 queries before p0, for block 0).
 #include "route_core.h"
 
 namespace hga {
 namespace {
 
-template <int G, int NI, bool kGroups>
+template <int G, int NI, bool kGroups, bool kPrev>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const uint16_t *__restrict__ Q, int64_t n_q, int64_t Hkv, int64_t p0,
-    const float *__restrict__ S, int64_t n_cap, int k,
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Q_prev, int64_t n_q,
+    int64_t Hkv, int kv_div, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
     const int32_t *__restrict__ chunk_ids, int kc, int c_lo,
     int32_t *__restrict__ ids, float *__restrict__ scores)
 {
     extern __shared__ uint32_t keys[];          // [candidates of this block]
     __shared__ RouteLds sh;
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t b = blockIdx.x / Hkv;
-    int32_t *out = ids + (g * (n_q / kC) + b) * k;
-    float *sout = scores ? scores + (g * (n_q / kC) + b) * k : nullptr;
+    const int64_t gkv = blockIdx.x % Hkv;
+    const int64_t rest = blockIdx.x / Hkv;
+    const int64_t u = gkv * kv_div + rest % kv_div;     // routing unit
+    const int64_t b = rest / kv_div;
+    int32_t *out = ids + (u * (n_q / kC) + b) * k;
+    float *sout = scores ? scores + (u * (n_q / kC) + b) * k : nullptr;
     auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {
-        const int64_t h = g * G + row / kC;
-        const int64_t i = b * kC + row % kC;
-        return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+        const int64_t h = u * G + row / kC;
+        if constexpr (kPrev) {
+            if (b == 0) {
+                // (no queries before p0 = 0: block 0 has no candidates then)
+                if (!Q_prev) return u32x4{0u, 0u, 0u, 0u};
+                return *(const u32x4 *)(Q_prev + (h * kC + row % kC) * kD + dseg * 8);
+            }
+            const int64_t i = (b - 1) * kC + row % kC;
+            return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+        } else {
+            const int64_t i = b * kC + row % kC;
+            return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
+        }
     };
-    route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, g, b, p0, S, n_cap, k,
+    route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, k,
                                                  chunk_ids, kc, c_lo,
                                     [&](int r, int id, float sc) __attribute__((always_inline)) {
                                         out[r] = id;
@@ -41,6 +57,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
 struct RouteArgs {
     const uint16_t *Q;
+    const uint16_t *Q_prev;     // strictly causal routing only
+    bool per_q_head;
     int64_t Hq, Hkv, p0, n_q;
     const float *S;             // chunk or group summaries
     int64_t n_cap;
@@ -52,20 +70,22 @@ struct RouteArgs {
     float *scores;
 };
 
-template <int G, int NI, bool kGroups>
+template <int G, int NI, bool kGroups, bool kPrev>
 hipError_t launch_route_gn(const RouteArgs &a, size_t shmem, hipStream_t stream)
 {
     const int64_t n_blocks = a.n_q / kC;
-    hipLaunchKernelGGL((route_kernel<G, NI, kGroups>), dim3((unsigned)(n_blocks * a.Hkv)),
-                       dim3(kRouteThreads), shmem, stream, a.Q, a.n_q, a.Hkv, a.p0, a.S,
-                       a.n_cap, a.k, a.chunk_ids, a.kc, (int)a.sink, a.ids, a.scores);
+    const int kv_div = a.per_q_head ? (int)(a.Hq / a.Hkv) : 1;
+    hipLaunchKernelGGL((route_kernel<G, NI, kGroups, kPrev>),
+                       dim3((unsigned)(n_blocks * a.Hkv * kv_div)), dim3(kRouteThreads), shmem,
+                       stream, a.Q, a.Q_prev, a.n_q, a.Hkv, kv_div, a.p0, a.S, a.n_cap, a.k,
+                       a.chunk_ids, a.kc, (int)a.sink, a.ids, a.scores);
     return hipGetLastError();
 }
 
 // Keys per lane of the register selection: the smallest class that holds the
 // largest candidate count; beyond 2048 (chunk routing only) the LDS path
 // takes over.
-template <int G, bool kGroups>
+template <int G, bool kGroups, bool kPrev>
 hipError_t launch_route_g(const RouteArgs &a, hipStream_t stream)
 {
     int64_t max_chunks = (a.p0 + a.n_q - kC) / kC - a.sink;
@@ -75,20 +95,21 @@ hipError_t launch_route_g(const RouteArgs &a, hipStream_t stream)
     // chunk routing keeps the keys; group routing also sorts up to kc ids there
     int64_t slots = max_eligible > a.kc ? max_eligible : (kGroups ? a.kc : max_eligible);
     const size_t shmem = (size_t)(slots > 0 ? slots : 1) * sizeof(uint32_t);
-    if (max_eligible <= 4 * 64) return launch_route_gn<G, 4, kGroups>(a, shmem, stream);
-    if (max_eligible <= 8 * 64) return launch_route_gn<G, 8, kGroups>(a, shmem, stream);
-    if (max_eligible <= 16 * 64) return launch_route_gn<G, 16, kGroups>(a, shmem, stream);
-    return launch_route_gn<G, kMaxRegKeys, kGroups>(a, shmem, stream);
+    if (max_eligible <= 4 * 64) return launch_route_gn<G, 4, kGroups, kPrev>(a, shmem, stream);
+    if (max_eligible <= 8 * 64) return launch_route_gn<G, 8, kGroups, kPrev>(a, shmem, stream);
+    if (max_eligible <= 16 * 64) return launch_route_gn<G, 16, kGroups, kPrev>(a, shmem, stream);
+    return launch_route_gn<G, kMaxRegKeys, kGroups, kPrev>(a, shmem, stream);
 }
 
-template <bool kGroups>
+// G here is the query heads of one routing unit: 1 for per-query-head routing.
+template <bool kGroups, bool kPrev>
 hipError_t launch_route_any(const RouteArgs &a, hipStream_t stream)
 {
-    switch (a.Hq / a.Hkv) {
-    case 1: return launch_route_g<1, kGroups>(a, stream);
-    case 2: return launch_route_g<2, kGroups>(a, stream);
-    case 4: return launch_route_g<4, kGroups>(a, stream);
-    case 8: return launch_route_g<8, kGroups>(a, stream);
+    switch (a.per_q_head ? 1 : a.Hq / a.Hkv) {
+    case 1: return launch_route_g<1, kGroups, kPrev>(a, stream);
+    case 2: return launch_route_g<2, kGroups, kPrev>(a, stream);
+    case 4: return launch_route_g<4, kGroups, kPrev>(a, stream);
+    case 8: return launch_route_g<8, kGroups, kPrev>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -97,11 +118,14 @@ hipError_t launch_route_any(const RouteArgs &a, hipStream_t stream)
 
 hipError_t launch_route(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
                         int64_t n_q, const float *S, int64_t n_cap, int32_t k, int32_t sink,
+                        bool per_q_head, bool prev_block, const uint16_t *Q_prev,
                         int32_t *ids, float *scores, hipStream_t stream)
 {
     if (n_q == 0 || k == 0) return hipSuccess;
-    const RouteArgs a{Q, Hq, Hkv, p0, n_q, S, n_cap, k, nullptr, 0, sink, ids, scores};
-    return launch_route_any<false>(a, stream);
+    const RouteArgs a{Q, Q_prev, per_q_head, Hq, Hkv, p0, n_q, S, n_cap, k, nullptr, 0, sink,
+                      ids, scores};
+    return prev_block ? launch_route_any<false, true>(a, stream)
+                      : launch_route_any<false, false>(a, stream);
 }
 
 hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64_t p0,
@@ -110,8 +134,9 @@ hipError_t launch_route_groups(const uint16_t *Q, int64_t Hq, int64_t Hkv, int64
                                int32_t *gids, float *scores, hipStream_t stream)
 {
     if (n_q == 0 || m == 0) return hipSuccess;
-    const RouteArgs a{Q, Hq, Hkv, p0, n_q, SG, n_gcap, m, chunk_ids, kc, sink, gids, scores};
-    return launch_route_any<true>(a, stream);
+    const RouteArgs a{Q, nullptr, false, Hq, Hkv, p0, n_q, SG, n_gcap, m, chunk_ids, kc, sink,
+                      gids, scores};
+    return launch_route_any<true, false>(a, stream);
 }
 
 }  // namespace hga

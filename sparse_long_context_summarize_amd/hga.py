@@ -21,13 +21,16 @@ HGA_ERR_CAPACITY = 3
 HGA_ERR_HIP = 4
 HGA_BF16 = 0
 
-EXPORTED = ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_route_attend_fwd",
+EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
+            "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
             "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
             "hga_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
             "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
+HGA_ROUTE_PER_KV_HEAD = 0
+HGA_ROUTE_PER_Q_HEAD = 1
 
 
 class hga_config(ctypes.Structure):
@@ -35,14 +38,15 @@ class hga_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("q_block", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("sink_chunks", ctypes.c_int32)]
+                ("sink_chunks", ctypes.c_int32), ("route_heads", ctypes.c_int32)]
 
 
 def make_config(n_q_heads: int, n_kv_heads: int, top_k: int, *, head_dim: int = 128,
                 chunk: int = 64, q_block: int = 64, softmax_scale: float = 0.0,
-                dtype: int = HGA_BF16, sink_chunks: int = 0) -> hga_config:
+                dtype: int = HGA_BF16, sink_chunks: int = 0,
+                route_heads: int = HGA_ROUTE_PER_KV_HEAD) -> hga_config:
     return hga_config(n_q_heads, n_kv_heads, head_dim, chunk, q_block, top_k,
-                      softmax_scale, dtype, sink_chunks)
+                      softmax_scale, dtype, sink_chunks, route_heads)
 
 
 class HGAError(RuntimeError):
@@ -70,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     L.hga_summarize.argtypes = [_cfgp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
     L.hga_route.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp]
+    L.hga_route_causal.argtypes = [_cfgp, _vp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp,
+                                   _vp]
     L.hga_attend_fwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]
     L.hga_attend_bwd_workspace_bytes.argtypes = [_cfgp, _i64]
     L.hga_attend_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -95,7 +101,8 @@ def lib() -> ctypes.CDLL:
     L.hga_attend_bwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
-    for fn in ("hga_summarize", "hga_route", "hga_attend_fwd", "hga_attend_bwd",
+    for fn in ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
+               "hga_attend_bwd",
                "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
                "hga_attend_bwd_groups", "hga_diag_gather", "hga_route_decode",
@@ -158,6 +165,15 @@ def _m_summarize(cfg: hga_config, K, tok_begin: int, n_tok: int, summaries, stre
 def _m_route(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids, scores=None,
              stream=None):
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _stream(stream))
+
+
+def _m_route_causal(cfg: hga_config, Q, Q_prev, p0: int, summaries, n_chunks_valid: int, ids,
+                    scores=None, stream=None):
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16),
+            _dev(Q_prev, "Q_prev", torch.bfloat16), p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
             _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
             _stream(stream))
@@ -284,6 +300,7 @@ def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=N
 
 
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
+            "hga_route_causal": _m_route_causal,
             "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
             "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
@@ -303,9 +320,19 @@ def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
 def hga_route(cfg: hga_config, Q: torch.Tensor, p0: int, summaries: torch.Tensor,
               n_chunks_valid: int, ids: torch.Tensor, scores: torch.Tensor | None = None,
               stream=None) -> None:
-    """Q bf16 [Hq][n_q][D]; ids int32 [Hkv][n_q/64][k]; scores f32 like ids or None."""
+    """Q bf16 [Hq][n_q][D]; ids int32 [U][n_q/64][k] (U = Hkv, or Hq with per-query-head
+    routing); scores f32 like ids or None."""
     _check("hga_route", lib().hga_route(
         *_m_route(cfg, Q, p0, summaries, n_chunks_valid, ids, scores, stream)))
+
+
+def hga_route_causal(cfg: hga_config, Q: torch.Tensor, Q_prev: torch.Tensor | None, p0: int,
+                     summaries: torch.Tensor, n_chunks_valid: int, ids: torch.Tensor,
+                     scores: torch.Tensor | None = None, stream=None) -> None:
+    """Strictly causal routing: block b scores with the 64 queries before it
+    (Q_prev bf16 [Hq][64][D] for the first block; None only when p0 == 0)."""
+    _check("hga_route_causal", lib().hga_route_causal(
+        *_m_route_causal(cfg, Q, Q_prev, p0, summaries, n_chunks_valid, ids, scores, stream)))
 
 
 def hga_attend_fwd(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

@@ -239,3 +239,32 @@ def test_decode_checks():
 
     assert attend(need - 1) == hga.HGA_ERR_CAPACITY
     assert attend(need, T=p0) == hga.HGA_ERR_INVALID_ARG
+
+
+def test_routing_variant_checks():
+    L = hga.lib()
+    bad = _cfg(route_heads=2)
+    assert _fwd(bad) == hga.HGA_ERR_INVALID_ARG
+    assert "route_heads" in hga.hga_last_error()
+    per_head = _cfg(route_heads=hga.HGA_ROUTE_PER_Q_HEAD)
+    # the group level, decode and the diagnostic know one id row per kv head
+    assert L.hga_route_groups(ctypes.byref(per_head), FAKE, 14336, 2048, FAKE, 14336 // 8, FAKE,
+                              8, FAKE, None, None) == hga.HGA_ERR_UNSUPPORTED
+    assert L.hga_attend_fwd_groups(ctypes.byref(per_head), FAKE, FAKE, FAKE, 16384, 14336,
+                                   2048, FAKE, 8, FAKE, FAKE, None) == hga.HGA_ERR_UNSUPPORTED
+    assert L.hga_route_decode(ctypes.byref(per_head), FAKE, 100, 1, FAKE, 1, 1, FAKE, None,
+                              FAKE, 1 << 20, None) == hga.HGA_ERR_UNSUPPORTED
+    # the backward workspace grows by the per-head dK and dV and the per-head
+    # counters and partial sums
+    n_q = 2048
+    a = hga.hga_attend_bwd_workspace_bytes(_cfg(), n_q)
+    b = hga.hga_attend_bwd_workspace_bytes(per_head, n_q)
+    up = lambda v: (v + 255) // 256 * 256
+    delta = up(32 * n_q * 4)
+    assert a == delta + up(8 * 32 * 4) + 2 * 2 * 8 * n_q * 128 * 4
+    assert b == delta + up(32 * 32 * 4) + 2 * 2 * 32 * n_q * 128 * 4 + 2 * 32 * n_q * 128 * 4
+    # strictly causal routing needs the queries before p0 once p0 > 0
+    args = lambda p0, qp: (ctypes.byref(_cfg()), FAKE, qp, p0, 2048, FAKE, 256, 256, FAKE,
+                           None, None)
+    assert L.hga_route_causal(*args(14336, None)) == hga.HGA_ERR_INVALID_ARG
+    assert "Q_prev" in hga.hga_last_error()
