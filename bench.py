@@ -311,6 +311,7 @@ def extra_timings(torch, hga, inputs, dev):
     res.update(segloop_timing(torch, hga, inputs, dev))
     res.update(group_timings(torch, hga, inputs, dev))
     res.update(decode_timings(torch, hga, inputs, dev))
+    res.update(variant_timings(torch, hga, inputs, dev))
     res.update(attend_timings(torch, hga, inputs, dev))
     try:
         times = []
@@ -461,6 +462,70 @@ def group_timings(torch, hga, inputs, dev):
         "groups16k_bwd_us": ms_bwd * 1e3,
         "groups16k_bwd_algorithmic_gflop": fl_bwd / 1e9,
         "groups16k_bwd_tflops": fl_bwd / (ms_bwd * 1e-3) / 1e12,
+    })
+    return res
+
+
+def variant_timings(torch, hga, inputs, dev):
+    """The routing variants at the 16K layer, each call HIP-event timed alone
+    (median of 10): per-query-head routing (one id row per query head, so the
+    G heads of a kv head gather their chunks separately) through the fused
+    route + attention, the routing alone, the attention alone and the
+    backward; strictly causal routing (hga_route_causal) beside the default
+    router."""
+    w = inputs.LAYER16K
+    x = inputs.generate(w)
+
+    def up(a):
+        return torch.from_numpy(a).to(torch.bfloat16).to(dev)
+
+    Q, K, V = up(x["Q"]), up(x["K"]), up(x["V"])
+    nb = w.n_q // C
+    cfg_h = hga.make_config(w.Hq, w.Hkv, w.k, route_heads=hga.HGA_ROUTE_PER_Q_HEAD)
+    cfg = hga.make_config(w.Hq, w.Hkv, w.k)
+    S = torch.empty((w.Hkv, w.T // C, w.D), device=dev)
+    hga.hga_summarize(cfg, K, 0, w.T, S)
+    ids_h = torch.empty((w.Hq, nb, w.k), dtype=torch.int32, device=dev)
+    ids = torch.empty((w.Hkv, nb, w.k), dtype=torch.int32, device=dev)
+    O = torch.empty((w.Hq, w.n_q, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.Hq, w.n_q), device=dev)
+    dO = up(np.random.default_rng(6).standard_normal((w.Hq, w.n_q, w.D), dtype=np.float32))
+    Q_prev = up(np.random.default_rng(7).standard_normal((w.Hq, C, w.D), dtype=np.float32))
+    dQ = torch.empty((w.Hq, w.n_q, w.D), device=dev)
+    dK = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+    dV = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+    ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg_h, w.n_q), dtype=torch.uint8,
+                     device=dev)
+    calls = {
+        "perhead16k_route_attend": hga.prepare("hga_route_attend_fwd", cfg_h, Q, K, V, w.p0, S,
+                                               w.T // C, ids_h, O, lse),
+        "perhead16k_route": hga.prepare("hga_route", cfg_h, Q, w.p0, S, w.T // C, ids_h),
+        "perhead16k_attend": hga.prepare("hga_attend_fwd", cfg_h, Q, K, V, w.p0, ids_h, O, lse),
+        "perhead16k_bwd": hga.prepare("hga_attend_bwd", cfg_h, Q, K, V, w.p0, ids_h, O, lse, dO,
+                                      dQ, dK, dV, ws),
+        "causal16k_route": hga.prepare("hga_route_causal", cfg, Q, Q_prev, w.p0, S, w.T // C,
+                                       ids),
+        "default16k_route": hga.prepare("hga_route", cfg, Q, w.p0, S, w.T // C, ids),
+    }
+    res = {}
+    for name, fn in calls.items():
+        fn()
+        res[f"{name}_us"] = _median_ms(torch, fn) * 1e3
+    calls["perhead16k_route_attend"]()
+    torch.cuda.synchronize()
+    g = ids_h.cpu().numpy()                    # one row per query head: G = 1 per unit
+    fl = attend_flops(g, w.n_q, 1, w.D, w.p0)
+    ab = attend_bytes(g, w.n_q, w.Hq, w.D, w.p0)
+    fl_bwd = bwd_flops(g, w.n_q, 1, w.D, w.p0)
+    t_att = res["perhead16k_attend_us"] * 1e-6
+    res.update({
+        "perhead16k_query_tokens_per_s": w.n_q / (res["perhead16k_route_attend_us"] * 1e-6),
+        "perhead16k_attend_algorithmic_gflop": fl / 1e9,
+        "perhead16k_attend_tflops": fl / t_att / 1e12,
+        "perhead16k_attend_gathered_GBps": ab / t_att / 1e9,
+        "perhead16k_attend_hbm_frac": ab / t_att / 8e12,
+        "perhead16k_bwd_algorithmic_gflop": fl_bwd / 1e9,
+        "perhead16k_bwd_tflops": fl_bwd / (res["perhead16k_bwd_us"] * 1e-6) / 1e12,
     })
     return res
 
