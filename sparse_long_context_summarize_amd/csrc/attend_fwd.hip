@@ -16,22 +16,18 @@
 //                            32 keys of each 32-key half; lane ^ 32 holds the
 //                            other 16, one lane swap joins them
 //   O^T[d][q] += V^T P^T     B = P^T straight from the S^T accumulators (bf16);
-//                            A = V^T read from the row-major V tile with the
-//                            gfx950 transposing LDS read ds_read_b64_tr_b16
-//                            (each 16-lane group turns four 4-element row
-//                            pieces into four 4-key columns), two per operand.
+//                            A = V^T, stored transposed in LDS (see store_v)
+//                            so that each operand is one 16-byte read.
 // The S^T accumulator's row order (8*(j/4) + 4*(lane/32) + j%4) fixes which
-// keys each lane's P^T operand holds; the transposing reads fetch V rows in
-// exactly that order, so no data is permuted anywhere.
+// keys each lane's P^T operand holds; store_v places V's keys in that order.
 // The running max is rescaled lazily: O^T and the row sum are only rescaled
 // when some row's max grows by more than 8 (log2 units), otherwise the stale
 // max stays and probabilities up to 2^8 enter the bf16 operand unchanged.
 //
-// Chunk tiles (32 KiB of K and V) are loaded two tiles ahead into registers
-// (16-byte coalesced loads, a 256-byte key row per 16 lanes) and written to a
-// double-buffered LDS tile one barrier before use. LDS rows are padded: K to
-// 272 B (conflict-free 16-byte operand reads), V to 320 B (the four rows a
-// transposing read touches start 64 B apart in the banks).
+// Chunk tiles (32 KiB of K and V) are loaded ahead into registers (16-byte
+// coalesced loads, a 256-byte key row per 16 lanes) and written to a
+// double-buffered LDS tile one barrier before use. K rows are padded to 272 B
+// (conflict-free 16-byte operand reads); V^T rows to 144 B.
 //
 // Workgroup w serves kv head w % Hkv: with 8 kv heads every block of one head
 // runs on the same XCD, where neighbouring blocks' overlapping chunk choices
