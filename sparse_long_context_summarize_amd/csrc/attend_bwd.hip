@@ -17,8 +17,8 @@
 //          as V^T does in the forward.
 //   dkdv   key-major over the active chunks only (history is detached): the
 //          workgroups of chunk a scan the routed ids for the later blocks that
-//          chose a; the list (own block first) is dealt round-robin to up to
-//          kSplit workgroups, each walking its blocks x the G query heads:
+//          chose a; the list's (block, query head) tiles, own block first,
+//          are dealt round-robin to up to kSplit workgroups:
 //          S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
 //          Wave w owns keys 32*(w&1).. and queries 32*(w>>1).. of each query
 //          tile; the two query halves are summed through LDS. A chunk chosen
@@ -405,7 +405,12 @@ constexpr int kBufBytes = kDlOff + kC * 4;
 static_assert(kBufBytes % 16 == 0, "buffer alignment");
 static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits");
 
-constexpr int kSplit = 2;                  // workgroups that share one chunk's block list
+// A chunk's query tiles go to one workgroup, or to kSplit of them when there
+// are more than kMinTiles (more workgroups per chunk measured slower: each
+// one, even one with nothing dealt, pays the scan and the set-up, and the
+// dkdv workgroup holds a whole CU).
+constexpr int kSplit = 2;
+constexpr int kMinTiles = 8;
 
 // kUnit = kGroup: a later block may have chosen only some of the chunk's 8
 // groups; the scan records them as an 8-bit mask per listed block, and the
@@ -501,11 +506,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         if (lane == 0) blist_n = cnt;
     }
     __syncthreads();
+    // The chunk's query tiles -- (listed block, query head) pairs, block-major
+    // -- are dealt round-robin to n_parts workgroups: this one takes tiles
+    // split, split + n_parts, ... (tile T: block blist[T / G], head T % G).
     const int n_list = blist_n;
-    const int n_parts = n_list < kSplit ? n_list : kSplit;
+    const int n_all = n_list * G;
+    const int n_parts = min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
     if (split >= n_parts) return;                 // nothing dealt to this workgroup
-    const int n_mine = (n_list - split + kSplit - 1) / kSplit;   // entries split, split+kSplit, ...
-    const int n_tiles = n_mine * G;
+    const int n_tiles = (n_all - split + n_parts - 1) / n_parts;
 
     const int col = lane & 31;
     const int half = lane >> 5;
@@ -520,9 +528,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
 
     auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
-        t = min(t, n_tiles - 1);
-        const int64_t bb = blist[split + kSplit * (t / G)];
-        const int64_t hh = g * G + t % G;
+        const int T = split + n_parts * min(t, n_tiles - 1);
+        const int64_t bb = blist[T / G];
+        const int64_t hh = g * G + T % G;
         return hh * n_q + bb * kC;
     };
     // Tile loader (all 256 threads): lane takes rows 4*kg .. 4*kg+3 of the
@@ -619,10 +627,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         }
         // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
         // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
-        const bool diag = split == 0 && (it / G) == 0;   // list entry 0 is the own block
+        const int entry = (split + n_parts * it) / G;    // list entry of this tile
+        const bool diag = entry == 0;                    // entry 0 is the own block
         // (group ids: this lane's key is dropped unless its group was chosen)
         const bool kept = kUnit == kC ||
-                          ((bmask[split + kSplit * (it / G)] >> ((32 * kh + col) >> 3)) & 1);
+                          ((bmask[entry] >> ((32 * kh + col) >> 3)) & 1);
         bf16x8 pb[2], dsb[2];
         bool big = false;
 #pragma unroll
