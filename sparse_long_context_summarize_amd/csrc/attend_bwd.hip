@@ -219,8 +219,12 @@ void bwd_dq_kernel(
     const int n_steps = 2 * n_pass;
     const bool kgrp = tid >= kDqThreads / 2;
 
-    const int hw = wave & 3, qt = wave >> 2;
-    const bool computes = hw < HW;
+    // (as in the forward: with HW < 4 the two query halves' waves sit on
+    // different SIMDs)
+    const int qt = wave >> 2;
+    const int lane4 = wave & 3;
+    const bool computes = lane4 / HW == qt % (4 / HW);
+    const int hw = lane4 % HW;                   // head slot
     const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
     const int half = lane >> 5;

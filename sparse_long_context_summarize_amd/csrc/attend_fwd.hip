@@ -204,11 +204,16 @@ void attend_fwd_kernel(
     const uint16_t *Kg = K + gkv * T_cap * kD;
     const uint16_t *Vg = V + gkv * T_cap * kD;
 
-    // Group A = waves 0-3, group B = waves 4-7: wave w computes head
-    // g*G + hg*HW + w%4 for queries 32*(w/4) .. +32 of the block.
+    // Group A = waves 0-3, group B = waves 4-7 (wave w runs on SIMD w % 4).
+    // Queries 32*qt .. +32 of the block go to group qt; within a group the
+    // waves of head slots 0 .. HW-1 compute (head g*G + hg*HW + slot). With
+    // HW < 4 the two groups use different waves (A the first HW, B the next
+    // HW), so their MFMA work lands on different SIMDs.
     const int grp = wave >> 2;
-    const int hw = wave & 3, qt = grp;
-    const bool computes = hw < HW;
+    const int qt = grp;
+    const int lane4 = wave & 3;
+    const bool computes = lane4 / HW == qt % (4 / HW);
+    const int hw = lane4 % HW;                   // head slot
     const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
     const int half = lane >> 5;
