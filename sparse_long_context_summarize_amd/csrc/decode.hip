@@ -15,7 +15,7 @@
 //                         over those keys, with the router's selection code.
 //   decode_partial_kernel split-K attention: the tiles of a (token, kv head)
 //                         -- sink chunks, routed chunks, the open chunk's
-//                         prefix -- are dealt kDecTiles at a time to
+//                         prefix -- are dealt kDecTiles (one) at a time to
 //                         n_split workgroups; each loads its tiles into LDS at
 //                         once, scores them on the vector ALUs (G query rows
 //                         are too few for the matrix cores) and writes, per
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void decode_select_kernel(
 }
 
 constexpr int kDecThreads = 256;
-constexpr int kDecTiles = 2;                // tiles per split workgroup
+constexpr int kDecTiles = 1;                // tiles per split workgroup
 constexpr int kDecStride = kD + 8;          // bf16 per LDS row (272 B)
 constexpr int kPartFloats = 2 + kD;         // max (log2 units), sum, output
 
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
 
 // One workgroup of kD threads per (token, query head): the splits' partials
 // merged in split order (every split's max and sum loaded at once first).
-constexpr int kMaxSplits = (kMaxSink + kMaxTopK + 1 + 1) / 2;
+constexpr int kMaxSplits = (kMaxSink + kMaxTopK + 1 + kDecTiles - 1) / kDecTiles;
 
 template <int G>
 __global__ __launch_bounds__(kD) void decode_combine_kernel(

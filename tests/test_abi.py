@@ -210,14 +210,15 @@ def test_decode_checks():
     cfg = _cfg(top_k=32)
     # router keys: one per candidate (chunks before the last token's open
     # chunk) per token and kv head; attention partials: 130 floats per split
-    # (two routed units a split) per token and query head; one size serves both
+    # (one tile of the token's list a split) per token and query head; one
+    # size serves both
     p0, n_q = 131071, 1
     keys = n_q * 8 * (p0 // 64) * 4
-    parts = n_q * 32 * ((32 + 1 + 1) // 2) * 130 * 4
+    parts = n_q * 32 * (32 + 1) * 130 * 4
     assert hga.hga_decode_workspace_bytes(cfg, p0, n_q) == max(keys, parts)
     assert hga.hga_decode_workspace_bytes(cfg, 100, 1) == parts
     assert hga.hga_decode_workspace_bytes(_cfg(top_k=32, sink_chunks=4), 64 * 10, 1) == \
-        1 * 32 * ((4 + 32 + 1 + 1) // 2) * 130 * 4
+        1 * 32 * (4 + 32 + 1) * 130 * 4
     assert hga.hga_decode_workspace_bytes(cfg, -1, 1) == 0
     assert hga.hga_decode_workspace_bytes(_cfg(head_dim=64), p0, 1) == 0
     need = hga.hga_decode_workspace_bytes(cfg, p0, n_q)
