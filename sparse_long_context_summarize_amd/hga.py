@@ -29,6 +29,7 @@ EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
             "hga_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
             "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
+HGA_MAX_SINK_CHUNKS = 64
 HGA_ROUTE_PER_KV_HEAD = 0
 HGA_ROUTE_PER_Q_HEAD = 1
 
