@@ -21,11 +21,12 @@
 //          are dealt round-robin to up to kSplit workgroups:
 //          S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
 //          Wave w owns keys 32*(w&1).. and queries 32*(w>>1).. of each query
-//          tile; the two query halves are summed through LDS. A chunk chosen
-//          by one block is written directly; otherwise every workgroup stores
-//          its partial sums and the last one to finish (a per-chunk counter)
-//          adds the partials in workgroup order and writes the result. This
-//          spreads the chunks that many blocks chose (routing concentrates on
+//          tile; the two query halves are summed through LDS. A chunk with
+//          at most kMinTiles tiles has one workgroup, which writes the result
+//          directly; a longer one is split, every workgroup stores its partial
+//          sums and the last one to finish (a per-chunk counter) adds the
+//          partials in workgroup order and writes the result. This spreads
+//          the chunks that many blocks chose (routing concentrates on
 //          high-scoring chunks) over several CUs.
 // Both kernels load their tiles two steps ahead into registers (two sets
 // used in a fixed order, steps run in pairs) and write them to double-buffered
