@@ -130,3 +130,38 @@ def test_decode_route_with_the_most_candidates(huge):
     torch.cuda.synchronize()
     ids_ref, sig = oracle.route_decode(Q, S_ref, p0, 32, 1, want_scores=True)
     check_ids(ids.cpu().numpy(), ids_ref, sig, p0, Bq=1, where="decode 24576 candidates")
+
+
+@pytest.mark.parametrize("gain", [6.0, 24.0])
+def test_peaked_softmax_forward_and_backward(gain):
+    """Queries scaled up: logits spread over tens of units, so the running max
+    keeps growing (rescales) and single keys take almost all the weight (the
+    backward's high/low split of large probabilities)."""
+    Hq, Hkv, D, T, n_q, k = 8, 2, 128, 1024, 256, 5
+    x = inputs.small_random(810 + int(gain), Hq, Hkv, D, T, n_q, bf16=True, with_dO=True)
+    x["Q"] = inputs.round_bf16(x["Q"] * np.float32(gain))
+    p0 = T - n_q
+    cfg = hga.make_config(Hq, Hkv, k)
+    Q, K, V = to_dev_bf16(x["Q"]), to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    S = torch.empty((Hkv, T // C, D), device="cuda")
+    hga.hga_summarize(cfg, K, 0, T, S)
+    ids = torch.empty((Hkv, n_q // C, k), dtype=torch.int32, device="cuda")
+    O = torch.empty((Hq, n_q, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, n_q), device="cuda")
+    hga.hga_route_attend_fwd(cfg, Q, K, V, p0, S, T // C, ids, O, lse)
+    dO = to_dev_bf16(x["dO"])
+    dQ = torch.empty((Hq, n_q, D), device="cuda")
+    dK = torch.empty((Hkv, n_q, D), device="cuda")
+    dV = torch.empty((Hkv, n_q, D), device="cuda")
+    ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg, n_q), dtype=torch.uint8,
+                     device="cuda")
+    hga.hga_attend_bwd(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, ws)
+    torch.cuda.synchronize()
+    g_ids = ids.cpu().numpy()
+    O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], g_ids, p0)
+    st = check_close(f"gain {gain} O", from_dev(O), O_ref)
+    check_close(f"gain {gain} lse", from_dev(lse), lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+    grads = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], g_ids, p0)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dQ, dK, dV), grads):
+        check_close(f"gain {gain} {name}", from_dev(got), ref)
+    log(f"gain {gain}: O {st}")
