@@ -29,9 +29,10 @@
 // double-buffered LDS tile one barrier before use. K rows are padded to 272 B
 // (conflict-free 16-byte operand reads); V^T rows to 144 B.
 //
-// Workgroup w serves kv head w % Hkv: with 8 kv heads every block of one head
-// runs on the same XCD, where neighbouring blocks' overlapping chunk choices
-// hit that XCD's L2.
+// Workgroups are dispatched with the kv head fastest (grid x), so workgroup w
+// serves kv head w % Hkv: with 8 kv heads every block of one head runs on the
+// same XCD, where neighbouring blocks' overlapping chunk choices hit that
+// XCD's L2.
 //
 // Per-query-head routing (one id row per query head) runs the G = 1 kernel
 // with kv_div = query heads per kv head: each query head is then its own
@@ -192,12 +193,15 @@ void attend_fwd_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
-    const int64_t rest0 = blockIdx.x / Hkv;
-    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id row
-    const int64_t rest = rest0 / kv_div;
-    const int hg = (int)(rest % NHG);
-    const int64_t b = rest / NHG;
+    // Grid (Hkv, kv_div * NHG, n_blocks): linear workgroup order runs over the
+    // kv heads fastest, and no index needs a division. y is the query head
+    // within its kv head's group (kv_div > 1, one id row per query head) or
+    // the workgroup's share of a G = 8 unit (NHG = 2); never both.
+    const int64_t gkv = blockIdx.x;                         // kv head
+    const int sub = (int)blockIdx.y;
+    const int64_t g = gkv * kv_div + (kv_div > 1 ? sub : 0);  // routing unit: its id row
+    const int hg = NHG > 1 ? sub : 0;
+    const int64_t b = blockIdx.z;
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
     const int64_t local_chunk = P / kC;
@@ -224,14 +228,33 @@ void attend_fwd_kernel(
     int32_t *id_row = ids + (g * n_blocks + b) * k;
     const int id_first = (kRouteNI == 0 && wave == 0 && lane < k) ? id_row[lane] : -1;
     // Q^T operand: lane holds Q[q = 32*qt + lane%32][d = 16*ks + 8*(lane/32) .. +8].
+    // With routing fused in and all G heads in this workgroup, the block's
+    // G*64 query rows are loaded whole (each load instruction reads four
+    // 256-B rows; piece p = row p/16, 16-byte segment p%16) into an LDS copy
+    // that both the router and the Q^T operands read; otherwise each wave
+    // loads its operand rows itself.
+    constexpr bool kQInLds = kRouteNI > 0 && NHG == 1;
+    constexpr int kQPieces = kQInLds ? G * kC * 16 / kThreads : 1;
     bf16x8 qf[8];
-    if (computes) {
+    u32x4 qraw[kQPieces];
+    if constexpr (kQInLds) {
+#pragma unroll
+        for (int j = 0; j < kQPieces; ++j) {
+            const int p = j * kThreads + tid, row = p >> 4, seg = p & 15;
+            qraw[j] = *(const u32x4 *)(Q + ((g * G + row / kC) * n_q + b * kC + row % kC) * kD +
+                                       seg * 8);
+        }
+    } else if (computes) {
         const uint16_t *qrow = Q + (h * n_q + b * kC + 32 * qt + col) * kD + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(qrow + 16 * ks);
     }
     TileRegs r0, r1;
-    if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
+    // (with routing fused in, the local tile is loaded behind the router's
+    // first summary rows instead: the query rows come first)
+    if (kRouteNI == 0) {
+        if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
+    }
 
     // Unit list: the local chunk, the sink window's units, then the valid
     // routed ids (past the sink, before P) in order, repeats dropped.
@@ -261,14 +284,18 @@ void attend_fwd_kernel(
         RouteLds &sh = *reinterpret_cast<RouteLds *>(&Vs[0][0]);
         uint32_t *keys = reinterpret_cast<uint32_t *>(&Ks[0][0]);
         uint16_t *qcopy = &Os[0][0];                // row r = head hw*64 + query
-        constexpr bool kQInLds = NHG == 1;
         if constexpr (kQInLds) {
-            if (computes) {
-                uint16_t *dst = qcopy + (hw * kC + 32 * qt + col) * kOStride + 8 * half;
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) *(bf16x8 *)(dst + 16 * ks) = qf[ks];
+            for (int j = 0; j < kQPieces; ++j) {
+                const int p = j * kThreads + tid, row = p >> 4, seg = p & 15;
+                *(u32x4 *)(qcopy + row * kOStride + seg * 8) = qraw[j];
             }
             __syncthreads();
+            if (computes) {
+                const uint16_t *src = qcopy + (hw * kC + 32 * qt + col) * kOStride + 8 * half;
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8 *)(src + 16 * ks);
+            }
         }
         auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {
             if constexpr (kQInLds) {
@@ -290,7 +317,11 @@ void attend_fwd_kernel(
                     id_row[r] = id;
                     if (sc_row) sc_row[r] = sc;
                 }
-            });
+            },
+            [&]() __attribute__((always_inline)) {
+                if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
+            },
+            std::integral_constant<bool, kQInLds>{});
         if (wave == 0) {
             write_sink_units(list + 1, n_sink);
             if (lane == 0) {
@@ -566,8 +597,10 @@ hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
     const int64_t n_blocks = a.n_q / kC;
     const float scale_log2 = a.scale * 1.44269504088896340736f;
     const int kv_div = a.per_q_head ? (int)(a.Hq / a.Hkv) : 1;
+    if (n_blocks > 65535) return hipErrorInvalidConfiguration;     // grid z limit
     hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit, kRouteNI>),
-                       dim3((unsigned)(n_blocks * a.Hkv * kv_div * NHG)), dim3(kThreads), 0,
+                       dim3((unsigned)a.Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
+                       dim3(kThreads), 0,
                        stream, a.Q, a.K, a.V, a.n_q, a.Hkv, kv_div, a.T_cap, a.p0, a.ids, a.k,
                        (int)a.sink, scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
     return hipGetLastError();

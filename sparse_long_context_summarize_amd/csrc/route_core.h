@@ -24,6 +24,8 @@
 #pragma once
 #include "hga_internal.h"
 
+#include <type_traits>
+
 namespace hga {
 namespace {
 
@@ -130,6 +132,23 @@ __device__ __forceinline__ float key_to_score(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// Max and min over the wave, the two reductions interleaved (independent
+// chains hide each other's DPP wait states); every lane receives both.
+__device__ __forceinline__ void wave_max_min_u32(uint32_t &mx, uint32_t &mn) {
+    mx = max(mx, dpp_u32<0xB1>(mx)); mn = min(mn, dpp_u32<0xB1>(mn));
+    mx = max(mx, dpp_u32<0x4E>(mx)); mn = min(mn, dpp_u32<0x4E>(mn));
+    mx = max(mx, dpp_u32<0x141>(mx)); mn = min(mn, dpp_u32<0x141>(mn));
+    mx = max(mx, dpp_u32<0x140>(mx)); mn = min(mn, dpp_u32<0x140>(mn));
+    const auto r = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+    const auto r2 = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+    mx = max((uint32_t)r[0], (uint32_t)r[1]);
+    mn = min((uint32_t)r2[0], (uint32_t)r2[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    const auto q2 = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+    mx = max((uint32_t)q[0], (uint32_t)q[1]);
+    mn = min((uint32_t)q2[0], (uint32_t)q2[1]);
+}
+
 // Wave-level top-k of keys[0..nE) (LDS), nE <= NI*64, by (key desc, candidate
 // index asc): one wave holds every key in registers (candidate c = it*64 +
 // lane), finds the k-th largest key bit by bit from ballot counts (stopping
@@ -167,10 +186,11 @@ __device__ __forceinline__ int select_top_k_reg(const uint32_t *keys, int nE, in
             mx = max(mx, key[it]);
             mn = min(mn, key[it] ? key[it] : 0xFFFFFFFFu);
         }
+        wave_max_min_u32(mx, mn);
         // (every lane holds the same max and min: readfirstlane lets the
         // threshold search run in scalar registers)
-        mx = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(mx));
-        mn = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(mn));
+        mx = (uint32_t)__builtin_amdgcn_readfirstlane((int)mx);
+        mn = (uint32_t)__builtin_amdgcn_readfirstlane((int)mn);
         // Bits above the highest bit in which the keys differ are shared.
         const uint32_t diff = mx ^ mn;
         const int top = diff ? 31 - __builtin_clz(diff) : -1;
@@ -248,6 +268,11 @@ __device__ __forceinline__ int sorted_chunk_set(const int32_t *row, int k, int64
     return n;
 }
 
+// No extra work (route_block's default hook).
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
 // LDS the router uses besides the candidate keys.
 struct RouteLds {
     float part[16][kD];
@@ -285,12 +310,17 @@ struct RouteLds {
 // b is the single token at p0 + b, and its candidates end at the start of its
 // own open chunk, P = 64*floor((p0 + b)/64).
 template <int G, int NI, bool kGroups, int kBatch, int kScoreWaves, typename QRow,
-          typename Emit, int kBq = kC>
+          typename Emit, int kBq = kC, typename Hook = NoHook, typename QLocal = std::false_type>
 __device__ __forceinline__ int route_block(
     RouteLds &sh, uint32_t *keys, QRow q_row, int64_t n_q, int64_t g,
     int64_t b, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
-    const int32_t *__restrict__ chunk_ids, int kc, int c_lo, Emit emit)
+    const int32_t *__restrict__ chunk_ids, int kc, int c_lo, Emit emit,
+    Hook after_loads = Hook{}, QLocal = QLocal{})
 {
+    // q_row reads LDS (QLocal true): the query-row sums come first and the
+    // summary rows are loaded after them; reading memory, both loads go out
+    // first so that their round trips overlap.
+    constexpr bool kQLocal = QLocal::value;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // (uniform across the wave: readfirstlane lets every wave-level branch
@@ -349,7 +379,8 @@ __device__ __forceinline__ int route_block(
                 w[m] = (r0 + 16 * m < kRows) ? q_row(r0 + 16 * m, dseg) : z;
             }
         }
-        if (wave * 4 < nE) load_batch(wave * 4);
+        // (clamped: waves past the end re-read the last row)
+        if (!kQLocal && nE > 0) load_batch(wave * 4);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -362,9 +393,11 @@ __device__ __forceinline__ int route_block(
             }
 #pragma unroll
         for (int e = 0; e < 8; ++e) sh.part[r0][dseg * 8 + e] = acc[e];
+        if (kQLocal && nE > 0) load_batch(wave * 4);
     } else if (scorer) {
-        if (wave * 4 < nE) load_batch(wave * 4);
+        if (nE > 0) load_batch(wave * 4);       // (clamped: waves past the end re-read the last row)
     }
+    after_loads();      // the caller's own loads, issued behind the summary rows
     __syncthreads();
     if (tid < kD) {
         float s = 0.f;
