@@ -15,11 +15,11 @@ namespace {
 
 __global__ __launch_bounds__(256) void summarize_kernel(
     const uint16_t *__restrict__ K, int64_t T_cap, int64_t c_begin,
-    int64_t n_chunks, float *__restrict__ S, int64_t n_cap)
+    float *__restrict__ S, int64_t n_cap)
 {
     __shared__ float part[4][kD];
-    const int64_t g = blockIdx.x / n_chunks;
-    const int64_t c = c_begin + blockIdx.x % n_chunks;
+    const int64_t g = blockIdx.y;                   // grid (chunks, kv heads)
+    const int64_t c = c_begin + blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int dseg = lane & 15;          // d = 8*dseg .. 8*dseg+7
@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void summarize_kernel(
 // eight groups of the chunk with no LDS pass.
 __global__ __launch_bounds__(256) void summarize_groups_kernel(
     const uint16_t *__restrict__ K, int64_t T_cap, int64_t c_begin,
-    int64_t n_chunks, float *__restrict__ SG, int64_t n_gcap)
+    float *__restrict__ SG, int64_t n_gcap)
 {
-    const int64_t g = blockIdx.x / n_chunks;
-    const int64_t c = c_begin + blockIdx.x % n_chunks;
+    const int64_t g = blockIdx.y;                   // grid (chunks, kv heads)
+    const int64_t c = c_begin + blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int dseg = lane & 15;
@@ -121,10 +121,10 @@ hipError_t launch_summarize_groups(const uint16_t *K, int64_t Hkv, int64_t T_cap
                                    int64_t n_gcap, hipStream_t stream)
 {
     const int64_t n_chunks = c_end - c_begin;
-    const int64_t n_units = Hkv * n_chunks;
-    if (n_units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(summarize_groups_kernel, dim3((unsigned)n_units), dim3(256), 0, stream,
-                       K, T_cap, c_begin, n_chunks, SG, n_gcap);
+    if (Hkv * n_chunks <= 0) return hipSuccess;
+    if (Hkv > 65535) return hipErrorInvalidConfiguration;      // grid y limit
+    hipLaunchKernelGGL(summarize_groups_kernel, dim3((unsigned)n_chunks, (unsigned)Hkv), dim3(256),
+                       0, stream, K, T_cap, c_begin, SG, n_gcap);
     return hipGetLastError();
 }
 
@@ -133,10 +133,10 @@ hipError_t launch_summarize(const uint16_t *K, int64_t Hkv, int64_t T_cap,
                             int64_t n_cap, hipStream_t stream)
 {
     const int64_t n_chunks = c_end - c_begin;
-    const int64_t n_units = Hkv * n_chunks;
-    if (n_units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(summarize_kernel, dim3((unsigned)n_units), dim3(256), 0, stream,
-                       K, T_cap, c_begin, n_chunks, S, n_cap);
+    if (Hkv * n_chunks <= 0) return hipSuccess;
+    if (Hkv > 65535) return hipErrorInvalidConfiguration;      // grid y limit
+    hipLaunchKernelGGL(summarize_kernel, dim3((unsigned)n_chunks, (unsigned)Hkv), dim3(256), 0,
+                       stream, K, T_cap, c_begin, S, n_cap);
     return hipGetLastError();
 }
 
