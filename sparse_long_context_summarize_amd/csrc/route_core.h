@@ -6,7 +6,8 @@
 // chunks).
 //
 //   1. qbar = mean of the block's G*64 query rows (fp32, LDS reduction); the
-//      first batch of summary rows is loaded together with the query rows;
+//      first batch of summary rows is loaded together with the query rows
+//      (or, when the caller holds the rows in LDS, right after their sums);
 //   2. score_c = qbar . S[g][c] for every candidate c: 16 lanes per chunk
 //      read one 512-byte summary row with coalesced 16-byte loads, each lane
 //      holding its 8-wide slice of qbar in registers; the 16 partial sums are
