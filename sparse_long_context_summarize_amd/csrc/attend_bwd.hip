@@ -182,12 +182,13 @@ void bwd_dq_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
-    const int64_t rest0 = blockIdx.x / Hkv;
-    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id row
-    const int64_t rest = rest0 / kv_div;
-    const int hg = (int)(rest % NHG);
-    const int64_t b = rest / NHG;
+    // grid (Hkv, kv_div * NHG, blocks): y is the query head within its kv
+    // head's group (kv_div > 1) or the workgroup's share of a G = 8 unit
+    const int64_t gkv = blockIdx.x;                         // kv head
+    const int sub = (int)blockIdx.y;
+    const int64_t g = gkv * kv_div + (kv_div > 1 ? sub : 0);  // routing unit: its id row
+    const int hg = NHG > 1 ? sub : 0;
+    const int64_t b = blockIdx.z;
     const int64_t n_blocks = n_q / kC;
     const int64_t P = p0 + b * kC;
     const int64_t local_chunk = P / kC;
@@ -439,12 +440,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t gkv = blockIdx.x % Hkv;                   // kv head
-    const int64_t rest0 = blockIdx.x / Hkv;
-    const int64_t g = gkv * kv_div + rest0 % kv_div;        // routing unit: its id rows
-    const int64_t rest = rest0 / kv_div;
-    const int split = (int)(rest % kSplit);
-    const int64_t a = rest / kSplit;             // active chunk = its own query block
+    // grid (Hkv, kv_div, blocks * kSplit)
+    const int64_t gkv = blockIdx.x;                         // kv head
+    const int64_t g = gkv * kv_div + blockIdx.y;            // routing unit: its id rows
+    const int split = (int)(blockIdx.z % kSplit);
+    const int64_t a = blockIdx.z / kSplit;       // active chunk = its own query block
     const int64_t n_blocks = n_q / kC;
     const int64_t ca = p0 / kC + a;               // absolute chunk index
 
@@ -821,14 +821,17 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
+    if (n_blocks * kSplit > 65535) return hipErrorInvalidConfiguration;     // grid z limit
     hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>),
-                       dim3((unsigned)(n_blocks * Hkv * kv_div * NHG)), dim3(kDqThreads), 0,
+                       dim3((unsigned)Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
+                       dim3(kDqThreads), 0,
                        stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, kv_div, T_cap, p0,
                        ids, k, (int)sink, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>),
-                       dim3((unsigned)(n_blocks * Hkv * kv_div * kSplit)), dim3(kThreads), 0,
+                       dim3((unsigned)Hkv, (unsigned)kv_div, (unsigned)(n_blocks * kSplit)),
+                       dim3(kThreads), 0,
                        stream, Q, K, V, dO, lse, delta, n_q, Hkv, kv_div, T_cap, p0, ids, k,
                        (int)sink, scale_log2, scale, dK, dV, part, counters);
     return hipGetLastError();

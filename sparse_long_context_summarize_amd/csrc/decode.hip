@@ -48,10 +48,9 @@ __global__ __launch_bounds__(kRouteThreads) void decode_score_kernel(
     __shared__ float qbar[kD];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
-    const int blk = (int)(rest % n_blk);
-    const int64_t i = rest / n_blk;
+    const int64_t g = blockIdx.x;                   // grid (Hkv, n_blk, n_q)
+    const int blk = (int)blockIdx.y;
+    const int64_t i = blockIdx.z;
     const int nE = decode_candidates(p0 + i, sink);
     const int c0 = blk * kScoreBlock;
     if (c0 >= nE) return;                       // uniform across the workgroup
@@ -122,8 +121,8 @@ __global__ __launch_bounds__(kSelWaves * 64) void decode_select_kernel(
     __shared__ int cand_pos[kSelWaves * kMaxTopK];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t i = blockIdx.x / Hkv;
+    const int64_t g = blockIdx.x;                   // grid (Hkv, n_q)
+    const int64_t i = blockIdx.y;
     const int nE = decode_candidates(p0 + i, sink);
     const uint32_t *kin = keys + (i * Hkv + g) * kcap;
     int32_t *out = ids + (g * n_q + i) * k;
@@ -182,10 +181,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(
     __shared__ float ps[4][HPW][kC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t g = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
-    const int j = (int)(rest % n_split);
-    const int64_t i = rest / n_split;
+    const int64_t g = blockIdx.x;                   // grid (Hkv, n_split, n_q)
+    const int j = (int)blockIdx.y;
+    const int64_t i = blockIdx.z;
     const int64_t p = p0 + i;
     const int64_t Pc = kC * (p / kC);           // start of the open chunk
     if (wave == 0) {
@@ -309,8 +307,8 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(
     __shared__ float ms[kMaxSplits], ws[kMaxSplits];
     __shared__ float M_s, L_s;
     const int d = threadIdx.x;
-    const int64_t h = blockIdx.x % (Hkv * G);
-    const int64_t i = blockIdx.x / (Hkv * G);
+    const int64_t h = blockIdx.x;                   // grid (Hkv * G, n_q)
+    const int64_t i = blockIdx.y;
     const int64_t g = h / G, hh = h % G;
     const float *base = part + ((i * Hkv + g) * n_split * G + hh) * kPartFloats;
     const int64_t step = (int64_t)G * kPartFloats;
@@ -346,15 +344,17 @@ hipError_t launch_route_decode_g(const uint16_t *Q, int64_t Hkv, int64_t p0, int
                                  hipStream_t stream)
 {
     const int64_t kcap = decode_key_capacity(p0, n_q, sink);
+    if (n_q > 65535) return hipErrorInvalidConfiguration;      // grid y / z limit
     if (kcap > 0) {
         const int n_blk = (int)((kcap + kScoreBlock - 1) / kScoreBlock);
-        hipLaunchKernelGGL((decode_score_kernel<G>), dim3((unsigned)(n_q * Hkv * n_blk)),
+        hipLaunchKernelGGL((decode_score_kernel<G>),
+                           dim3((unsigned)Hkv, (unsigned)n_blk, (unsigned)n_q),
                            dim3(kRouteThreads), 0, stream, Q, n_q, Hkv, p0, S, n_cap,
                            (int)sink, n_blk, kcap, keys);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 grid((unsigned)(n_q * Hkv)), block(kSelWaves * 64);
+    const dim3 grid((unsigned)Hkv, (unsigned)n_q), block(kSelWaves * 64);
 #define HGA_SELECT_DEC(NI)                                                                  \
     hipLaunchKernelGGL((decode_select_kernel<NI>), grid, block, 0, stream, n_q, Hkv, p0, k,  \
                        (int)sink, kcap, keys, ids, scores)
@@ -377,13 +377,15 @@ hipError_t launch_attend_decode_g(const uint16_t *Q, const uint16_t *K, const ui
                                   float *lse, float *part, hipStream_t stream)
 {
     const int n_split = decode_splits(k, sink);
-    hipLaunchKernelGGL((decode_partial_kernel<G>), dim3((unsigned)(n_q * Hkv * n_split)),
+    if (n_q > 65535) return hipErrorInvalidConfiguration;      // grid y / z limit
+    hipLaunchKernelGGL((decode_partial_kernel<G>),
+                       dim3((unsigned)Hkv, (unsigned)n_split, (unsigned)n_q),
                        dim3(kDecThreads), 0, stream, Q, K, V, n_q, Hkv, T_cap, p0, ids, k,
                        (int)sink, scale * 1.44269504088896340736f, n_split, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<G>), dim3((unsigned)(n_q * Hkv * G)), dim3(kD), 0,
-                       stream, part, n_q, Hkv, n_split, O, lse);
+    hipLaunchKernelGGL((decode_combine_kernel<G>), dim3((unsigned)(Hkv * G), (unsigned)n_q),
+                       dim3(kD), 0, stream, part, n_q, Hkv, n_split, O, lse);
     return hipGetLastError();
 }
 

@@ -26,10 +26,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 {
     extern __shared__ uint32_t keys[];          // [candidates of this block]
     __shared__ RouteLds sh;
-    const int64_t gkv = blockIdx.x % Hkv;
-    const int64_t rest = blockIdx.x / Hkv;
-    const int64_t u = gkv * kv_div + rest % kv_div;     // routing unit
-    const int64_t b = rest / kv_div;
+    const int64_t gkv = blockIdx.x;                     // grid (Hkv, kv_div, blocks)
+    const int64_t u = gkv * kv_div + blockIdx.y;        // routing unit
+    const int64_t b = blockIdx.z;
     int32_t *out = ids + (u * (n_q / kC) + b) * k;
     float *sout = scores ? scores + (u * (n_q / kC) + b) * k : nullptr;
     auto q_row = [&](int row, int dseg) __attribute__((always_inline)) {
@@ -75,8 +74,10 @@ hipError_t launch_route_gn(const RouteArgs &a, size_t shmem, hipStream_t stream)
 {
     const int64_t n_blocks = a.n_q / kC;
     const int kv_div = a.per_q_head ? (int)(a.Hq / a.Hkv) : 1;
+    if (n_blocks > 65535) return hipErrorInvalidConfiguration;     // grid z limit
     hipLaunchKernelGGL((route_kernel<G, NI, kGroups, kPrev>),
-                       dim3((unsigned)(n_blocks * a.Hkv * kv_div)), dim3(kRouteThreads), shmem,
+                       dim3((unsigned)a.Hkv, (unsigned)kv_div, (unsigned)n_blocks),
+                       dim3(kRouteThreads), shmem,
                        stream, a.Q, a.Q_prev, a.n_q, a.Hkv, kv_div, a.p0, a.S, a.n_cap, a.k,
                        a.chunk_ids, a.kc, (int)a.sink, a.ids, a.scores);
     return hipGetLastError();
