@@ -167,7 +167,7 @@ void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
-    int64_t n_q, int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0,
+    int64_t n_q, int kv_div, int64_t T_cap, int64_t p0,
     const int32_t *__restrict__ ids, int k, int sink, float scale_log2, float scale,
     float *__restrict__ dQ)
 {
@@ -825,7 +825,7 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>),
                        dim3((unsigned)Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
                        dim3(kDqThreads), 0,
-                       stream, Q, K, V, dO, lse, delta, counters, n_q, Hkv, kv_div, T_cap, p0,
+                       stream, Q, K, V, dO, lse, delta, counters, n_q, kv_div, T_cap, p0,
                        ids, k, (int)sink, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

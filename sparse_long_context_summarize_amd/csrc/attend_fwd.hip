@@ -176,7 +176,7 @@ template <int G, int kUnit, int kRouteNI>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, int64_t n_q, int64_t Hkv, int kv_div, int64_t T_cap,
+    const uint16_t *__restrict__ V, int64_t n_q, int kv_div, int64_t T_cap,
     int64_t p0, int32_t *__restrict__ ids, int k, int sink, float scale_log2,
     uint16_t *__restrict__ O, float *__restrict__ lse,
     const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores)
@@ -601,7 +601,7 @@ hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
     hipLaunchKernelGGL((attend_fwd_kernel<G, kUnit, kRouteNI>),
                        dim3((unsigned)a.Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
                        dim3(kThreads), 0,
-                       stream, a.Q, a.K, a.V, a.n_q, a.Hkv, kv_div, a.T_cap, a.p0, a.ids, a.k,
+                       stream, a.Q, a.K, a.V, a.n_q, kv_div, a.T_cap, a.p0, a.ids, a.k,
                        (int)a.sink, scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
     return hipGetLastError();
 }

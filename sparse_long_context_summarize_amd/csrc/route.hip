@@ -20,7 +20,7 @@ namespace {
 template <int G, int NI, bool kGroups, bool kPrev>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Q_prev, int64_t n_q,
-    int64_t Hkv, int kv_div, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
+    int kv_div, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
     const int32_t *__restrict__ chunk_ids, int kc, int c_lo,
     int32_t *__restrict__ ids, float *__restrict__ scores)
 {
@@ -78,7 +78,7 @@ hipError_t launch_route_gn(const RouteArgs &a, size_t shmem, hipStream_t stream)
     hipLaunchKernelGGL((route_kernel<G, NI, kGroups, kPrev>),
                        dim3((unsigned)a.Hkv, (unsigned)kv_div, (unsigned)n_blocks),
                        dim3(kRouteThreads), shmem,
-                       stream, a.Q, a.Q_prev, a.n_q, a.Hkv, kv_div, a.p0, a.S, a.n_cap, a.k,
+                       stream, a.Q, a.Q_prev, a.n_q, kv_div, a.p0, a.S, a.n_cap, a.k,
                        a.chunk_ids, a.kc, (int)a.sink, a.ids, a.scores);
     return hipGetLastError();
 }

@@ -76,7 +76,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 // Wave-level selection of the k largest keys[0..n) (ties: lower position
 // first). Writes the chosen positions, ascending, to out_pos (LDS) and
 // returns their number, min(k, n). Every lane of the wave must call it.
-__device__ int wave_select(const uint32_t *keys, int n, int k, int *out_pos)
+__device__ __forceinline__ int wave_select(const uint32_t *keys, int n, int k, int *out_pos)
 {
     const int lane = threadIdx.x & 63;
     if (n <= k) {
