@@ -56,7 +56,7 @@ typedef enum hga_dtype { HGA_BF16 = 0 } hga_dtype;
 
 typedef struct hga_config {
     int32_t n_q_heads;      /* Hq; a multiple of n_kv_heads                    */
-    int32_t n_kv_heads;     /* Hkv; G = Hq / Hkv must be 1, 2, 4 or 8          */
+    int32_t n_kv_heads;     /* Hkv <= 65535; G = Hq / Hkv must be 1, 2, 4 or 8 */
     int32_t head_dim;       /* D; must be 128                                  */
     int32_t chunk;          /* C; must be 64 (the pages' example chunk length) */
     int32_t q_block;        /* Bq; must equal chunk                            */
@@ -180,7 +180,8 @@ hga_status hga_route_causal(const hga_config *cfg, const void *Q, const void *Q_
  * de-duplication work).
  *   Q, O   device bf16 [Hq][n_q][D];   K, V device bf16 [Hkv][T_cap][D]
  *   ids    device int32 [U][n_q/Bq][k] (U as for hga_route); lse device f32 [Hq][n_q]
- *   p0     multiple of C; n_q multiple of Bq; p0 + n_q <= T_cap
+ *   p0     multiple of C; n_q multiple of Bq; p0 + n_q <= T_cap; at most 65535
+ *          query blocks per call (HGA_ERR_UNSUPPORTED)
  */
 hga_status hga_attend_fwd(const hga_config *cfg, const void *Q, const void *K,
                           const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
@@ -332,7 +333,8 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
  * candidates the chunks s <= c < Pc/C (s = cfg->sink_chunks), and
  * ids[g][i][:] the min(k, Pc/C - s) of highest score, ties to the lower id,
  * ascending, then -1.
- *   Q        device bf16 [Hq][n_q][D]
+ *   Q        device bf16 [Hq][n_q][D]; at most 65535 tokens per call
+ *            (HGA_ERR_UNSUPPORTED)
  *   ids      device int32 [Hkv][n_q][k];  scores_or_null as for hga_route
  *   summaries: (p0 + n_q - 1)/C <= n_chunks_valid <= n_chunk_cap, else
  *            HGA_ERR_CAPACITY

@@ -36,6 +36,9 @@ hga_status check_config(const hga_config *cfg)
     if (cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0)
         return fail(HGA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d, Hkv=%d)",
                     cfg->n_q_heads, cfg->n_kv_heads);
+    if (cfg->n_kv_heads > 65535)
+        return fail(HGA_ERR_UNSUPPORTED, "n_kv_heads must be at most 65535 (got %d)",
+                    cfg->n_kv_heads);
     if (cfg->n_q_heads % cfg->n_kv_heads != 0)
         return fail(HGA_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
                     cfg->n_q_heads, cfg->n_kv_heads);
@@ -97,8 +100,9 @@ hga_status check_segment(int64_t p0, int64_t n_q, int64_t T_cap, bool need_T)
     if (need_T && p0 + n_q > T_cap)
         return fail(HGA_ERR_INVALID_ARG, "p0 + n_q (%lld) exceeds T_cap (%lld)",
                     (long long)(p0 + n_q), (long long)T_cap);
-    if (n_q / hga::kC > (int64_t)INT32_MAX / 64)
-        return fail(HGA_ERR_UNSUPPORTED, "n_q too large");
+    if (n_q / hga::kC > 65535)      // one launch's grid holds the query blocks
+        return fail(HGA_ERR_UNSUPPORTED, "n_q (%lld) exceeds 65535 query blocks of %d",
+                    (long long)n_q, hga::kC);
     return HGA_OK;
 }
 
@@ -413,6 +417,8 @@ hga_status hga_route_decode(const hga_config *cfg, const void *Q, int64_t p0, in
     if (st != HGA_OK) return st;
     if (p0 < 0 || n_q < 0 || n_chunks_valid < 0 || n_chunk_cap < 0)
         return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
+    if (n_q > 65535)
+        return fail(HGA_ERR_UNSUPPORTED, "at most 65535 tokens per call (got %lld)", (long long)n_q);
     if (n_chunks_valid > n_chunk_cap)
         return fail(HGA_ERR_CAPACITY, "n_chunks_valid (%lld) exceeds n_chunk_cap (%lld)",
                     (long long)n_chunks_valid, (long long)n_chunk_cap);
@@ -457,6 +463,8 @@ hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K
     if (st != HGA_OK) return st;
     if (p0 < 0 || n_q < 0 || T_cap < 0)
         return fail(HGA_ERR_INVALID_ARG, "negative position, count or capacity");
+    if (n_q > 65535)
+        return fail(HGA_ERR_UNSUPPORTED, "at most 65535 tokens per call (got %lld)", (long long)n_q);
     if (p0 + n_q > T_cap)
         return fail(HGA_ERR_INVALID_ARG, "p0 + n_q (%lld) exceeds T_cap (%lld)",
                     (long long)(p0 + n_q), (long long)T_cap);

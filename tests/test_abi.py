@@ -242,6 +242,26 @@ def test_decode_checks():
     assert attend(need, T=p0) == hga.HGA_ERR_INVALID_ARG
 
 
+def test_grid_limits():
+    """Sizes past what one launch's grid holds are refused before any launch:
+    more than 65535 query blocks, more than 65535 decode tokens, more than
+    65535 kv heads."""
+    L = hga.lib()
+    cfg = _cfg()
+    n_big = 65536 * 64
+    assert _fwd(cfg, p0=0, n_q=n_big, T=n_big) == hga.HGA_ERR_UNSUPPORTED
+    assert "65535 query blocks" in hga.hga_last_error()
+    assert _fwd(_cfg(n_q_heads=65536, n_kv_heads=65536)) == hga.HGA_ERR_UNSUPPORTED
+    assert "n_kv_heads" in hga.hga_last_error()
+    p0, n_q = 64 * 100, 65536
+    assert L.hga_route_decode(ctypes.byref(cfg), FAKE, p0, n_q, FAKE, 4096, 4096, FAKE, None,
+                              FAKE, 1 << 40, None) == hga.HGA_ERR_UNSUPPORTED
+    assert "tokens per call" in hga.hga_last_error()
+    assert L.hga_attend_decode(ctypes.byref(cfg), FAKE, FAKE, FAKE, p0 + n_q, p0, n_q, FAKE,
+                               FAKE, FAKE, FAKE, 1 << 40, None) == hga.HGA_ERR_UNSUPPORTED
+    assert "tokens per call" in hga.hga_last_error()
+
+
 def test_routing_variant_checks():
     L = hga.lib()
     bad = _cfg(route_heads=2)
