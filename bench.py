@@ -43,8 +43,8 @@ C = 64
 # recorded; for any other source the traffic is reported as null.
 MEASURED_TRAFFIC = {"sources": ["sparse_long_context_summarize_amd/csrc/attend_fwd.hip",
                                 "sparse_long_context_summarize_amd/csrc/route_core.h"],
-                    "sha256_prefix": "e10638db418bf996",
-                    "fetch_kib": 30419.9, "fetch_factor": 2.0,
+                    "sha256_prefix": "66dda4241221b5ba",
+                    "fetch_kib": 30427.7, "fetch_factor": 2.0,
                     "write_kib": 16656.0, "write_factor": 1.0}
 
 
@@ -481,6 +481,17 @@ def group_timings(torch, hga, inputs, dev):
         for fn in calls.values():
             fn()
 
+    # both routing levels and the group attention in one call
+    fused = hga.prepare("hga_route_attend_fwd_groups", cfg, Q, K, V, w.p0, S, w.T // C, SG, ids,
+                        gids, O, lse)
+    fused()
+    res["groups16k_route_attend_fwd_groups_us"] = _median_ms(torch, fused) * 1e3
+
+    def layer_fused():
+        calls["summarize"]()
+        calls["summarize_groups"]()
+        fused()
+
     # backward of the group attention at the same layer (dO ~ N(0, 1))
     dO = up(np.random.default_rng(5).standard_normal((w.Hq, w.n_q, w.D), dtype=np.float32))
     dQ = torch.empty((w.Hq, w.n_q, w.D), device=dev)
@@ -492,6 +503,7 @@ def group_timings(torch, hga, inputs, dev):
                       dV, ws)
 
     ms = _median_ms(torch, layer)
+    ms_fused = _median_ms(torch, layer_fused)
     ms_bwd = _median_ms(torch, bwd)
     g = gids.cpu().numpy()
     fl_bwd = bwd_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
@@ -501,6 +513,8 @@ def group_timings(torch, hga, inputs, dev):
     res.update({
         "groups16k_layer_fwd_us": ms * 1e3,
         "groups16k_query_tokens_per_s": w.n_q / (ms * 1e-3),
+        "groups16k_fused_layer_fwd_us": ms_fused * 1e3,
+        "groups16k_fused_query_tokens_per_s": w.n_q / (ms_fused * 1e-3),
         "groups16k_group_top_k": w.m,
         "groups16k_attend_algorithmic_gflop": fl / 1e9,
         "groups16k_attend_tflops": fl / t_att / 1e12,

@@ -304,6 +304,33 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
                                  float *lse, hipStream_t stream);
 
 /*
+ * hga_route_attend_fwd_groups -- both routing levels and the group attention
+ * of one segment (gist.science technical summary 2.1: chunks first, then the
+ * 8-token groups inside them): the outputs of hga_route (chunk_ids; no chunk
+ * scores), hga_route_groups (group_ids, scores_or_null) and
+ * hga_attend_fwd_groups (O, lse) on the same inputs, bit for bit. With
+ * 0 < cfg->top_k <= 32, group_top_k > 0 and at most 8704 candidate chunks per
+ * block it is one launch: each workgroup routes its block at both levels and
+ * then attends; otherwise the three kernels run in turn. Per-kv-head routing
+ * only (HGA_ERR_UNSUPPORTED otherwise).
+ *   summaries, n_chunk_cap, n_chunks_valid   as for hga_route_attend_fwd
+ *   group_summaries, n_group_cap, group_top_k as for hga_route_groups
+ *   chunk_ids   device int32 [Hkv][n_q/Bq][cfg->top_k], written (needed when
+ *               cfg->top_k > 0)
+ *   group_ids   device int32 [Hkv][n_q/Bq][group_top_k], written;
+ *               group_scores_or_null as hga_route_groups' scores_or_null
+ *   Q, K, V, O, lse, T_cap, p0, n_q as for hga_attend_fwd
+ */
+hga_status hga_route_attend_fwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                       const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                       const float *summaries, int64_t n_chunk_cap,
+                                       int64_t n_chunks_valid, const float *group_summaries,
+                                       int64_t n_group_cap, int32_t group_top_k,
+                                       int32_t *chunk_ids, int32_t *group_ids,
+                                       float *group_scores_or_null, void *O, float *lse,
+                                       hipStream_t stream);
+
+/*
  * hga_attend_bwd_groups -- hga_attend_bwd for hga_attend_fwd_groups: the same
  * gradients (dQ of every active query; dK, dV of the active keys, summed over
  * the G heads; history detached) with A(i) built from group_ids as in

@@ -167,11 +167,14 @@ __device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vt, int dt, int ks,
 // ids are 8-token group ids (the second routing level); each routed tile is
 // gathered from 8 groups, and the last one masks the keys of its missing
 // groups when their number is not a multiple of 8.
-// kRouteNI = 0: ids are an input. kRouteNI > 0 (chunk tiles only): the
-// workgroup first routes its block itself with the router's own code
-// (route_block, NI = kRouteNI keys per lane), writes ids (and scores, if not
-// null) exactly as the routing kernel would, and attends over that choice;
-// S / n_cap are the chunk summaries.
+// kRouteNI = 0: ids are an input. kRouteNI > 0: the workgroup first routes
+// its block itself with the router's own code (route_block, NI = kRouteNI
+// keys per lane for the chunk candidates), writes ids (and scores, if not
+// null) exactly as the routing kernels would, and attends over that choice;
+// S / n_cap are the chunk summaries. For group tiles the routing has two
+// levels: the block's kc chunks (written to chunk_ids_out), then m = k groups
+// among those chunks' groups against the group summaries SG / n_gcap (at most
+// kFusedGroupChunks chunks, so 4 keys per lane hold every group candidate).
 template <int G, int kUnit, int kRouteNI>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attend_fwd_kernel(
@@ -179,9 +182,11 @@ void attend_fwd_kernel(
     const uint16_t *__restrict__ V, int64_t n_q, int kv_div, int64_t T_cap,
     int64_t p0, int32_t *__restrict__ ids, int k, int sink, float scale_log2,
     uint16_t *__restrict__ O, float *__restrict__ lse,
-    const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores)
+    const float *__restrict__ S, int64_t n_cap, float *__restrict__ scores,
+    const float *__restrict__ SG, int64_t n_gcap, int kc, int32_t *__restrict__ chunk_ids_out)
 {
-    static_assert(kRouteNI == 0 || kUnit == kC, "fused routing picks chunks");
+    static_assert(kFusedGroupChunks * (kC / kGroup) <= 4 * 64,
+                  "fused group routing keeps every group candidate in 4 keys per lane");
     constexpr int HW = G < 4 ? G : 4;            // query heads per workgroup
     constexpr int NHG = G / HW;                  // workgroups per unit
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile];
@@ -309,19 +314,40 @@ void attend_fwd_kernel(
         const bool wr = hg == 0;            // one workgroup of a unit writes the ids
         float *sc_row = (scores && wr) ? scores + (g * n_blocks + b) * k : nullptr;
         constexpr int kBatchR = G >= 8 ? 4 : 8;
-        const int n_sel = route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
-            sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, k, nullptr, 0, sink,
-            [&](int r, int id, float sc) __attribute__((always_inline)) {
-                list[1 + n_sink + r] = id;
-                if (wr) {
-                    id_row[r] = id;
-                    if (sc_row) sc_row[r] = sc;
-                }
-            },
-            [&]() __attribute__((always_inline)) {
-                if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
-            },
-            std::integral_constant<bool, kQInLds>{});
+        auto load_local = [&]() __attribute__((always_inline)) {
+            if (grp == 0) load_v(r0, Vg, P); else load_k(r0, Kg, P);
+        };
+        const std::integral_constant<bool, kQInLds> q_local{};
+        auto emit_unit = [&](int r, int id, float sc) __attribute__((always_inline)) {
+            list[1 + n_sink + r] = id;
+            if (wr) {
+                id_row[r] = id;
+                if (sc_row) sc_row[r] = sc;
+            }
+        };
+        int n_sel;
+        if constexpr (kUnit == kC) {
+            n_sel = route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
+                sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, k, nullptr, 0, sink, emit_unit,
+                load_local, q_local);
+        } else {
+            // the block's chunks into chunk_sel (and the chunk id output),
+            // then the groups of those chunks into the tile list
+            __shared__ int chunk_sel[kFusedGroupChunks];
+            int32_t *crow = (chunk_ids_out && wr) ? chunk_ids_out + (g * n_blocks + b) * kc
+                                                  : nullptr;
+            route_block<G, kRouteNI, false, kBatchR, kThreads / 64>(
+                sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, kc, nullptr, 0, sink,
+                [&](int r, int id, float) __attribute__((always_inline)) {
+                    chunk_sel[r] = id;
+                    if (crow) crow[r] = id;
+                },
+                load_local, q_local);
+            __syncthreads();
+            n_sel = route_block<G, 4, true, kBatchR, kThreads / 64>(
+                sh, keys, q_row, n_q, gkv, b, p0, SG, n_gcap, k, chunk_sel, kc, sink, emit_unit,
+                NoHook{}, q_local);
+        }
         if (wave == 0) {
             write_sink_units(list + 1, n_sink);
             if (lane == 0) {
@@ -588,6 +614,10 @@ struct FwdArgs {
     const float *S;          // fused routing only
     int64_t n_cap;
     float *scores;
+    const float *SG;         // fused group routing only
+    int64_t n_gcap;
+    int32_t kc;
+    int32_t *chunk_ids;
 };
 
 template <int G, int kUnit, int kRouteNI>
@@ -602,7 +632,8 @@ hipError_t launch_g(const FwdArgs &a, hipStream_t stream)
                        dim3((unsigned)a.Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
                        dim3(kThreads), 0,
                        stream, a.Q, a.K, a.V, a.n_q, kv_div, a.T_cap, a.p0, a.ids, a.k,
-                       (int)a.sink, scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores);
+                       (int)a.sink, scale_log2, a.O, a.lse, a.S, a.n_cap, a.scores, a.SG,
+                       a.n_gcap, (int)a.kc, a.chunk_ids);
     return hipGetLastError();
 }
 
@@ -664,6 +695,26 @@ hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const u
     if (max_eligible <= 8 * 64) return launch_unit<kC, 8>(a, stream);
     if (max_eligible <= 16 * 64) return launch_unit<kC, 16>(a, stream);
     return launch_unit<kC, 32>(a, stream);
+}
+
+hipError_t launch_route_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
+                                          const uint16_t *V, int64_t Hq, int64_t Hkv,
+                                          int64_t T_cap, int64_t p0, int64_t n_q,
+                                          const float *S, int64_t n_cap, int32_t kc,
+                                          const float *SG, int64_t n_gcap, int32_t m,
+                                          int32_t sink, float scale, int32_t *chunk_ids,
+                                          int32_t *gids, float *gscores, uint16_t *O, float *lse,
+                                          hipStream_t stream)
+{
+    if (kc <= 0 || kc > kFusedGroupChunks || m <= 0) return hipErrorInvalidValue;
+    const FwdArgs a{Q, K, V, false, Hq, Hkv, T_cap, p0, n_q, gids, m, sink, scale, O, lse,
+                    S, n_cap, gscores, SG, n_gcap, kc, chunk_ids};
+    // keys per lane of the chunk router's register selection (as above)
+    const int64_t max_eligible = (p0 + n_q - kC) / kC - sink;
+    if (max_eligible <= 4 * 64) return launch_unit<kGroup, 4>(a, stream);
+    if (max_eligible <= 8 * 64) return launch_unit<kGroup, 8>(a, stream);
+    if (max_eligible <= 16 * 64) return launch_unit<kGroup, 16>(a, stream);
+    return launch_unit<kGroup, 32>(a, stream);
 }
 
 }  // namespace hga

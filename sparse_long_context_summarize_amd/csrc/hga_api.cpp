@@ -366,6 +366,87 @@ hga_status hga_attend_fwd_groups(const hga_config *cfg, const void *Q, const voi
                       "hga_attend_fwd_groups launch");
 }
 
+hga_status hga_route_attend_fwd_groups(const hga_config *cfg, const void *Q, const void *K,
+                                       const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                       const float *summaries, int64_t n_chunk_cap,
+                                       int64_t n_chunks_valid, const float *group_summaries,
+                                       int64_t n_group_cap, int32_t group_top_k,
+                                       int32_t *chunk_ids, int32_t *group_ids,
+                                       float *group_scores_or_null, void *O, float *lse,
+                                       hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_kv_head_routing(cfg, "hga_route_attend_fwd_groups");
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (group_top_k < 0 || group_top_k > hga::kMaxGroupTopK)
+        return fail(HGA_ERR_INVALID_ARG, "group_top_k must be in [0, %d] (got %d)",
+                    hga::kMaxGroupTopK, group_top_k);
+    if (n_chunks_valid < 0 || n_chunk_cap < 0 || n_group_cap < 0)
+        return fail(HGA_ERR_INVALID_ARG, "negative chunk or group count");
+    if (n_chunks_valid > n_chunk_cap)
+        return fail(HGA_ERR_CAPACITY, "n_chunks_valid (%lld) exceeds n_chunk_cap (%lld)",
+                    (long long)n_chunks_valid, (long long)n_chunk_cap);
+    if (n_q == 0) return HGA_OK;
+    const int64_t need = (p0 + n_q - hga::kC) / hga::kC;   // eligible chunks of the last block
+    if (cfg->top_k > 0) {
+        if (need > n_chunks_valid)
+            return fail(HGA_ERR_CAPACITY, "the last query block needs %lld summaries, %lld valid",
+                        (long long)need, (long long)n_chunks_valid);
+        if (need > kMaxEligible)
+            return fail(HGA_ERR_UNSUPPORTED, "more than %lld candidate chunks per block",
+                        (long long)kMaxEligible);
+        if (group_top_k > 0 && need * (hga::kC / hga::kGroup) > n_group_cap)
+            return fail(HGA_ERR_CAPACITY,
+                        "the last query block may route to %lld groups, the buffer holds %lld",
+                        (long long)(need * (hga::kC / hga::kGroup)), (long long)n_group_cap);
+    }
+    if (!Q || !K || !V || !O || !lse || (group_top_k > 0 && !group_ids) ||
+        (cfg->top_k > 0 && (!chunk_ids || (need > 0 && !summaries) ||
+                            (group_top_k > 0 && need > 0 && !group_summaries))))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const float scale = effective_scale(cfg);
+    const bool fused = cfg->top_k > 0 && cfg->top_k <= hga::kFusedGroupChunks &&
+                       group_top_k > 0 &&
+                       need - cfg->sink_chunks <= hga::route_attend_max_candidates();
+    if (fused)
+        return hip_status(hga::launch_route_attend_fwd_groups(
+                              (const uint16_t *)Q, (const uint16_t *)K, (const uint16_t *)V,
+                              cfg->n_q_heads, cfg->n_kv_heads, T_cap, p0, n_q, summaries,
+                              n_chunk_cap, cfg->top_k, group_summaries, n_group_cap,
+                              group_top_k, cfg->sink_chunks, scale, chunk_ids, group_ids,
+                              group_scores_or_null, (uint16_t *)O, lse, stream),
+                          "hga_route_attend_fwd_groups launch");
+    // otherwise the three kernels in turn, as hga_route, hga_route_groups and
+    // hga_attend_fwd_groups run them
+    if (cfg->top_k > 0) {
+        st = hip_status(hga::launch_route((const uint16_t *)Q, cfg->n_q_heads, cfg->n_kv_heads,
+                                          p0, n_q, summaries, n_chunk_cap, cfg->top_k,
+                                          cfg->sink_chunks, false, false, nullptr, chunk_ids,
+                                          nullptr, stream),
+                        "hga_route_attend_fwd_groups route launch");
+        if (st != HGA_OK) return st;
+    }
+    if (group_top_k > 0) {
+        st = hip_status(hga::launch_route_groups((const uint16_t *)Q, cfg->n_q_heads,
+                                                 cfg->n_kv_heads, p0, n_q, group_summaries,
+                                                 n_group_cap, chunk_ids, cfg->top_k, group_top_k,
+                                                 cfg->sink_chunks, group_ids,
+                                                 group_scores_or_null, stream),
+                        "hga_route_attend_fwd_groups group route launch");
+        if (st != HGA_OK) return st;
+    }
+    return hip_status(hga::launch_attend_fwd_groups((const uint16_t *)Q, (const uint16_t *)K,
+                                                    (const uint16_t *)V, cfg->n_q_heads,
+                                                    cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
+                                                    group_top_k, cfg->sink_chunks, scale,
+                                                    (uint16_t *)O, lse, stream),
+                      "hga_route_attend_fwd_groups attend launch");
+}
+
 hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const void *K,
                                  const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
                                  const int32_t *group_ids, int32_t group_top_k, const void *O,

@@ -18,6 +18,9 @@ constexpr int kMaxSink = HGA_MAX_SINK_CHUNKS;
 // tile list lengths: local + sink + routed units, chunk and group level
 constexpr int kChunkListMax = 1 + kMaxSink + kMaxTopK;
 constexpr int kGroupListMax = 1 + kMaxSink * (64 / kGroup) + kMaxGroupTopK;
+// chunk budget up to which the two routing levels run inside the group
+// attention kernel (launch_route_attend_fwd_groups)
+constexpr int kFusedGroupChunks = 32;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -158,6 +161,18 @@ hipError_t launch_route_attend_fwd(const uint16_t *Q, const uint16_t *K, const u
                                    int32_t sink, bool per_q_head, float scale, int32_t *ids,
                                    float *scores, uint16_t *O, float *lse, hipStream_t stream);
 int64_t route_attend_max_candidates();
+// Both routing levels and group attention in one launch (chunk ids, group ids
+// and group scores written as launch_route and launch_route_groups would
+// write them). Needs 0 < kc <= kFusedGroupChunks, m > 0 and (p0 + n_q - C)/C
+// <= route_attend_max_candidates().
+hipError_t launch_route_attend_fwd_groups(const uint16_t *Q, const uint16_t *K,
+                                          const uint16_t *V, int64_t Hq, int64_t Hkv,
+                                          int64_t T_cap, int64_t p0, int64_t n_q,
+                                          const float *S, int64_t n_cap, int32_t kc,
+                                          const float *SG, int64_t n_gcap, int32_t m,
+                                          int32_t sink, float scale, int32_t *chunk_ids,
+                                          int32_t *gids, float *gscores, uint16_t *O, float *lse,
+                                          hipStream_t stream);
 // Routed decode (decode.hip). One workspace of decode_workspace_bytes serves
 // the router (the keys of up to decode_key_capacity candidates per token and
 // kv head) and then the attention (the partials of decode_splits(k, sink)

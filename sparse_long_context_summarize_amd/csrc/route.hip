@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             return *(const u32x4 *)(Q + (h * n_q + i) * kD + dseg * 8);
         }
     };
+    const int32_t *chunk_row = kGroups ? chunk_ids + (gkv * (n_q / kC) + b) * kc : nullptr;
     route_block<G, NI, kGroups, 16, kRouteWaves>(sh, keys, q_row, n_q, gkv, b, p0, S, n_cap, k,
-                                                 chunk_ids, kc, c_lo,
+                                                 chunk_row, kc, c_lo,
                                     [&](int r, int id, float sc) __attribute__((always_inline)) {
                                         out[r] = id;
                                         if (sout) sout[r] = sc;

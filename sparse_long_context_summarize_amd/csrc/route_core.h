@@ -297,9 +297,9 @@ struct RouteLds {
 // kGroups = false: chunk routing, candidates every chunk c with c_lo <= c <
 // P/C (c_lo = the sink window's chunk count), rows of S.
 // kGroups = true: group routing (second level), candidates the 8 groups of
-// each distinct valid chunk (c_lo <= c < P/C) of chunk_ids[g][b], in
-// ascending group order, rows of the group summaries S; k is then the group
-// budget.
+// each distinct valid chunk (c_lo <= c < P/C) of chunk_row (the block's kc
+// chunk ids, in global memory or LDS), in ascending group order, rows of the
+// group summaries S; k is then the group budget.
 // kBatch: summary rows per lane in flight; kScoreWaves: waves that score
 // (the first kScoreWaves of the workgroup). Both only distribute the
 // candidates over lanes: each score's arithmetic, and so every score, is the
@@ -315,7 +315,7 @@ template <int G, int NI, bool kGroups, int kBatch, int kScoreWaves, typename QRo
 __device__ __forceinline__ int route_block(
     RouteLds &sh, uint32_t *keys, QRow q_row, int64_t n_q, int64_t g,
     int64_t b, int64_t p0, const float *__restrict__ S, int64_t n_cap, int k,
-    const int32_t *__restrict__ chunk_ids, int kc, int c_lo, Emit emit,
+    const int32_t *chunk_row, int kc, int c_lo, Emit emit,
     Hook after_loads = Hook{}, QLocal = QLocal{})
 {
     // q_row reads LDS (QLocal true): the query-row sums come first and the
@@ -328,15 +328,13 @@ __device__ __forceinline__ int route_block(
     // below, and the selection inside them, run on scalar registers)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool act = wave < kRouteWaves;
-    const int64_t n_blocks = n_q / kBq;
     const int64_t P = kBq == kC ? p0 + b * kC : kC * ((p0 + b) / kC);
     int *chl = sh.chl;
     int nE = (int)max((int64_t)0, P / kC - c_lo);
     if (kGroups) {
         // 0. the block's distinct valid routed chunks, ascending
         if (wave == 0) {
-            const int n = sorted_chunk_set(chunk_ids + (g * n_blocks + b) * kc, kc, c_lo,
-                                           P / kC, chl, (int *)keys);
+            const int n = sorted_chunk_set(chunk_row, kc, c_lo, P / kC, chl, (int *)keys);
             if (lane == 0) sh.n_ch = n;
         }
         __syncthreads();

@@ -25,6 +25,7 @@ EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
             "hga_route_attend_fwd",
             "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
+            "hga_route_attend_fwd_groups",
             "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
             "hga_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
             "hga_status_string", "hga_last_error", "hga_version")
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                    _vp, _vp, _vp]
     L.hga_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp]
+    L.hga_route_attend_fwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64,
+                                              _i64, _vp, _i64, ctypes.c_int32, _vp, _vp, _vp,
+                                              _vp, _vp, _vp]
     L.hga_route_decode.argtypes = [_cfgp, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp]
     L.hga_decode_workspace_bytes.argtypes = [_cfgp, _i64, _i64]
@@ -106,6 +110,7 @@ def lib() -> ctypes.CDLL:
                "hga_attend_bwd",
                "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
+               "hga_route_attend_fwd_groups",
                "hga_attend_bwd_groups", "hga_diag_gather", "hga_route_decode",
                "hga_attend_decode"):
         getattr(L, fn).restype = ctypes.c_int
@@ -235,6 +240,23 @@ def _m_route_groups(cfg: hga_config, Q, p0: int, group_summaries, chunk_ids, gro
             _stream(stream))
 
 
+def _m_route_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int,
+                               group_summaries, chunk_ids, group_ids, O, lse, scores=None,
+                               stream=None):
+    if group_ids.dim() != 3:
+        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16))
+    if K.shape != V.shape:
+        raise ValueError("K and V shapes differ")
+    return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
+            group_ids.shape[2], _dev(chunk_ids, "chunk_ids", torch.int32),
+            _dev(group_ids, "group_ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
+
+
 def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, stream=None):
     args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16))
@@ -306,6 +328,7 @@ _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
             "hga_attend_fwd_groups": _m_attend_fwd_groups,
+            "hga_route_attend_fwd_groups": _m_route_attend_fwd_groups,
             "hga_attend_bwd_groups": _m_attend_bwd_groups,
             "hga_diag_gather": _m_diag_gather, "hga_route_decode": _m_route_decode,
             "hga_attend_decode": _m_attend_decode}
@@ -388,6 +411,21 @@ def hga_attend_fwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: 
     """Attention over routed 8-token groups plus the causal local block."""
     _check("hga_attend_fwd_groups", lib().hga_attend_fwd_groups(
         *_m_attend_fwd_groups(cfg, Q, K, V, p0, group_ids, O, lse, stream)))
+
+
+def hga_route_attend_fwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor,
+                                V: torch.Tensor, p0: int, summaries: torch.Tensor,
+                                n_chunks_valid: int, group_summaries: torch.Tensor,
+                                chunk_ids: torch.Tensor, group_ids: torch.Tensor, O: torch.Tensor,
+                                lse: torch.Tensor, scores: torch.Tensor | None = None,
+                                stream=None) -> None:
+    """hga_route, hga_route_groups and hga_attend_fwd_groups in one call
+    (one launch when 0 < top_k <= 32); chunk_ids [Hkv][n_q/64][top_k] and
+    group_ids [Hkv][n_q/64][group_top_k] are written as those calls write them."""
+    _check("hga_route_attend_fwd_groups", lib().hga_route_attend_fwd_groups(
+        *_m_route_attend_fwd_groups(cfg, Q, K, V, p0, summaries, n_chunks_valid,
+                                    group_summaries, chunk_ids, group_ids, O, lse, scores,
+                                    stream)))
 
 
 def hga_attend_bwd_groups(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,

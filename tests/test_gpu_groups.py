@@ -276,3 +276,73 @@ def test_messy_group_rows():
     g[0, 3] = np.arange(m) * 1 + 50                    # 70 distinct, last tile 6 of 8
     res = gpu_group_forward(x, p0, 4, 8, gids_override=g)
     check_group_attend(x, res, p0, where="messy groups")
+
+
+# ------------------------------------------------ both routing levels fused
+
+def _fused_and_separate(x, p0, k, m, sink=0):
+    """hga_route_attend_fwd_groups against hga_route + hga_route_groups +
+    hga_attend_fwd_groups on the same device inputs."""
+    Hq, n_q, D = x["Q"].shape
+    Hkv, T, _ = x["K"].shape
+    nb = n_q // C
+    n_valid = (p0 + n_q) // C
+    n_gcap = n_valid * (C // U)
+    cfg = hga.make_config(Hq, Hkv, k, sink_chunks=sink)
+    Qd, Kd, Vd = to_dev_bf16(x["Q"]), to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    S = torch.zeros((Hkv, n_valid, D), device="cuda")
+    SG = torch.zeros((Hkv, n_gcap, D), device="cuda")
+    hga.hga_summarize(cfg, Kd, 0, p0 + n_q, S)
+    hga.hga_summarize_groups(cfg, Kd, 0, p0 + n_q, SG)
+    out = {}
+    for tag in ("separate", "fused"):
+        fill = -7 if tag == "separate" else -9
+        ids = torch.full((Hkv, nb, k), fill, dtype=torch.int32, device="cuda")
+        gids = torch.full((Hkv, nb, m), fill, dtype=torch.int32, device="cuda")
+        gsc = torch.full((Hkv, nb, m), float(fill), device="cuda")
+        O = torch.full((Hq, n_q, D), float(fill), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((Hq, n_q), float(fill), device="cuda")
+        if tag == "separate":
+            hga.hga_route(cfg, Qd, p0, S, n_valid, ids)
+            hga.hga_route_groups(cfg, Qd, p0, SG, ids, gids, gsc)
+            hga.hga_attend_fwd_groups(cfg, Qd, Kd, Vd, p0, gids, O, lse)
+        else:
+            hga.hga_route_attend_fwd_groups(cfg, Qd, Kd, Vd, p0, S, n_valid, SG, ids, gids, O,
+                                            lse, gsc)
+        torch.cuda.synchronize()
+        out[tag] = dict(ids=ids.cpu().numpy(), gids=gids.cpu().numpy(), gscores=from_dev(gsc),
+                        O=from_dev(O), lse=from_dev(lse))
+    return out["separate"], out["fused"]
+
+
+def _assert_same(a, b, where):
+    for name in ("ids", "gids", "gscores", "O", "lse"):
+        np.testing.assert_array_equal(b[name], a[name], err_msg=f"{where}: {name}")
+
+
+@pytest.mark.parametrize("sink", [0, 2])
+def test_layer16k_groups_fused(sink):
+    # top_k = 16 <= 32: one launch, both routing levels in each workgroup
+    w = inputs.LAYER16K_GROUPS
+    x = inputs.generate(w)
+    log(f"layer16k groups fused, sink {sink}")
+    a, b = _fused_and_separate(x, w.p0, w.k, w.m, sink=sink)
+    _assert_same(a, b, f"layer16k fused sink={sink}")
+    assert (b["gids"] >= 0).sum() > 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,k,m,p0,sink", [
+    (1, 1, 3, 20, 768, 0),      # G = 1
+    (8, 4, 5, 40, 768, 1),      # G = 2, sink window
+    (16, 4, 32, 256, 3840, 0),  # G = 4, the largest fused chunk budget, every group kept
+    (8, 1, 7, 33, 768, 0),      # G = 8: two workgroups per unit
+    (4, 1, 8, 16, 0, 0),        # first segment: block 0 has no candidates
+    (4, 1, 40, 64, 3840, 0),    # top_k > 32: the three kernels in turn
+])
+def test_groups_fused_layouts(Hq, Hkv, k, m, p0, sink):
+    n_q = 256
+    T = p0 + n_q
+    x = inputs.small_random(300 + Hq + k, Hq, Hkv, 128, T, n_q, bf16=True)
+    log(f"groups fused Hq={Hq} Hkv={Hkv} k={k} m={m} p0={p0} sink={sink}")
+    a, b = _fused_and_separate(x, p0, k, m, sink=sink)
+    _assert_same(a, b, f"Hq={Hq} Hkv={Hkv} k={k} m={m} p0={p0} sink={sink}")
