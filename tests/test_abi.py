@@ -262,6 +262,25 @@ def test_grid_limits():
     assert "tokens per call" in hga.hga_last_error()
 
 
+def test_route_attend_fwd_groups_checks():
+    """hga_route_attend_fwd_groups refuses bad arguments before any launch."""
+    L = hga.lib()
+
+    def call(cfg, m=64, n_gcap=16384 // 8, chunk_ids=FAKE, group_ids=FAKE, n_valid=256):
+        return L.hga_route_attend_fwd_groups(ctypes.byref(cfg), FAKE, FAKE, FAKE, 16384, 14336,
+                                             2048, FAKE, 256, n_valid, FAKE, n_gcap, m,
+                                             chunk_ids, group_ids, None, FAKE, FAKE, None)
+
+    cfg = _cfg()
+    assert call(_cfg(route_heads=hga.HGA_ROUTE_PER_Q_HEAD)) == hga.HGA_ERR_UNSUPPORTED
+    assert call(cfg, m=2049) == hga.HGA_ERR_INVALID_ARG
+    assert "group_top_k" in hga.hga_last_error()
+    assert call(cfg, n_gcap=100) == hga.HGA_ERR_CAPACITY          # groups of 255 chunks needed
+    assert call(cfg, n_valid=200) == hga.HGA_ERR_CAPACITY         # summaries of 255 chunks needed
+    assert call(cfg, chunk_ids=None) == hga.HGA_ERR_INVALID_ARG
+    assert call(cfg, group_ids=None) == hga.HGA_ERR_INVALID_ARG
+
+
 def test_routing_variant_checks():
     L = hga.lib()
     bad = _cfg(route_heads=2)
