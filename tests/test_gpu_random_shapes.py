@@ -1,7 +1,8 @@
 """Seeded random shapes through the fused entry points against the oracle:
-hga_summarize + hga_route_attend_fwd (chunk routing, then attention) and
+hga_summarize + hga_route_attend_fwd (chunk routing, then attention),
 hga_summarize_groups + hga_route_attend_fwd_groups (both routing levels,
-then group attention), with mixed head layouts (G = 1, 2, 4, 8), budgets,
+then group attention) and hga_attend_bwd after the fused forward (per kv
+head and per query head), with mixed head layouts (G = 1, 2, 4, 8), budgets,
 sink windows, history lengths and segment lengths. Ids pass under the gap
 rule, outputs under the bf16 bar (tests/parity.py)."""
 import os
@@ -104,3 +105,40 @@ def test_random_shape_route_attend_groups(seed):
     O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], gids, p0, C=U, sink=sink * C)
     check_close(f"{where} O", from_dev(O), O_ref)
     check_close(f"{where} lse", from_dev(lse), lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shape_backward(seed):
+    # odd seeds route per query head (one id row per query head)
+    Hq, Hkv, n_q, p0, sink, k, _ = _shape(200 + seed)
+    per_q = seed % 2 == 1
+    where = (f"seed {seed}: Hq={Hq} Hkv={Hkv} n_q={n_q} p0={p0} sink={sink} k={k} "
+             f"per_q_head={per_q}")
+    print(where, flush=True)
+    x = inputs.small_random(9200 + seed, Hq, Hkv, 128, p0 + n_q, n_q, bf16=True, with_dO=True)
+    Qd, Kd, Vd, dOd = (to_dev_bf16(x[n]) for n in ("Q", "K", "V", "dO"))
+    cfg = hga.make_config(Hq, Hkv, k, sink_chunks=sink,
+                          route_heads=hga.HGA_ROUTE_PER_Q_HEAD if per_q else
+                          hga.HGA_ROUTE_PER_KV_HEAD)
+    n_valid = (p0 + n_q) // C
+    S = torch.zeros((Hkv, n_valid, 128), device="cuda")
+    hga.hga_summarize(cfg, Kd, 0, p0 + n_q, S)
+    ids = torch.full(((Hq if per_q else Hkv), n_q // C, k), -7, dtype=torch.int32, device="cuda")
+    O = torch.empty((Hq, n_q, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, n_q), device="cuda")
+    hga.hga_route_attend_fwd(cfg, Qd, Kd, Vd, p0, S, n_valid, ids, O, lse)
+    nan = float("nan")
+    dQ = torch.full((Hq, n_q, 128), nan, device="cuda")
+    dK = torch.full((Hkv, n_q, 128), nan, device="cuda")
+    dV = torch.full((Hkv, n_q, 128), nan, device="cuda")
+    ws = torch.full((hga.hga_attend_bwd_workspace_bytes(cfg, n_q),), 255, dtype=torch.uint8,
+                    device="cuda")
+    hga.hga_attend_bwd(cfg, Qd, Kd, Vd, p0, ids, O, lse, dOd, dQ, dK, dV, ws)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    refs = oracle.attend_bwd(x["Q"], x["K"], x["V"], x["dO"], ids, p0, sink=sink * C,
+                             per_q_head=per_q)
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dQ, dK, dV), refs):
+        got = from_dev(got)
+        assert np.all(np.isfinite(got)), f"{where} {name}: unwritten or non-finite"
+        check_close(f"{where} {name}", got, ref)
