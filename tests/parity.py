@@ -55,11 +55,12 @@ def check_ids(gpu_ids: np.ndarray, ref_ids: np.ndarray, sigma: np.ndarray, p0: i
             assert na == 0 or (a[0] >= lo and a[na - 1] < nE), ctx
             if np.array_equal(a, r):
                 continue
-            sig = sigma[g, b, lo:nE]
-            M = np.max(np.abs(sig))
-            kth = np.sort(sig)[::-1][nr - 1]
+            # candidate scores; sigma is indexed by absolute chunk id
+            cand = sigma[g, b, lo:nE]
+            M = np.max(np.abs(cand))
+            kth = np.sort(cand)[::-1][nr - 1]
             for c in set(a[:na].tolist()) ^ set(r[:nr].tolist()):
-                assert abs(sig[c] - kth) <= GAP * M, (ctx, c, sig[c], kth, M)
+                assert abs(sigma[g, b, c] - kth) <= GAP * M, (ctx, c, sigma[g, b, c], kth, M)
             near_ties += 1
     return near_ties
 
