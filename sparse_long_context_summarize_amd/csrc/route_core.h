@@ -73,6 +73,32 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// The selection threshold: the largest T with #{key >= T} >= k, given the
+// largest and smallest key (mx, mn) and count_ge(x) = #{key >= x} over the
+// candidates (n > k >= 1 of them). Bits above the highest bit in which the
+// keys differ are shared by every key; below it T is built one bit at a
+// time, and the search stops as soon as exactly k keys reach the candidate
+// threshold (they are then the k largest, and no lower bit can change which
+// keys are taken). When every key is equal, T is that key. The chosen set is
+// then every key > T plus the lowest-positioned keys == T, k in all. Host and
+// device code: the CPU tests run this very function.
+template <typename CountGe>
+__host__ __device__ __forceinline__ uint32_t select_threshold(uint32_t mx, uint32_t mn, int k,
+                                                              CountGe count_ge)
+{
+    const uint32_t diff = mx ^ mn;
+    if (diff == 0u) return mx;
+    const int top = 31 - __builtin_clz(diff);
+    uint32_t T = (top == 31) ? 0u : (mx & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        const int cnt = count_ge(cand);
+        if (cnt >= k) T = cand;
+        if (cnt == k) break;
+    }
+    return T;
+}
+
 // Wave-level selection of the k largest keys[0..n) (ties: lower position
 // first). Writes the chosen positions, ascending, to out_pos (LDS) and
 // returns their number, min(k, n). Every lane of the wave must call it.
@@ -91,23 +117,14 @@ __device__ __forceinline__ int wave_select(const uint32_t *keys, int n, int k, i
     }
     mx = wave_max_u32(mx);
     mn = wave_min_u32(mn);
-    // Bits above the highest bit in which the keys differ are shared by all.
-    const uint32_t diff = mx ^ mn;
-    int top = diff ? 31 - __builtin_clz(diff) : -1;
-    uint32_t T = (top >= 31) ? 0u : (mx & ~((2u << top) - 1u));
-    // Largest T with #{key >= T} >= k, one bit at a time; once exactly k keys
-    // reach a candidate threshold they are the k largest, and no lower bit
-    // can change which keys are taken.
-    for (int bit = top; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
+    const uint32_t T = select_threshold(mx, mn, k, [&](uint32_t cand) __attribute__((always_inline)) {
         int cnt = 0;
         for (int base = 0; base < n; base += 64) {
             const int p = base + lane;
             cnt += __popcll(__ballot(p < n && keys[p] >= cand));
         }
-        if (cnt >= k) T = cand;
-        if (cnt == k) break;
-    }
+        return cnt;
+    });
     int n_gt = 0;
     for (int base = 0; base < n; base += 64) {
         const int p = base + lane;
@@ -123,8 +140,9 @@ __device__ __forceinline__ int wave_select(const uint32_t *keys, int n, int k, i
         const bool take = (p < n && x > T) || (eq && eq_seen + lanes_below(em) < need);
         eq_seen += __popcll(em);
         const uint64_t sm = __ballot(take);
-        if (take) out_pos[out + lanes_below(sm)] = p;
-        out += __popcll(sm);
+        // (exactly k keys are taken; the bound only guards out_pos's size)
+        if (take && out + lanes_below(sm) < k) out_pos[out + lanes_below(sm)] = p;
+        out = min(k, out + __popcll(sm));
     }
     return out;
 }
@@ -152,7 +170,7 @@ __device__ __forceinline__ void wave_max_min_u32(uint32_t &mx, uint32_t &mn) {
 
 // Wave-level top-k of keys[0..nE) (LDS), nE <= NI*64, by (key desc, candidate
 // index asc): one wave holds every key in registers (candidate c = it*64 +
-// lane), finds the k-th largest key bit by bit from ballot counts (stopping
+// lane), finds the selection threshold bit by bit from ballot counts (stopping
 // as soon as exactly k keys reach the threshold being built), takes ties at
 // that key from the lowest candidates, and passes id_of(c) of the chosen
 // candidates in ascending candidate order (ballot + mbcnt compaction) with
@@ -192,21 +210,12 @@ __device__ __forceinline__ int select_top_k_reg(const uint32_t *keys, int nE, in
         // threshold search run in scalar registers)
         mx = (uint32_t)__builtin_amdgcn_readfirstlane((int)mx);
         mn = (uint32_t)__builtin_amdgcn_readfirstlane((int)mn);
-        // Bits above the highest bit in which the keys differ are shared.
-        const uint32_t diff = mx ^ mn;
-        const int top = diff ? 31 - __builtin_clz(diff) : -1;
-        uint32_t T = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)((top < 0) ? mx : (top >= 31 ? 0u : (mx & ~((2u << top) - 1u)))));
-        // Largest T with #{key >= T} >= k, one bit at a time; once exactly k
-        // keys reach a candidate threshold they are the k largest.
-        for (int bit = __builtin_amdgcn_readfirstlane(top); bit >= 0; --bit) {
-            const uint32_t cand = T | (1u << bit);
+        const uint32_t T = select_threshold(mx, mn, k, [&](uint32_t cand) __attribute__((always_inline)) {
             int cnt = 0;
 #pragma unroll
             for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
-            if (cnt >= k) T = cand;
-            if (cnt == k) break;
-        }
+            return cnt;
+        });
         int n_gt = 0;
 #pragma unroll
         for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));

@@ -157,6 +157,49 @@ def _dev(t: torch.Tensor | None, name: str, dtype: torch.dtype):
     return t.data_ptr()
 
 
+def _units(cfg: hga_config) -> int:
+    """Id rows per query block: one per kv head, or per query head."""
+    return cfg.n_q_heads if cfg.route_heads == HGA_ROUTE_PER_Q_HEAD else cfg.n_kv_heads
+
+
+def _blocks(cfg: hga_config, n_q: int) -> int:
+    return n_q // cfg.q_block if cfg.q_block > 0 else 0
+
+
+def _shape(t, name: str, want) -> None:
+    """Refuse a tensor whose shape differs from the one the call implies (a
+    wrong shape would otherwise become an out-of-bounds device access: the C
+    ABI sees pointers only). Entries of `want` that are None are free."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        shown = tuple("*" if w is None else w for w in want)
+        raise ValueError(f"{name} has shape {got}; this call needs {shown}")
+
+
+def _q_shapes(cfg: hga_config, Q, name: str = "Q") -> int:
+    _shape(Q, name, (cfg.n_q_heads, None, cfg.head_dim))
+    return Q.shape[1]
+
+
+def _kv_shapes(cfg: hga_config, K, V=None) -> None:
+    _shape(K, "K", (cfg.n_kv_heads, None, cfg.head_dim))
+    if V is not None and tuple(K.shape) != tuple(V.shape):
+        raise ValueError("K and V shapes differ")
+
+
+def _summary_shapes(cfg: hga_config, S, name: str = "summaries") -> None:
+    _shape(S, name, (cfg.n_kv_heads, None, cfg.head_dim))
+
+
+def _out_shapes(cfg: hga_config, n_q: int, O, lse, O_name: str = "O") -> None:
+    _shape(O, O_name, (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(lse, "lse", (cfg.n_q_heads, n_q))
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -164,12 +207,18 @@ def _stream(stream) -> int | None:
 
 
 def _m_summarize(cfg: hga_config, K, tok_begin: int, n_tok: int, summaries, stream=None):
+    _kv_shapes(cfg, K)
+    _summary_shapes(cfg, summaries)
     return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), K.shape[1], tok_begin, n_tok,
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], _stream(stream))
 
 
 def _m_route(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids, scores=None,
              stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _summary_shapes(cfg, summaries)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _shape(scores, "scores", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
             _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
@@ -178,6 +227,11 @@ def _m_route(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids, s
 
 def _m_route_causal(cfg: hga_config, Q, Q_prev, p0: int, summaries, n_chunks_valid: int, ids,
                     scores=None, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _shape(Q_prev, "Q_prev", (cfg.n_q_heads, cfg.q_block, cfg.head_dim))
+    _summary_shapes(cfg, summaries)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _shape(scores, "scores", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16),
             _dev(Q_prev, "Q_prev", torch.bfloat16), p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
@@ -186,6 +240,10 @@ def _m_route_causal(cfg: hga_config, Q, Q_prev, p0: int, summaries, n_chunks_val
 
 
 def _m_attend_fwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
     args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16))
     if K.shape != V.shape:
@@ -196,6 +254,14 @@ def _m_attend_fwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, stream=None):
 
 def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV, workspace,
                   stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
+    _shape(dO, "dO", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dQ, "dQ", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dK, "dK", (cfg.n_kv_heads, n_q, cfg.head_dim))
+    _shape(dV, "dV", (cfg.n_kv_heads, n_q, cfg.head_dim))
     if K.shape != V.shape:
         raise ValueError("K and V shapes differ")
     if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
@@ -212,6 +278,12 @@ def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV
 
 def _m_route_attend_fwd(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int, ids,
                         O, lse, scores=None, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _summary_shapes(cfg, summaries)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _shape(scores, "scores", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
     args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16))
     if K.shape != V.shape:
@@ -224,6 +296,8 @@ def _m_route_attend_fwd(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_v
 
 def _m_summarize_groups(cfg: hga_config, K, tok_begin: int, n_tok: int, group_summaries,
                         stream=None):
+    _kv_shapes(cfg, K)
+    _summary_shapes(cfg, group_summaries, "group_summaries")
     return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), K.shape[1], tok_begin, n_tok,
             _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
             _stream(stream))
@@ -231,8 +305,11 @@ def _m_summarize_groups(cfg: hga_config, K, tok_begin: int, n_tok: int, group_su
 
 def _m_route_groups(cfg: hga_config, Q, p0: int, group_summaries, chunk_ids, group_ids,
                     scores=None, stream=None):
-    if group_ids.dim() != 3:
-        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    n_q = _q_shapes(cfg, Q)
+    _summary_shapes(cfg, group_summaries, "group_summaries")
+    _shape(chunk_ids, "chunk_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), cfg.top_k))
+    _shape(group_ids, "group_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), None))
+    _shape(scores, "scores", (cfg.n_kv_heads, _blocks(cfg, n_q), group_ids.shape[2]))
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
             _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
             _dev(chunk_ids, "chunk_ids", torch.int32), group_ids.shape[2],
@@ -243,12 +320,16 @@ def _m_route_groups(cfg: hga_config, Q, p0: int, group_summaries, chunk_ids, gro
 def _m_route_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int,
                                group_summaries, chunk_ids, group_ids, O, lse, scores=None,
                                stream=None):
-    if group_ids.dim() != 3:
-        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _summary_shapes(cfg, summaries)
+    _summary_shapes(cfg, group_summaries, "group_summaries")
+    _shape(chunk_ids, "chunk_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), cfg.top_k))
+    _shape(group_ids, "group_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), None))
+    _shape(scores, "scores", (cfg.n_kv_heads, _blocks(cfg, n_q), group_ids.shape[2]))
+    _out_shapes(cfg, n_q, O, lse)
     args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16))
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
     return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
             _dev(group_summaries, "group_summaries", torch.float32), group_summaries.shape[1],
@@ -258,12 +339,12 @@ def _m_route_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, summaries, n_c
 
 
 def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(group_ids, "group_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), None))
+    _out_shapes(cfg, n_q, O, lse)
     args = (_dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16))
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
-    if group_ids.dim() != 3:
-        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
     return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
             _dev(group_ids, "group_ids", torch.int32), group_ids.shape[2],
             _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
@@ -271,10 +352,14 @@ def _m_attend_fwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, s
 
 def _m_attend_bwd_groups(cfg: hga_config, Q, K, V, p0: int, group_ids, O, lse, dO, dQ, dK, dV,
                         workspace, stream=None):
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
-    if group_ids.dim() != 3:
-        raise ValueError("group_ids must be [Hkv][n_q/64][group_top_k]")
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(group_ids, "group_ids", (cfg.n_kv_heads, _blocks(cfg, n_q), None))
+    _out_shapes(cfg, n_q, O, lse)
+    _shape(dO, "dO", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dQ, "dQ", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dK, "dK", (cfg.n_kv_heads, n_q, cfg.head_dim))
+    _shape(dV, "dV", (cfg.n_kv_heads, n_q, cfg.head_dim))
     if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
             or not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous GPU memory")
@@ -297,6 +382,10 @@ def _workspace(workspace):
 
 def _m_route_decode(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int, ids,
                     workspace, scores=None, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _summary_shapes(cfg, summaries)
+    _shape(ids, "ids", (cfg.n_kv_heads, n_q, cfg.top_k))
+    _shape(scores, "scores", (cfg.n_kv_heads, n_q, cfg.top_k))
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), p0, Q.shape[1],
             _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
             _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
@@ -304,8 +393,10 @@ def _m_route_decode(cfg: hga_config, Q, p0: int, summaries, n_chunks_valid: int,
 
 
 def _m_attend_decode(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, workspace, stream=None):
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(ids, "ids", (cfg.n_kv_heads, n_q, cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
     _workspace(workspace)
     return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
             _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
@@ -315,8 +406,8 @@ def _m_attend_decode(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, workspace, 
 
 
 def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=None):
-    if K.shape != V.shape:
-        raise ValueError("K and V shapes differ")
+    _kv_shapes(cfg, K, V)
+    _shape(ids, "ids", (cfg.n_kv_heads, _blocks(cfg, n_q), cfg.top_k))
     return (ctypes.byref(cfg), _dev(K, "K", torch.bfloat16), _dev(V, "V", torch.bfloat16),
             K.shape[1], p0, n_q, _dev(ids, "ids", torch.int32), _dev(sink, "sink", torch.int32),
             sink.numel(), _stream(stream))

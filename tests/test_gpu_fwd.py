@@ -328,3 +328,42 @@ def test_repeated_and_unsorted_ids_count_once():
     O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], ids, p0)
     check_close("repeats O", res["O"], O_ref)
     check_close("repeats lse", res["lse"], lse_ref, atol=1e-3, rtol=0, rel_l2=None)
+
+
+@pytest.mark.parametrize("sink", [0, 2])
+def test_zero_query_block_over_2200_candidates(sink):
+    """A query block of zeros scores every chunk exactly 0, so every candidate
+    ties and the tie rule alone fixes the ids (the lowest candidates past the
+    sink). With 2198-2199 candidates this runs the two-stage selection, whose
+    threshold search must then take exactly k keys; both the routing kernel
+    and the fused routing + attention kernel are checked against the oracle."""
+    Hq, Hkv, D, n_q, k = 4, 2, 128, 128, 16
+    T = 64 * 2200
+    p0 = T - n_q
+    x = inputs.small_random(21, Hq, Hkv, D, T, n_q, bf16=True)
+    x["Q"][:, :C] = 0.0                            # block 0 of every head
+    n_valid = T // C
+    cfg = hga.make_config(Hq, Hkv, k, sink_chunks=sink)
+    Qd, Kd, Vd = to_dev_bf16(x["Q"]), to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    S = torch.empty((Hkv, n_valid, D), device="cuda")
+    hga.hga_summarize(cfg, Kd, 0, T, S)
+    S_ref = oracle.summarize(x["K"], C, 0, n_valid)
+    ids_ref, sigma = oracle.route(x["Q"], S_ref, p0, k, Hkv, want_scores=True, sink=64 * sink)
+    assert np.array_equal(ids_ref[:, 0], np.tile(np.arange(sink, sink + k), (Hkv, 1)))
+    for fused in (False, True):
+        ids = torch.full((Hkv, n_q // C, k), -7, dtype=torch.int32, device="cuda")
+        O = torch.full((Hq, n_q, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((Hq, n_q), float("nan"), device="cuda")
+        log(f"zero block, 2200 candidates, sink {sink}, fused {fused}")
+        if fused:
+            hga.hga_route_attend_fwd(cfg, Qd, Kd, Vd, p0, S, n_valid, ids, O, lse)
+        else:
+            hga.hga_route(cfg, Qd, p0, S, n_valid, ids)
+            hga.hga_attend_fwd(cfg, Qd, Kd, Vd, p0, ids, O, lse)
+        torch.cuda.synchronize()
+        got = ids.cpu().numpy()
+        np.testing.assert_array_equal(got[:, 0], ids_ref[:, 0])
+        check_ids(got, ids_ref, sigma, p0, sink_chunks=sink, where="zero block")
+        O_ref, lse_ref = oracle.attend_fwd(x["Q"], x["K"], x["V"], got, p0, sink=64 * sink)
+        check_close("zero block O", from_dev(O), O_ref)
+        check_close("zero block lse", from_dev(lse), lse_ref, atol=1e-3, rtol=0, rel_l2=None)
