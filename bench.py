@@ -17,6 +17,7 @@ and the 36-layer x 8-segment loop are timed separately and reported under
 "extra"; they are not part of the step.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+                    [--no-extra] [--kernel-loop NAME]
 """
 from __future__ import annotations
 
@@ -33,6 +34,9 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 C = 64
+# untimed steps enqueued before the W warm-up steps (about 5 ms of work at the
+# 16K layer): the clocks reach their steady state before the timed steps
+SETUP_STEPS = 100
 
 # HBM bytes the routing + attention kernel moves per launch at this
 # workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB
@@ -106,14 +110,15 @@ class HipTimer:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # (2000 steps time about 0.1 s: the GPU's clocks drop while the host
-    # synchronises before the timed region and take about a millisecond to
-    # return, which a 200-step window would count as several percent of it)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the backward and segment-loop timings")
+    ap.add_argument("--kernel-loop", default=None, choices=sorted(KERNEL_LOOPS),
+                    help="only launch one call N times back to back at one workload (for "
+                         "rocprofv3 kernel traces and counter passes) and exit")
+    ap.add_argument("--loop-launches", type=int, default=50)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy (x*1 elementwise) of MIB MiB five times (to scale HBM "
                          "byte counters against a kernel of known traffic) and exit")
@@ -195,6 +200,81 @@ def bwd_flops(ids: np.ndarray, n_q: int, G: int, D: int, p0: int, unit: int = C)
     return float(G * (6 * D * hist + 10 * D * act))
 
 
+KERNEL_LOOPS = {
+    "attend16k": "hga_attend_fwd at the 16K layer (ids from hga_route)",
+    "attend128k": "hga_attend_fwd at the 128K-history workload (ids from hga_route)",
+    "route_attend16k": "hga_route_attend_fwd at the 16K layer",
+    "summarize16k": "hga_summarize of the 16K layer's active segment",
+    "bwd16k": "hga_attend_bwd at the 16K backward workload",
+    "decode128k": "hga_route_decode + hga_attend_decode, one token after the 128K history",
+}
+
+
+def kernel_loop(torch, hga, inputs, name, n):
+    """Launch one call n times back to back (after 5 untimed launches and a
+    synchronize) and print what ran: a short program for rocprofv3."""
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
+
+    w = {"attend128k": inputs.LAYER128K, "decode128k": inputs.LAYER128K,
+         "bwd16k": inputs.BWD16K}.get(name, inputs.LAYER16K)
+    x = inputs.generate(w)
+    Q, K, V = up(x["Q"]), up(x["K"]), up(x["V"])
+    cfg = hga.make_config(w.Hq, w.Hkv, w.k)
+    nb = w.n_q // C
+    S = torch.zeros((w.Hkv, w.T // C, w.D), device=dev)
+    ids = torch.empty((w.Hkv, nb, w.k), dtype=torch.int32, device=dev)
+    O = torch.empty((w.Hq, w.n_q, w.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.Hq, w.n_q), device=dev)
+    if name == "summarize16k":
+        hga.hga_summarize(cfg, K, 0, w.p0, S)
+        run = hga.prepare("hga_summarize", cfg, K, w.p0, w.n_q, S)
+    elif name == "decode128k":
+        p0 = w.T - 1
+        n_closed = p0 // C
+        Qd = up(x["Q"][:, :1])
+        hga.hga_summarize(cfg, K, 0, n_closed * C, S)
+        dids = torch.empty((w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
+        Od = torch.empty((w.Hq, 1, w.D), dtype=torch.bfloat16, device=dev)
+        lsed = torch.empty((w.Hq, 1), device=dev)
+        ws = torch.empty(hga.hga_decode_workspace_bytes(cfg, p0, 1), dtype=torch.uint8,
+                         device=dev)
+        r = hga.prepare("hga_route_decode", cfg, Qd, p0, S, n_closed, dids, ws)
+        a = hga.prepare("hga_attend_decode", cfg, Qd, K, V, p0, dids, Od, lsed, ws)
+
+        def run():
+            r()
+            a()
+    else:
+        hga.hga_summarize(cfg, K, 0, w.T, S)
+        hga.hga_route(cfg, Q, w.p0, S, w.T // C, ids)
+        if name in ("attend16k", "attend128k"):
+            run = hga.prepare("hga_attend_fwd", cfg, Q, K, V, w.p0, ids, O, lse)
+        elif name == "route_attend16k":
+            run = hga.prepare("hga_route_attend_fwd", cfg, Q, K, V, w.p0, S, w.T // C, ids, O,
+                              lse)
+        else:   # bwd16k
+            hga.hga_attend_fwd(cfg, Q, K, V, w.p0, ids, O, lse)
+            dO = up(x["dO"])
+            dQ = torch.empty((w.Hq, w.n_q, w.D), device=dev)
+            dK = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+            dV = torch.empty((w.Hkv, w.n_q, w.D), device=dev)
+            ws = torch.empty(hga.hga_attend_bwd_workspace_bytes(cfg, w.n_q), dtype=torch.uint8,
+                             device=dev)
+            run = hga.prepare("hga_attend_bwd", cfg, Q, K, V, w.p0, ids, O, lse, dO, dQ, dK,
+                              dV, ws)
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    for _ in range(n):
+        run()
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_loop": name, "what": KERNEL_LOOPS[name], "workload": w.name,
+                      "launches": n}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -218,6 +298,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4}))
         return
     hga.lib()    # raises if libhga.so is missing: no fallback
+    if args.kernel_loop:
+        kernel_loop(torch, hga, inputs, args.kernel_loop, args.loop_launches)
+        return
 
     w = inputs.LAYER16K
     x = inputs.generate(w)
@@ -237,56 +320,64 @@ def main():
     hga.hga_summarize(cfg, K, 0, w.p0, S)          # history summaries: outside the step
     n_valid = (w.p0 + w.n_q) // C
 
-    # Arguments are marshalled once; each step makes the two C calls. HIP
-    # event pairs on the launch stream time single kernels on a sample of the
-    # timed steps (the routing + attention kernel on every 32nd step, summarize
-    # on another): an event pair around every kernel of every step would
-    # itself add to the step.
+    # Arguments are marshalled once; each step makes the two C calls.
     run_sum = hga.prepare("hga_summarize", cfg, K, w.p0, w.n_q, S)
     run_fused = hga.prepare("hga_route_attend_fwd", cfg, Q, K, V, w.p0, S, n_valid, ids, O, lse)
-    SAMPLE = 32
-    which = {0: "route_attend", 16: "summarize"}
-    ev = {name: [] for name in ("summarize", "route_attend")}
     timer = HipTimer()
     stream = torch.cuda.current_stream().cuda_stream      # the stream the calls launch on
-    pairs = [(timer.event(), timer.event()) if which.get(i % SAMPLE) else None
-             for i in range(args.steps)]
 
-    def step(i=None):
-        name = which.get(i % SAMPLE) if i is not None else None
-        e = pairs[i] if name else None
-        if name == "summarize": timer.record(e[0], stream)
+    def step():
         run_sum()
-        if name == "summarize": timer.record(e[1], stream)
-        if name == "route_attend": timer.record(e[0], stream)
         run_fused()
-        if name == "route_attend": timer.record(e[1], stream)
-        if name:
-            ev[name].append(e)
 
-    # Set-up: the first launches of each kernel load its code object and the
-    # clocks ramp up (single launches of several hundred microseconds were
-    # seen); 100 untimed steps settle that before the warm-up steps.
-    for _ in range(100):
+    # Code objects load on the first launches; after this synchronize the
+    # rest of the run is enqueued without a host wait, so the GPU never idles
+    # (an idle GPU lowers its clocks, and they take about a millisecond to
+    # return): set-up steps, then the W warm-up steps, then the K timed steps
+    # between two in-stream events, then the kernel-timing steps.
+    for _ in range(3):
         step()
     torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for _ in range(SETUP_STEPS):
+        step()
     for _ in range(args.warmup):
         step()
+    e_begin, e_end = timer.event(), timer.event()
+    timer.record(e_begin, stream)
+    for _ in range(args.steps):
+        step()
+    timer.record(e_end, stream)
+    # Kernel durations: HIP event pairs around each kernel of the next
+    # max(K, 16) steps (enqueued right behind the timed ones; an event pair
+    # costs step time, so none sits inside the timed region).
+    n_kern = max(args.steps, 16)
+    pairs = [((timer.event(), timer.event()), (timer.event(), timer.event()))
+             for _ in range(n_kern)]
+    for (es, ef) in pairs:
+        timer.record(es[0], stream)
+        run_sum()
+        timer.record(es[1], stream)
+        timer.record(ef[0], stream)
+        run_fused()
+        timer.record(ef[1], stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    ms = {k: (float(np.mean([timer.elapsed_ms(a, b) for a, b in v])) if v else None)
-          for k, v in ev.items()}
+    wall = time.perf_counter() - t_wall0
+    elapsed = timer.elapsed_ms(e_begin, e_end) * 1e-3
+    ms = {"summarize": float(np.mean([timer.elapsed_ms(a, b) for (a, b), _ in pairs])),
+          "route_attend": float(np.mean([timer.elapsed_ms(a, b) for _, (a, b) in pairs]))}
+    ms_per_step = elapsed / args.steps * 1e3
+    if ms["route_attend"] > ms_per_step:
+        print(f"bench.py: the routing + attention kernel's mean duration "
+              f"({ms['route_attend'] * 1e3:.2f} us over {n_kern} launches) exceeds the measured "
+              f"step ({ms_per_step * 1e3:.2f} us): the timing is inconsistent, no result printed",
+              file=sys.stderr)
+        sys.exit(3)
     ids_np = ids.cpu().numpy()
     flops = attend_flops(ids_np, w.n_q, w.G, w.D, w.p0)
     abytes = attend_bytes(ids_np, w.n_q, w.Hq, w.D, w.p0)
     launch_ms = ms["route_attend"]
     achieved = flops / (launch_ms * 1e-3) / 1e12
-    ms_per_step = elapsed / args.steps * 1e3
     value = w.n_q * args.steps / elapsed
 
     out = {
@@ -314,6 +405,11 @@ def main():
             "traffic": measured_traffic_bytes(),
         },
         "kernels_ms": ms,
+        "timing": {"step": "in-stream HIP events around the K timed steps, enqueued right "
+                           "behind the warm-up steps with no host wait in between",
+                   "kernels": f"HIP event pairs around each kernel of {n_kern} further steps",
+                   "setup_steps": SETUP_STEPS,
+                   "wall_s_setup_warmup_timed_kernel_steps": wall},
         "attend_algorithmic": {"flops": flops, "bytes": abytes,
                                "executed_flops": attend_flops_executed(ids_np, w.G, w.D, w.p0),
                                "gathered_GBps": abytes / (launch_ms * 1e-3) / 1e9,
@@ -678,18 +774,42 @@ def segloop_timing(torch, hga, inputs, dev):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b)
+    # every one of the 36 layers processes all 16384 query tokens once
     return {"segloop_36x8_ms": ms,
-            "segloop_query_tokens_per_s_per_layer": w.T * inputs.SEGLOOP_LAYERS / (ms * 1e-3) /
-                                                     inputs.SEGLOOP_LAYERS}
+            "segloop_query_tokens_per_s_per_layer": w.T * inputs.SEGLOOP_LAYERS / (ms * 1e-3),
+            "segloop_query_tokens_per_s_whole_stack": w.T / (ms * 1e-3)}
+
+
+def host_cpu():
+    """What the host offers: its logical CPU count (nproc), the CPUs this
+    process may run on, and the CPU model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"), "model": model}
 
 
 def cpu_baseline(inputs, w, x):
     """The CPU oracle (plain C, fp64, OpenMP over output rows) on the same
     workload: summaries of the active segment, routing of every block and
     attention of every query, repeated for about 10 s; the median pass gives
-    the rate."""
+    the rate. Threads: every CPU this process may use, capped by
+    OMP_NUM_THREADS when the host sets it (GPU hosts that share their CPUs
+    between GPUs set it to each GPU's share)."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
+    cpu = host_cpu()
+    threads = cpu["affinity_cpus"]
+    if cpu["omp_num_threads_env"]:
+        try:
+            threads = min(threads, int(cpu["omp_num_threads_env"]))
+        except ValueError:
+            pass
     oracle.set_threads(threads)
     n_cap = w.T // C
     S = oracle.summarize(x["K"], C, 0, w.p0 // C, n_cap=n_cap)
@@ -709,7 +829,14 @@ def cpu_baseline(inputs, w, x):
             "kind": "oracle",
             "sample": f"the full {w.name} forward (active-segment summaries, routing of all "
                       f"{w.n_blocks} blocks, attention of all {w.n_q} queries x {w.Hq} heads), "
-                      f"median of {len(times)} passes, {sum(times):.1f} s in total"}
+                      f"median of {len(times)} passes, {sum(times):.1f} s in total",
+            "host": cpu,
+            "context": {"note": "the pages' end-to-end QLoRA training throughput of Qwen3-8B "
+                                "at 2,048 tokens on one Quadro RTX 5000 (gist.science "
+                                "technical summary 4.2; the authors' abstract); another "
+                                "machine and another measure, quoted for context only",
+                        "hga_training_tokens_per_s": 217.75,
+                        "dense_training_tokens_per_s": 207.02}}
 
 
 if __name__ == "__main__":
