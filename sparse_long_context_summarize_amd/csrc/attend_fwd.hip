@@ -20,9 +20,14 @@
 //                            so that each operand is one 16-byte read.
 // The S^T accumulator's row order (8*(j/4) + 4*(lane/32) + j%4) fixes which
 // keys each lane's P^T operand holds; store_v places V's keys in that order.
-// The running max is rescaled lazily: O^T and the row sum are only rescaled
-// when some row's max grows by more than 8 (log2 units), otherwise the stale
-// max stays and probabilities up to 2^8 enter the bf16 operand unchanged.
+// The softmax needs no row maximum per tile: probabilities are taken against
+// the running maximum as it stands, p = 2^(s*c - m), and only when a row's
+// tile sum of p exceeds 2^16 (or is not finite) is the exact maximum taken,
+// O^T and the row sum rescaled and p recomputed. Every p that enters the bf16
+// operand is then at most 2^16, so O^T and the row sums keep their fp32
+// relative precision; m starts at -FLT_MAX, so the first (local) tile always
+// takes the exact path. This keeps the max reduction, and its wait on the
+// last S^T MFMA, off the MFMA half-step.
 //
 // Chunk tiles (32 KiB of K and V) are loaded ahead into registers (16-byte
 // coalesced loads, a 256-byte key row per 16 lanes) and written to a
@@ -37,45 +42,31 @@
 // Per-query-head routing (one id row per query head) runs the G = 1 kernel
 // with kv_div = query heads per kv head: each query head is then its own
 // unit, reading its own id row and its kv head's K and V.
+#include "attend_tiles.h"
 #include "route_core.h"
 
+#include <float.h>
 #include <type_traits>
 
 namespace hga {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kKStride = kD + 8;            // bf16 per K row in LDS (272 B)
-constexpr int kVtStride = kC + 8;           // bf16 per V^T row (one d) in LDS (144 B)
-constexpr int kKTile = kC * kKStride;       // elements
-constexpr int kVtTile = kD * kVtStride;     // elements
-constexpr int kPieces = kC * kD * 2 * 2 / 16 / kThreads;      // 16-byte pieces per thread
-constexpr float kLazy = 8.0f;               // log2 growth that forces a rescale
-// s_waitcnt immediates (gfx9 encoding).
-constexpr int kWaitVm8 = 0x0F78;       // vector memory count 8, others no wait
-constexpr int kWaitLgkm0 = 0xC07F;     // LDS/scalar count 0, others no wait
-constexpr int kOStride = 136;          // output staging row: 128 bf16 + 8 pad
+constexpr int kPieces = kTilePieces;
+constexpr float kSumLimit = 65536.0f;       // tile row sum that forces an exact rescale
 constexpr int kLook = 6;                // MFMA operands read this many MFMAs ahead
 
-static_assert(kPieces == 4, "tile loader assumes 4 pieces per thread");
+static_assert(kPieces * 16 * kThreads / 2 == kC * kD * 2, "one loader group moves one tile");
 
 // Tile loaders. Waves 4-7 ("K group") move K tiles, waves 0-3 ("V group")
 // move V tiles; each thread holds four 16-byte pieces of one tile.
-struct TileRegs {
-    u32x4 p[kPieces];
-};
-
 // The loaders take the first token of a chunk tile (consecutive rows), or
 // row_tok(r), the token of tile row r (0..63), for a tile whose rows come 8 at
 // a time from its groups.
-// K group, u = thread - 256: piece j is key row 16*j + u/16, d = 8*(u%16) .. +8
-// (each load instruction reads four 256-B rows).
+// K group, u = thread - 256 (see load_k_rows).
 __device__ __forceinline__ void load_k(TileRegs &tr, const uint16_t *Kg, int64_t tok0)
 {
-    const int u = threadIdx.x - kThreads / 2;
-    const uint16_t *src = Kg + (tok0 + (u >> 4)) * kD + (u & 15) * 8;
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + 16 * j * kD);
+    load_k_rows(tr, Kg, tok0, (int)threadIdx.x - kThreads / 2);
 }
 
 // Group tiles: the K group thread takes rows r0 + 2*j of one 8-row group,
@@ -102,21 +93,13 @@ __device__ __forceinline__ void store_k_grp(const TileRegs &tr, uint16_t *Ks)
 
 __device__ __forceinline__ void store_k(const TileRegs &tr, uint16_t *Ks)
 {
-    const int u = threadIdx.x - kThreads / 2;
-    uint16_t *dst = Ks + (u >> 4) * kKStride + (u & 15) * 8;
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) *(u32x4 *)(dst + 16 * j * kKStride) = tr.p[j];
+    store_k_rows(tr, Ks, (int)threadIdx.x - kThreads / 2);
 }
 
-// V group, u = thread: lane takes keys 4*kg .. 4*kg+3 of the 8-wide d slice
-// dp, kg = lane%16, dp = 4*(u/64) + lane/16; piece j is key 4*kg + j.
+// V group, u = thread (see load_v_rows).
 __device__ __forceinline__ void load_v(TileRegs &tr, const uint16_t *Vg, int64_t tok0)
 {
-    const int u = threadIdx.x, lane = u & 63;
-    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
-    const uint16_t *src = Vg + (tok0 + 4 * kg) * kD + dp * 8;
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + j * kD);
+    load_v_rows(tr, Vg, tok0, (int)threadIdx.x);
 }
 
 // (rows 4*kg .. 4*kg+3 lie in one 8-row group, so one row_tok call serves them)
@@ -130,37 +113,10 @@ __device__ __forceinline__ void load_v(TileRegs &tr, const uint16_t *Vg, RowTok 
     for (int j = 0; j < kPieces; ++j) tr.p[j] = *(const u32x4 *)(src + j * kD);
 }
 
-// V goes to LDS transposed, V^T[d][pos], where within each 16-key group
-// position 8*h + 4*u + m holds key 8*u + 4*h + m: then the 8 keys that lane l
-// needs for one P^T operand (keys 16*ks + 8*u + 4*(l/32) + m, the S^T
-// accumulator's row order) sit at 8 consecutive positions, one 16-byte read.
-// The 4 keys x 8 d block a lane holds is transposed in registers (byte
-// permutes) and written as 8 rows of 4 keys; with kg = lane%16 the 64 lanes'
-// 8-byte writes fall on distinct banks.
+// V goes to LDS transposed (see store_v_rows).
 __device__ __forceinline__ void store_v(const TileRegs &tr, uint16_t *Vt)
 {
-    const int u = threadIdx.x, lane = u & 63;
-    const int kg = lane & 15, dp = 4 * (u >> 6) + (lane >> 4);
-    const int pos = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-    uint16_t *dst = Vt + (8 * dp) * kVtStride + pos;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        // element e of each key's 8-wide slice is the low (e even) or high
-        // half of dword e/2; keys (0,1) and (2,3) pack into two dwords.
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 w;
-        w[0] = __builtin_amdgcn_perm(tr.p[1][e >> 1], tr.p[0][e >> 1], sel);
-        w[1] = __builtin_amdgcn_perm(tr.p[3][e >> 1], tr.p[2][e >> 1], sel);
-        *(u32x2 *)(dst + e * kVtStride) = w;
-    }
-}
-
-// A operand V^T[d][key] for d-tile dt, k-step ks: lane gets d = 32*dt + lane%32
-// and keys 16*ks + 8*u + 4*(lane/32) + m (element 4u + m), matching the key
-// order of the P^T operand taken from the S^T accumulators.
-__device__ __forceinline__ bf16x8 vt_operand(const uint16_t *Vt, int dt, int ks, int lane)
-{
-    return *(const bf16x8 *)(Vt + (32 * dt + (lane & 31)) * kVtStride + 16 * ks + 8 * (lane >> 5));
+    store_v_rows(tr, Vt, (int)threadIdx.x);
 }
 
 // kUnit = kC: ids are chunk ids, one tile per routed chunk. kUnit = kGroup:
@@ -393,7 +349,7 @@ void attend_fwd_kernel(
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -FLT_MAX, l_run = 0.f;
     f32x16 s[2];        // S^T of a tile, from its MFMA half-step to its softmax
     bf16x8 pb[4];       // P^T of a tile, from its softmax to the next MFMA half-step
 
@@ -442,6 +398,8 @@ void attend_fwd_kernel(
     // online softmax in the log2 domain with a lazy rescale, P^T to bf16.
     auto va = [&](int t) __attribute__((always_inline)) {
         if (!computes) return;
+        // (keeps this half-step's arithmetic behind the barrier before it)
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]));
         if (t == 0) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -460,24 +418,9 @@ void attend_fwd_kernel(
                     if (key >= n_keys) s[kt][j] = -INFINITY;
                 }
         }
-        // (four independent max / sum chains keep the VALU pipeline full)
-        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) m4[j & 3] = fmaxf(m4[j & 3], s[kt][j]);
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = fmaxf(mx, partner32(mx)) * scale_log2;
-        if (__ballot(mx > m_run + kLazy) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-        }
+        // Probabilities against the running maximum as it stands; the exact
+        // maximum is only taken when a row's tile sum leaves [0, 2^16] (or is
+        // not finite), which also covers the first tile (m_run = -FLT_MAX).
         float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -487,7 +430,38 @@ void attend_fwd_kernel(
                 ps4[j & 3] += p;
                 pb[2 * kt + (j >> 3)][j & 7] = (__bf16)p;
             }
-        l_run += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+        float ls = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pb[kk]));
+        const float row = ls + partner32(ls);
+        if (__ballot(!(row <= kSumLimit)) != 0) {
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) m4[j & 3] = fmaxf(m4[j & 3], s[kt][j]);
+            float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            mx = fmaxf(mx, partner32(mx)) * scale_log2;
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+            float qs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][j], scale_log2, -m_new));
+                    qs4[j & 3] += p;
+                    pb[2 * kt + (j >> 3)][j & 7] = (__bf16)p;
+                }
+            ls = (qs4[0] + qs4[1]) + (qs4[2] + qs4[3]);
+        }
+        l_run += ls;
     };
 
     // Loader duties, in the group's softmax half-steps. V group, tile t: V(t)

@@ -145,16 +145,14 @@ def test_layer16k():
     full_check(x, w.p0, w.k, res, where="layer16k")
 
 
-def test_layer128k_sampled():
+def test_layer128k():
+    """The 128K-history workload: summaries, every id row, and every output
+    row of every (block, query head) unit against the oracle."""
     w = inputs.LAYER128K
     log(f"layer128k: {w}")
     x = inputs.generate(w)
     res = gpu_forward(x, w.p0, w.k)
-    rng = np.random.default_rng(123)
-    mask = (rng.random((w.Hq, w.n_blocks)) < 1 / 16).astype(np.uint8)
-    mask[:, 0] = 1
-    mask[:, -1] = 1
-    full_check(x, w.p0, w.k, res, unit_mask=mask, where="layer128k")
+    full_check(x, w.p0, w.k, res, where="layer128k")
 
 
 def test_determinism_layer16k():
@@ -215,6 +213,45 @@ def _segment_layers(layers):
 @pytest.mark.parametrize("group", range(6))
 def test_segment_loop(group):
     _segment_layers(range(6 * group, 6 * group + 6))
+
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_segment_loop_fused_every_unit(layer):
+    """One layer of the segment loop through the calls the benchmark times:
+    hga_summarize appends the segment's chunks, then hga_route_attend_fwd
+    routes and attends in one launch; summaries, ids, scores and every row of
+    O and lse of all 8 segments are compared with the oracle."""
+    w = inputs.seg_layer_workload(layer)
+    x = inputs.generate(w)
+    Hq, Hkv, D = w.Hq, w.Hkv, w.D
+    cfg = hga.make_config(Hq, Hkv, w.k)
+    Kd, Vd, Qd = to_dev_bf16(x["K"]), to_dev_bf16(x["V"]), to_dev_bf16(x["Q"])
+    n_cap = w.T // C
+    S = torch.full((Hkv, n_cap, D), float("nan"), device="cuda")
+    S_ref = oracle.summarize(x["K"], C, 0, n_cap)
+    for s in range(inputs.SEGLOOP_SEGMENTS):
+        p0 = s * inputs.SEGLOOP_SEG_LEN
+        n_q = inputs.SEGLOOP_SEG_LEN
+        nb = n_q // C
+        Qs = Qd[:, p0:p0 + n_q].contiguous()
+        where = f"segloop fused layer {layer} seg {s}"
+        log(where)
+        hga.hga_summarize(cfg, Kd, p0, n_q, S)
+        ids = torch.full((Hkv, nb, w.k), -7, dtype=torch.int32, device="cuda")
+        scores = torch.full((Hkv, nb, w.k), float("nan"), device="cuda")
+        O = torch.full((Hq, n_q, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((Hq, n_q), float("nan"), device="cuda")
+        hga.hga_route_attend_fwd(cfg, Qs, Kd, Vd, p0, S, (p0 + n_q) // C, ids, O, lse, scores)
+        torch.cuda.synchronize()
+        Sg = from_dev(S)
+        rows = slice(p0 // C, (p0 + n_q) // C)
+        err = np.abs(Sg[:, rows] - S_ref[:, rows])
+        assert np.all(err <= summary_bound(x["K"], rows.start, rows.stop)), where
+        xs = dict(Q=x["Q"][:, p0:p0 + n_q], K=x["K"], V=x["V"])
+        res = dict(ids=ids.cpu().numpy(), scores=from_dev(scores), O=from_dev(O),
+                   lse=from_dev(lse))
+        check_route(xs, res, S_ref, p0, w.k, where)
+        check_attend(xs, res, p0, None, where)
 
 
 # ----------------------------------------------------------------- edge cases
