@@ -5,7 +5,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "hga_internal.h"
+
+// The workspace of hga_attend_bwd_noalloc: one file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends. Host
+// code never passes this name to a kernel (on the host it is only a stand-in
+// for the symbol): it uses the device address that hipGetSymbolAddress
+// returns for the current device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[HGA_BWD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -103,6 +112,72 @@ hga_status check_segment(int64_t p0, int64_t n_q, int64_t T_cap, bool need_T)
     if (n_q / hga::kC > 65535)      // one launch's grid holds the query blocks
         return fail(HGA_ERR_UNSUPPORTED, "n_q (%lld) exceeds 65535 query blocks of %d",
                     (long long)n_q, hga::kC);
+    return HGA_OK;
+}
+
+// hga_attend_bwd's checks and launch, on a given workspace.
+hga_status attend_bwd_checked(const hga_config *cfg, const void *Q, const void *K,
+                              const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                              const int32_t *ids, const void *O, const float *lse,
+                              const void *dO, float *dQ, float *dK_active, float *dV_active,
+                              void *workspace, size_t ws_bytes, hipStream_t stream,
+                              const char *what)
+{
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    st = check_segment(p0, n_q, T_cap, true);
+    if (st != HGA_OK) return st;
+    if (n_q == 0) return HGA_OK;
+    if (n_q > hga::bwd_max_queries())
+        return fail(HGA_ERR_UNSUPPORTED, "backward supports at most %lld active queries",
+                    (long long)hga::bwd_max_queries());
+    if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
+        (cfg->top_k > 0 && !ids))
+        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q,
+                                                 per_q_head(cfg));
+    if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    if (ws_bytes < need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    return hip_status(hga::launch_attend_bwd((const uint16_t *)Q, (const uint16_t *)K,
+                                             (const uint16_t *)V, cfg->n_q_heads,
+                                             cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
+                                             cfg->sink_chunks, per_q_head(cfg),
+                                             effective_scale(cfg), (const uint16_t *)O, lse,
+                                             (const uint16_t *)dO, dQ, dK_active, dV_active,
+                                             workspace, stream),
+                      what);
+}
+
+// Device address of `scratch` on the device of `stream`, looked up once per
+// device (with that device current) and kept. The stream's device must be
+// the current one.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices];
+
+hga_status scratch_address(hipStream_t stream, void **out)
+{
+    int dev = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+        return fail(HGA_ERR_INVALID_ARG, "the stream belongs to device %d, the current device is %d",
+                    sdev, dev);
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(HGA_ERR_UNSUPPORTED, "device %d: the scratch table covers devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(HGA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
     return HGA_OK;
 }
 
@@ -608,30 +683,35 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K, c
                           hipStream_t stream)
 {
     g_last_error[0] = '\0';
+    return attend_bwd_checked(cfg, Q, K, V, T_cap, p0, n_q, ids, O, lse, dO, dQ, dK_active,
+                              dV_active, workspace, ws_bytes, stream, "hga_attend_bwd launch");
+}
+
+hga_status hga_attend_bwd_noalloc(const hga_config *cfg, const void *Q, const void *K,
+                                  const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                  const int32_t *ids, const void *O, const float *lse,
+                                  const void *dO, float *dQ, float *dK_active,
+                                  float *dV_active, hipStream_t stream)
+{
+    g_last_error[0] = '\0';
     hga_status st = check_config(cfg);
     if (st != HGA_OK) return st;
     st = check_segment(p0, n_q, T_cap, true);
     if (st != HGA_OK) return st;
     if (n_q == 0) return HGA_OK;
-    if (n_q > hga::bwd_max_queries())
-        return fail(HGA_ERR_UNSUPPORTED, "backward supports at most %lld active queries",
-                    (long long)hga::bwd_max_queries());
-    if (!Q || !K || !V || !lse || !dO || !dQ || !dK_active || !dV_active ||
-        (cfg->top_k > 0 && !ids))
-        return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
     const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q,
                                                  per_q_head(cfg));
-    if (need > 0 && !workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
-    if (ws_bytes < need)
-        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
-    return hip_status(hga::launch_attend_bwd((const uint16_t *)Q, (const uint16_t *)K,
-                                             (const uint16_t *)V, cfg->n_q_heads,
-                                             cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
-                                             cfg->sink_chunks, per_q_head(cfg),
-                                             effective_scale(cfg), (const uint16_t *)O, lse,
-                                             (const uint16_t *)dO, dQ, dK_active, dV_active,
-                                             workspace, stream),
-                      "hga_attend_bwd launch");
+    if (need > (size_t)HGA_BWD_NOALLOC_SCRATCH_BYTES)
+        return fail(HGA_ERR_CAPACITY,
+                    "hga_attend_bwd_noalloc: this call needs %zu bytes of workspace, the "
+                    "library's fixed scratch holds %zu (use hga_attend_bwd with a caller "
+                    "workspace)", need, (size_t)HGA_BWD_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    st = scratch_address(stream, &ws);
+    if (st != HGA_OK) return st;
+    return attend_bwd_checked(cfg, Q, K, V, T_cap, p0, n_q, ids, O, lse, dO, dQ, dK_active,
+                              dV_active, ws, (size_t)HGA_BWD_NOALLOC_SCRATCH_BYTES, stream,
+                              "hga_attend_bwd_noalloc launch");
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@ HGA_BF16 = 0
 
 EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
             "hga_route_attend_fwd",
-            "hga_attend_bwd_workspace_bytes", "hga_attend_bwd",
+            "hga_attend_bwd_workspace_bytes", "hga_attend_bwd", "hga_attend_bwd_noalloc",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
             "hga_route_attend_fwd_groups",
             "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
@@ -33,6 +33,7 @@ HGA_GROUP = 8
 HGA_MAX_SINK_CHUNKS = 64
 HGA_ROUTE_PER_KV_HEAD = 0
 HGA_ROUTE_PER_Q_HEAD = 1
+HGA_BWD_NOALLOC_SCRATCH_BYTES = 40 * 1024 * 1024
 
 
 class hga_config(ctypes.Structure):
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.hga_attend_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.hga_attend_bwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    L.hga_attend_bwd_noalloc.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp]
     L.hga_route_attend_fwd.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64,
                                        _vp, _vp, _vp, _vp, _vp]
     L.hga_summarize_groups.argtypes = [_cfgp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]
@@ -107,7 +110,7 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
     for fn in ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
-               "hga_attend_bwd",
+               "hga_attend_bwd", "hga_attend_bwd_noalloc",
                "hga_route_attend_fwd",
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
                "hga_route_attend_fwd_groups",
@@ -276,6 +279,24 @@ def _m_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV
             _dev(dV, "dV", torch.float32), workspace.data_ptr(), ws_bytes, _stream(stream))
 
 
+def _m_attend_bwd_noalloc(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV,
+                          stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _shape(ids, "ids", (_units(cfg), _blocks(cfg, n_q), cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
+    _shape(dO, "dO", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dQ, "dQ", (cfg.n_q_heads, n_q, cfg.head_dim))
+    _shape(dK, "dK", (cfg.n_kv_heads, n_q, cfg.head_dim))
+    _shape(dV, "dV", (cfg.n_kv_heads, n_q, cfg.head_dim))
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+            _dev(ids, "ids", torch.int32), _dev(O, "O", torch.bfloat16),
+            _dev(lse, "lse", torch.float32), _dev(dO, "dO", torch.bfloat16),
+            _dev(dQ, "dQ", torch.float32), _dev(dK, "dK", torch.float32),
+            _dev(dV, "dV", torch.float32), _stream(stream))
+
+
 def _m_route_attend_fwd(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int, ids,
                         O, lse, scores=None, stream=None):
     n_q = _q_shapes(cfg, Q)
@@ -416,6 +437,7 @@ def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=N
 _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_route_causal": _m_route_causal,
             "hga_attend_fwd": _m_attend_fwd, "hga_attend_bwd": _m_attend_bwd,
+            "hga_attend_bwd_noalloc": _m_attend_bwd_noalloc,
             "hga_route_attend_fwd": _m_route_attend_fwd,
             "hga_summarize_groups": _m_summarize_groups, "hga_route_groups": _m_route_groups,
             "hga_attend_fwd_groups": _m_attend_fwd_groups,
@@ -467,6 +489,13 @@ def hga_attend_bwd(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, d
     """dQ f32 [Hq][n_q][D]; dK, dV f32 [Hkv][n_q][D] (active keys) are written."""
     _check("hga_attend_bwd", lib().hga_attend_bwd(
         *_m_attend_bwd(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, workspace, stream)))
+
+
+def hga_attend_bwd_noalloc(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, dO, dQ, dK, dV,
+                           stream=None) -> None:
+    """hga_attend_bwd on the library's fixed scratch (no workspace argument)."""
+    _check("hga_attend_bwd_noalloc", lib().hga_attend_bwd_noalloc(
+        *_m_attend_bwd_noalloc(cfg, Q, K, V, p0, ids, O, lse, dO, dQ, dK, dV, stream)))
 
 
 def hga_route_attend_fwd(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
