@@ -14,8 +14,10 @@
  *     D = 128, chunk C = 64, query block Bq = C, top-k k. Query head h uses
  *     key/value head h / G.
  *   - All buffers are caller-owned, contiguous device memory. The library
- *     never allocates or frees device memory and keeps no global mutable
- *     state apart from a thread-local error string; it is reentrant.
+ *     never allocates or frees device memory. Its only global state is a
+ *     thread-local error string and, for hga_attend_bwd_noalloc, a static
+ *     device scratch array with a mutex-guarded table of its per-device
+ *     addresses; every other call is reentrant.
  *   - Layouts (row-major, innermost last):
  *       Q, O, dO        bf16  [Hq][n_q][D]      active queries p0 .. p0+n_q-1
  *       K, V            bf16  [Hkv][T_cap][D]   every position 0 .. T_cap-1
