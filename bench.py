@@ -210,6 +210,7 @@ KERNEL_LOOPS = {
     "summarize16k": "hga_summarize of the 16K layer's active segment",
     "bwd16k": "hga_attend_bwd at the 16K backward workload",
     "decode128k": "hga_route_decode + hga_attend_decode, one token after the 128K history",
+    "decode128k_fused": "hga_route_attend_decode, one token after the 128K history",
 }
 
 
@@ -222,7 +223,8 @@ def kernel_loop(torch, hga, inputs, name, n):
         return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(dev)
 
     w = {"attend128k": inputs.LAYER128K, "decode128k": inputs.LAYER128K,
-         "bwd16k": inputs.BWD16K}.get(name, inputs.LAYER16K)
+         "decode128k_fused": inputs.LAYER128K, "bwd16k": inputs.BWD16K}.get(name,
+                                                                          inputs.LAYER16K)
     x = inputs.generate(w)
     Q, K, V = up(x["Q"]), up(x["K"]), up(x["V"])
     cfg = hga.make_config(w.Hq, w.Hkv, w.k)
@@ -234,7 +236,7 @@ def kernel_loop(torch, hga, inputs, name, n):
     if name == "summarize16k":
         hga.hga_summarize(cfg, K, 0, w.p0, S)
         run = hga.prepare("hga_summarize", cfg, K, w.p0, w.n_q, S)
-    elif name == "decode128k":
+    elif name in ("decode128k", "decode128k_fused"):
         p0 = w.T - 1
         n_closed = p0 // C
         Qd = up(x["Q"][:, :1])
@@ -242,14 +244,20 @@ def kernel_loop(torch, hga, inputs, name, n):
         dids = torch.empty((w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
         Od = torch.empty((w.Hq, 1, w.D), dtype=torch.bfloat16, device=dev)
         lsed = torch.empty((w.Hq, 1), device=dev)
-        ws = torch.empty(hga.hga_decode_workspace_bytes(cfg, p0, 1), dtype=torch.uint8,
-                         device=dev)
-        r = hga.prepare("hga_route_decode", cfg, Qd, p0, S, n_closed, dids, ws)
-        a = hga.prepare("hga_attend_decode", cfg, Qd, K, V, p0, dids, Od, lsed, ws)
+        if name == "decode128k_fused":
+            ws = torch.empty(hga.hga_route_attend_decode_workspace_bytes(cfg, p0, 1),
+                             dtype=torch.uint8, device=dev)
+            run = hga.prepare("hga_route_attend_decode", cfg, Qd, K, V, p0, S, n_closed, dids,
+                              Od, lsed, ws)
+        else:
+            ws = torch.empty(hga.hga_decode_workspace_bytes(cfg, p0, 1), dtype=torch.uint8,
+                             device=dev)
+            r = hga.prepare("hga_route_decode", cfg, Qd, p0, S, n_closed, dids, ws)
+            a = hga.prepare("hga_attend_decode", cfg, Qd, K, V, p0, dids, Od, lsed, ws)
 
-        def run():
-            r()
-            a()
+            def run():
+                r()
+                a()
     else:
         hga.hga_summarize(cfg, K, 0, w.T, S)
         hga.hga_route(cfg, Q, w.p0, S, w.T // C, ids)
@@ -692,7 +700,8 @@ def variant_timings(torch, hga, inputs, dev):
 def decode_timings(torch, hga, inputs, dev):
     """Routed decode at batch 1: one token after the 128K-history workload's
     last position (k = 32) and 8 tokens after the 16K layer's (k = 16), each
-    call and the step (route + attend) HIP-event timed (median of 10).
+    call HIP-event timed (median of 10): the routing and the attention calls,
+    the two in turn, and the step as one hga_route_attend_decode call.
     Algorithmic bytes: the summaries each token scores, its routed and open
     chunks' K and V (bf16), Q read and O written."""
     res = {}
@@ -717,13 +726,18 @@ def decode_timings(torch, hga, inputs, dev):
                          device=dev)
         route = hga.prepare("hga_route_decode", cfg, Q, p0, S, n_closed, ids, ws)
         attend = hga.prepare("hga_attend_decode", cfg, Q, K, V, p0, ids, O, lse, ws)
+        ws_f = torch.empty(hga.hga_route_attend_decode_workspace_bytes(cfg, p0, n_q),
+                           dtype=torch.uint8, device=dev)
+        step = hga.prepare("hga_route_attend_decode", cfg, Q, K, V, p0, S, n_closed, ids, O,
+                           lse, ws_f)
 
-        def step():
+        def two_calls():
             route()
             attend()
 
         t_route = _median_ms(torch, route)
         t_att = _median_ms(torch, attend)
+        t_two = _median_ms(torch, two_calls)
         t_step = _median_ms(torch, step)
         toks = p0 + np.arange(n_q)
         n_sum = float(sum(t // C for t in toks)) * w.Hkv
@@ -733,6 +747,7 @@ def decode_timings(torch, hga, inputs, dev):
         res.update({
             f"{tag}_route_us": t_route * 1e3,
             f"{tag}_attend_us": t_att * 1e3,
+            f"{tag}_two_calls_us": t_two * 1e3,
             f"{tag}_step_us": t_step * 1e3,
             f"{tag}_tokens_per_s": n_q / (t_step * 1e-3),
             f"{tag}_algorithmic_MB": (route_bytes + att_bytes) / 1e6,

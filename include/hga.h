@@ -425,6 +425,31 @@ hga_status hga_attend_decode(const hga_config *cfg, const void *Q, const void *K
                              int64_t T_cap, int64_t p0, int64_t n_q, const int32_t *ids, void *O,
                              float *lse, void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * hga_route_attend_decode -- hga_route_decode followed by hga_attend_decode in
+ * one call (three launches instead of four): ids, scores_or_null, O and lse
+ * are written exactly as those two calls write them, bit for bit. The routing
+ * keeps, per block of 256 candidates, that block's top k; every attention
+ * split then selects the top k among those survivors itself, and the splits'
+ * partials are merged as hga_attend_decode merges them.
+ *   Arguments as for hga_route_decode and hga_attend_decode; ids may be NULL
+ *   only when top_k == 0 (then summaries is not read either).
+ *   workspace  device scratch of at least
+ *            hga_route_attend_decode_workspace_bytes(cfg, p0, n_q) bytes, else
+ *            HGA_ERR_CAPACITY; owned by the caller, contents on entry
+ *            ignored; calls that share it must not overlap in time.
+ *   HGA_ERR_UNSUPPORTED when the blocks' survivors (256-candidate blocks of
+ *   the last token times top_k) exceed 12288; the two separate calls take
+ *   those sizes.
+ */
+size_t hga_route_attend_decode_workspace_bytes(const hga_config *cfg, int64_t p0, int64_t n_q);
+hga_status hga_route_attend_decode(const hga_config *cfg, const void *Q, const void *K,
+                                   const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
+                                   const float *summaries, int64_t n_chunk_cap,
+                                   int64_t n_chunks_valid, int32_t *ids, float *scores_or_null,
+                                   void *O, float *lse, void *workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Diagnostic (not a step of the method).
  * ---------------------------------------------------------------------- */

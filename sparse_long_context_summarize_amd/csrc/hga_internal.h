@@ -190,6 +190,20 @@ hipError_t launch_attend_decode(const uint16_t *Q, const uint16_t *K, const uint
                                 int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,
                                 float scale, uint16_t *O, float *lse, void *workspace,
                                 hipStream_t stream);
+// The decode step's routing and attention in two launches (ids, scores, O and
+// lse equal to launch_route_decode + launch_attend_decode); its own workspace
+// size. route_attend_decode_fits: false when the survivors of the last token's
+// scoring blocks exceed what the attention kernel selects among.
+size_t route_attend_decode_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t p0, int64_t n_q,
+                                           int32_t k, int32_t sink);
+bool route_attend_decode_fits(int64_t Hq, int64_t Hkv, int64_t p0, int64_t n_q, int32_t k,
+                              int32_t sink);
+hipError_t launch_route_attend_decode(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                      int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
+                                      int64_t n_q, const float *S, int64_t n_cap, int32_t k,
+                                      int32_t sink, float scale, int32_t *ids, float *scores,
+                                      uint16_t *O, float *lse, void *workspace,
+                                      hipStream_t stream);
 // Gather-only diagnostic (diag.hip): sink holds gather_sink_words words.
 hipError_t launch_gather(const uint16_t *K, const uint16_t *V, int64_t Hkv, int64_t T_cap,
                          int64_t p0, int64_t n_q, const int32_t *ids, int32_t k, int32_t sink,

@@ -27,7 +27,8 @@ EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
             "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
             "hga_route_attend_fwd_groups",
             "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
-            "hga_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
+            "hga_attend_decode", "hga_route_attend_decode_workspace_bytes",
+            "hga_route_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
             "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
 HGA_MAX_SINK_CHUNKS = 64
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.hga_decode_workspace_bytes.restype = ctypes.c_size_t
     L.hga_attend_decode.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                     ctypes.c_size_t, _vp]
+    L.hga_route_attend_decode_workspace_bytes.argtypes = [_cfgp, _i64, _i64]
+    L.hga_route_attend_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.hga_route_attend_decode.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64,
+                                          _i64, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     L.hga_diag_gather_sink_words.argtypes = [_cfgp, _i64]
     L.hga_diag_gather_sink_words.restype = ctypes.c_size_t
     L.hga_diag_gather.argtypes = [_cfgp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t,
@@ -115,7 +120,7 @@ def lib() -> ctypes.CDLL:
                "hga_summarize_groups", "hga_route_groups", "hga_attend_fwd_groups",
                "hga_route_attend_fwd_groups",
                "hga_attend_bwd_groups", "hga_diag_gather", "hga_route_decode",
-               "hga_attend_decode"):
+               "hga_attend_decode", "hga_route_attend_decode"):
         getattr(L, fn).restype = ctypes.c_int
     L.hga_status_string.argtypes = [ctypes.c_int]
     L.hga_status_string.restype = ctypes.c_char_p
@@ -310,7 +315,8 @@ def _m_route_attend_fwd(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_v
     if K.shape != V.shape:
         raise ValueError("K and V shapes differ")
     return (ctypes.byref(cfg), *args, K.shape[1], p0, Q.shape[1],
-            _dev(summaries, "summaries", torch.float32), summaries.shape[1], n_chunks_valid,
+            _dev(summaries, "summaries", torch.float32),
+            summaries.shape[1] if summaries is not None else 0, n_chunks_valid,
             _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
             _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32), _stream(stream))
 
@@ -426,6 +432,23 @@ def _m_attend_decode(cfg: hga_config, Q, K, V, p0: int, ids, O, lse, workspace, 
             workspace.numel() * workspace.element_size(), _stream(stream))
 
 
+def _m_route_attend_decode(cfg: hga_config, Q, K, V, p0: int, summaries, n_chunks_valid: int,
+                           ids, O, lse, workspace, scores=None, stream=None):
+    n_q = _q_shapes(cfg, Q)
+    _kv_shapes(cfg, K, V)
+    _summary_shapes(cfg, summaries)
+    _shape(ids, "ids", (cfg.n_kv_heads, n_q, cfg.top_k))
+    _shape(scores, "scores", (cfg.n_kv_heads, n_q, cfg.top_k))
+    _out_shapes(cfg, n_q, O, lse)
+    return (ctypes.byref(cfg), _dev(Q, "Q", torch.bfloat16), _dev(K, "K", torch.bfloat16),
+            _dev(V, "V", torch.bfloat16), K.shape[1], p0, Q.shape[1],
+            _dev(summaries, "summaries", torch.float32),
+            summaries.shape[1] if summaries is not None else 0, n_chunks_valid,
+            _dev(ids, "ids", torch.int32), _dev(scores, "scores", torch.float32),
+            _dev(O, "O", torch.bfloat16), _dev(lse, "lse", torch.float32),
+            *_workspace(workspace), _stream(stream))
+
+
 def _m_diag_gather(cfg: hga_config, K, V, p0: int, n_q: int, ids, sink, stream=None):
     _kv_shapes(cfg, K, V)
     _shape(ids, "ids", (cfg.n_kv_heads, _blocks(cfg, n_q), cfg.top_k))
@@ -444,7 +467,8 @@ _MARSHAL = {"hga_summarize": _m_summarize, "hga_route": _m_route,
             "hga_route_attend_fwd_groups": _m_route_attend_fwd_groups,
             "hga_attend_bwd_groups": _m_attend_bwd_groups,
             "hga_diag_gather": _m_diag_gather, "hga_route_decode": _m_route_decode,
-            "hga_attend_decode": _m_attend_decode}
+            "hga_attend_decode": _m_attend_decode,
+            "hga_route_attend_decode": _m_route_attend_decode}
 
 
 def hga_summarize(cfg: hga_config, K: torch.Tensor, tok_begin: int, n_tok: int,
@@ -577,6 +601,21 @@ def hga_attend_decode(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torc
     """Attention of a decode step (split over the routed chunks, then merged)."""
     _check("hga_attend_decode", lib().hga_attend_decode(
         *_m_attend_decode(cfg, Q, K, V, p0, ids, O, lse, workspace, stream)))
+
+
+def hga_route_attend_decode_workspace_bytes(cfg: hga_config, p0: int, n_q: int) -> int:
+    return int(lib().hga_route_attend_decode_workspace_bytes(ctypes.byref(cfg), p0, n_q))
+
+
+def hga_route_attend_decode(cfg: hga_config, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                            p0: int, summaries: torch.Tensor, n_chunks_valid: int,
+                            ids: torch.Tensor, O: torch.Tensor, lse: torch.Tensor,
+                            workspace: torch.Tensor, scores: torch.Tensor | None = None,
+                            stream=None) -> None:
+    """Routing and attention of a decode step in one call (two launches)."""
+    _check("hga_route_attend_decode", lib().hga_route_attend_decode(
+        *_m_route_attend_decode(cfg, Q, K, V, p0, summaries, n_chunks_valid, ids, O, lse,
+                                workspace, scores, stream)))
 
 
 def hga_diag_gather_sink_words(cfg: hga_config, n_q: int) -> int:

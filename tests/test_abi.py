@@ -242,6 +242,52 @@ def test_decode_checks():
     assert attend(need, T=p0) == hga.HGA_ERR_INVALID_ARG
 
 
+def test_route_attend_decode_checks():
+    """hga_route_attend_decode: its workspace (the scoring blocks' survivor
+    keys and ids, the split partials, each 256-B aligned) and its refusals,
+    all before any launch."""
+    L = hga.lib()
+    cfg = _cfg(top_k=32)
+    p0, n_q = 131071, 1
+    n_blk = -(-(p0 // 64) // 256)                 # 2047 candidates in blocks of 256
+    surv = n_q * 8 * n_blk * 32 * 4
+    parts = n_q * 32 * (32 + 1) * 130 * 4
+    need = surv + surv + parts
+    assert hga.hga_route_attend_decode_workspace_bytes(cfg, p0, n_q) == need
+    assert hga.hga_route_attend_decode_workspace_bytes(cfg, -1, 1) == 0
+    n_closed = p0 // 64
+
+    def call(cfg=cfg, p0=p0, n_q=n_q, T=p0 + n_q, n_valid=n_closed, ids=FAKE, ws=FAKE,
+             ws_bytes=need):
+        return L.hga_route_attend_decode(ctypes.byref(cfg), FAKE, FAKE, FAKE, T, p0, n_q,
+                                         FAKE, n_closed + 8, n_valid, ids, None, FAKE, FAKE,
+                                         ws, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == hga.HGA_ERR_CAPACITY
+    assert "workspace" in hga.hga_last_error()
+    assert call(ws=None) == hga.HGA_ERR_INVALID_ARG
+    assert call(T=p0) == hga.HGA_ERR_INVALID_ARG
+    assert call(n_valid=n_closed - 1) == hga.HGA_ERR_CAPACITY
+    assert call(n_valid=n_closed + 9) == hga.HGA_ERR_CAPACITY            # above the cap
+    assert call(ids=None) == hga.HGA_ERR_INVALID_ARG
+    assert call(n_q=65536, T=p0 + 65536) == hga.HGA_ERR_UNSUPPORTED
+    assert call(n_q=0) == hga.HGA_OK
+    # top_k 256 over 13000 candidates: 51 blocks x 256 survivors > 12288
+    big = _cfg(top_k=256)
+    p_big = 64 * 13000 + 3
+    n_big = hga.hga_route_attend_decode_workspace_bytes(big, p_big, 1)
+    assert L.hga_route_attend_decode(ctypes.byref(big), FAKE, FAKE, FAKE, p_big + 1, p_big, 1,
+                                     FAKE, 13000, 13000, FAKE, None, FAKE, FAKE, FAKE, n_big,
+                                     None) == hga.HGA_ERR_UNSUPPORTED
+    assert "hga_route_decode" in hga.hga_last_error()
+    # no routing: ids and summaries may be NULL
+    k0 = _cfg(top_k=0)
+    n0 = hga.hga_route_attend_decode_workspace_bytes(k0, p0, 1)
+    assert L.hga_route_attend_decode(ctypes.byref(k0), FAKE, FAKE, FAKE, p0 + 1, p0, 0, None,
+                                     0, 0, None, None, FAKE, FAKE, FAKE, n0,
+                                     None) == hga.HGA_OK
+
+
 def test_grid_limits():
     """Sizes past what one launch's grid holds are refused before any launch:
     more than 65535 query blocks, more than 65535 decode tokens, more than

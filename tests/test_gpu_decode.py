@@ -1,7 +1,10 @@
 """GPU parity of routed decode (hga_route_decode, hga_attend_decode) against
 the CPU oracle: a step of n_q tokens at positions p0 .. p0+n_q-1, each routing
 on its own query heads over the closed chunks before its open chunk and
-attending the sink window, its chunks and its open chunk up to itself."""
+attending the sink window, its chunks and its open chunk up to itself. Every
+routed case also runs hga_route_attend_decode (twice, on a workspace filled
+with 0xFF) and requires its ids, scores, O and lse to equal the two separate
+calls' bit for bit."""
 import os
 
 import numpy as np
@@ -53,8 +56,33 @@ def decode(x, p0, n_q, k, s=0, ids_override=None):
     lse = torch.full((Hq, n_q), float("nan"), device="cuda")
     hga.hga_attend_decode(cfg, Qd, K, V, p0, ids, O, lse, ws)
     torch.cuda.synchronize()
+    if ids_override is None:
+        fused_equals_separate(cfg, Qd, K, V, p0, S, n_closed, ids, sc, O, lse)
     return dict(ids=ids.cpu().numpy(), scores=from_dev(sc), O=from_dev(O), lse=from_dev(lse),
                 S=from_dev(S), Q=Q, n_closed=n_closed)
+
+
+def fused_equals_separate(cfg, Qd, K, V, p0, S, n_closed, ids, sc, O, lse):
+    """hga_route_attend_decode on a 0xFF-filled workspace, called twice (the
+    second call finds the first one's survivors and partials), against the
+    separate calls' outputs: equal bit for bit."""
+    n_q = Qd.shape[1]
+    ws = torch.full((hga.hga_route_attend_decode_workspace_bytes(cfg, p0, n_q),), 255,
+                    dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        ids_f = torch.full_like(ids, -7)
+        sc_f = torch.full_like(sc, float("nan"))
+        O_f = torch.full_like(O, float("nan"))
+        lse_f = torch.full_like(lse, float("nan"))
+        hga.hga_route_attend_decode(cfg, Qd, K, V, p0, S, n_closed, ids_f, O_f, lse_f, ws, sc_f)
+        torch.cuda.synchronize()
+        assert torch.equal(ids_f, ids), f"fused ids differ (call {rep})"
+        assert torch.equal(sc_f.view(torch.int32), sc.view(torch.int32)), \
+            f"fused scores differ (call {rep})"
+        assert torch.equal(O_f.view(torch.int16), O.view(torch.int16)), \
+            f"fused O differs (call {rep})"
+        assert torch.equal(lse_f.view(torch.int32), lse.view(torch.int32)), \
+            f"fused lse differs (call {rep})"
 
 
 def check(x, p0, n_q, k, s, res, where, routed=True):
@@ -114,6 +142,43 @@ def test_two_stage_selection_with_many_candidates():
     x = inputs.small_random(613, 2, 1, 128, T, 3, bf16=True)
     res = decode(x, p0, 3, 100, s=1)
     check(x, p0, 3, 100, 1, res, "5000 candidates, k=100")
+
+
+def test_fused_large_survivor_selection():
+    """4500 candidates, k = 256: 18 scoring blocks leave 4608 survivors, which
+    the fused call's four waves select among with 48 keys per lane."""
+    T, p0 = 64 * 4501, 64 * 4500 + 5
+    x = inputs.small_random(614, 2, 1, 128, T, 2, bf16=True)
+    res = decode(x, p0, 2, 256)
+    check(x, p0, 2, 256, 0, res, "4500 candidates, k=256")
+
+
+def test_fused_without_routing():
+    """top_k = 0: the fused call attends the sink window and the open chunk,
+    with no id row (and the separate attention call agrees)."""
+    T, p0, n_q = 2048, 1500, 4
+    x = inputs.small_random(615, 4, 2, 128, T, n_q, bf16=True)
+    cfg = hga.make_config(4, 2, 0, sink_chunks=3)
+    Qd = to_dev_bf16(x["Q"][:, :n_q])
+    K, V = to_dev_bf16(x["K"]), to_dev_bf16(x["V"])
+    outs = []
+    for fused in (False, True):
+        O = torch.full((4, n_q, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((4, n_q), float("nan"), device="cuda")
+        if fused:
+            ws = torch.full((hga.hga_route_attend_decode_workspace_bytes(cfg, p0, n_q),), 255,
+                            dtype=torch.uint8, device="cuda")
+            hga.hga_route_attend_decode(cfg, Qd, K, V, p0, None, 0, None, O, lse, ws)
+        else:
+            ws = torch.full((hga.hga_decode_workspace_bytes(cfg, p0, n_q),), 255,
+                            dtype=torch.uint8, device="cuda")
+            hga.hga_attend_decode(cfg, Qd, K, V, p0, None, O, lse, ws)
+        torch.cuda.synchronize()
+        outs.append((O.view(torch.int16).clone(), lse.view(torch.int32).clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ids0 = np.zeros((2, n_q, 0), np.int32)
+    O_ref, lse_ref = oracle.attend_decode(x["Q"][:, :n_q], x["K"], x["V"], ids0, p0, sink=3 * C)
+    check_close("k=0 fused O", from_dev(outs[1][0].view(torch.bfloat16)), O_ref)
 
 
 def test_largest_budget_and_sink():
