@@ -16,22 +16,28 @@
 //          few keys. K^T sits in LDS under the accumulator's key permutation,
 //          as V^T does in the forward.
 //   dkdv   key-major over the active chunks only (history is detached): the
-//          workgroups of chunk a scan the routed ids for the later blocks that
-//          chose a; the list's (block, query head) tiles, own block first,
-//          are dealt round-robin to up to kSplit workgroups:
+//          dq workgroup of block a also lists the later blocks whose ids chose
+//          chunk a (the dkdv plan); the list's (block, query head) tiles, own
+//          block first, are dealt round-robin to up to kSplit parts, and a
+//          persistent grid (one workgroup per CU) takes (chunk, unit, part)
+//          items from a work queue:
 //          S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
 //          Wave w owns keys 32*(w&1).. and queries 32*(w>>1).. of each query
 //          tile; the two query halves are summed through LDS. A chunk with
-//          at most kMinTiles tiles has one workgroup, which writes the result
-//          directly; a longer one is split, every workgroup stores its partial
-//          sums and the last one to finish (a per-chunk counter) adds the
-//          partials in workgroup order and writes the result. This spreads
-//          the chunks that many blocks chose (routing concentrates on
-//          high-scoring chunks) over several CUs.
+//          at most kMinTiles tiles is one part, which writes the result
+//          directly; a longer one is split, every part stores its partial
+//          sums at device scope (the first into the chunk's own dK / dV rows,
+//          the others into workspace slots) and the last one to finish (a
+//          per-chunk counter) adds the partials in part order and writes the
+//          result. This spreads the chunks that many blocks chose (routing
+//          concentrates on high-scoring chunks) over several CUs.
 // Both kernels load their tiles two steps ahead into registers (two sets
 // used in a fixed order, steps run in pairs) and write them to double-buffered
 // LDS one barrier before use; transposed copies are written with byte
 // permutes in a lane order whose 8-byte writes fall on distinct banks.
+#include <algorithm>
+#include <atomic>
+
 #include "hga_internal.h"
 
 namespace hga {
@@ -57,6 +63,86 @@ __device__ __forceinline__ f32x16 zero16() {
 #pragma unroll
     for (int j = 0; j < 16; ++j) z[j] = 0.f;
     return z;
+}
+
+// ----------------------------------------------------------- the dkdv plan
+
+// The query blocks that attend active chunk a of routing unit g: its own
+// block (causal) and every later block whose id row lists it (or, for group
+// ids, any of its groups) -- every later block if the chunk lies in the sink
+// window -- in ascending block order, each with the mask of the chunk's
+// groups it attends. The dq workgroup of block a (whose unit and block the
+// dkdv workgroups of chunk a share) finds them and stores them for the dkdv
+// kernel: plan_n[g][a] entries of plan_blk[g][a][.] (block ids) and
+// plan_msk[g][a][.] (group masks).
+//
+// Scan, by four waves (wave w of them: blocks a+1+w, a+5+w, ...; each id row
+// spread over the 64 lanes, kScanRows rows loaded before any is used): the
+// mask by block into rmask (LDS, n_blocks entries).
+template <int kUnit>
+__device__ __forceinline__ void plan_scan(const int32_t *__restrict__ ids, int64_t g, int64_t a,
+                                          int64_t n_blocks, int k, int64_t ca, int sink,
+                                          int wave4, uint8_t *rmask)
+{
+    constexpr int kScanRows = 4;
+    const int lane = threadIdx.x & 63;
+    const int32_t ca32 = (int32_t)ca;
+    for (int64_t base = a + 1 + wave4; base < n_blocks; base += 4 * kScanRows) {
+        uint32_t msk[kScanRows];
+#pragma unroll
+        for (int rr = 0; rr < kScanRows; ++rr) msk[rr] = 0u;
+        for (int c0 = 0; c0 < k; c0 += 64) {
+            int32_t u[kScanRows];
+#pragma unroll
+            for (int rr = 0; rr < kScanRows; ++rr) {
+                const int64_t bb = base + 4 * rr;
+                u[rr] = (bb < n_blocks && c0 + lane < k)
+                            ? ids[(g * n_blocks + bb) * k + c0 + lane] : -1;
+            }
+#pragma unroll
+            for (int rr = 0; rr < kScanRows; ++rr) {
+                if constexpr (kUnit == kC) {
+                    msk[rr] |= __ballot(u[rr] == ca32) != 0 ? 0xFFu : 0u;
+                } else {
+                    const bool in = (u[rr] >> 3) == ca32;
+#pragma unroll
+                    for (int bit = 0; bit < 8; ++bit)
+                        msk[rr] |= __ballot(in && (u[rr] & 7) == bit) != 0 ? 1u << bit : 0u;
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < kScanRows; ++rr) {
+            const int64_t bb = base + 4 * rr;
+            if (ca < sink) msk[rr] = 0xFFu;
+            if (lane == 0 && bb < n_blocks) rmask[bb] = (uint8_t)msk[rr];
+        }
+    }
+}
+
+// Compaction of the scan (one wave, after a barrier): the plan entries of
+// chunk a, own block first, then the hit blocks in ascending order.
+__device__ __forceinline__ void plan_store(const uint8_t *rmask, int64_t a, int64_t n_blocks,
+                                           int *plan_n, uint16_t *plan_blk, uint8_t *plan_msk)
+{
+    const int lane = threadIdx.x & 63;
+    if (lane == 0) {
+        plan_blk[0] = (uint16_t)a;
+        plan_msk[0] = 0xFF;
+    }
+    int cnt = 1;
+    for (int64_t base = a + 1; base < n_blocks; base += 64) {
+        const int64_t bb = base + lane;
+        const uint32_t msk = bb < n_blocks ? rmask[bb] : 0u;
+        const bool hit = msk != 0;
+        const uint64_t m = __ballot(hit);
+        if (hit) {
+            plan_blk[cnt + lanes_below(m)] = (uint16_t)bb;
+            plan_msk[cnt + lanes_below(m)] = (uint8_t)msk;
+        }
+        cnt += __popcll(m);
+    }
+    if (lane == 0) *plan_n = cnt;
 }
 
 // --------------------------------------------------------------------- dq
@@ -167,6 +253,8 @@ void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
+    int *__restrict__ next_item, int *__restrict__ plan_n, uint16_t *__restrict__ plan_blk,
+    uint8_t *__restrict__ plan_msk,
     int64_t n_q, int kv_div, int64_t T_cap, int64_t p0,
     const int32_t *__restrict__ ids, int k, int sink, float scale_log2, float scale,
     float *__restrict__ dQ)
@@ -178,6 +266,7 @@ void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t Kts[2][kTTile];
     __shared__ int list[(kUnit == kC ? kChunkListMax : kGroupListMax) + 1];
     __shared__ int list_n;
+    __shared__ uint8_t rmask[kMaxBlocksDkdv];   // the dkdv plan's scan, by block
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -209,6 +298,11 @@ void bwd_dq_kernel(
     }
     // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
+    if (g == 0 && b == 0 && hg == 0 && tid == 0) *next_item = 0;
+    // waves 4..7 scan for the dkdv plan of chunk b (stored after the first
+    // barrier below)
+    if (hg == 0 && wave >= 4)
+        plan_scan<kUnit>(ids, g, b, n_blocks, k, p0 / kC + b, sink, wave - 4, rmask);
     __syncthreads();
     const int n_units = list_n - 1;
     const int n_tiles = (kUnit == kC ? n_units : (n_units + 7) / 8) + 1;
@@ -273,6 +367,11 @@ void bwd_dq_kernel(
     store(r0, 0);
     // Q, dO and lse have landed once the first tile has (issued before it).
     __syncthreads();
+    if (hg == 0 && wave == 4) {
+        const int64_t pr = g * n_blocks + b;
+        plan_store(rmask, b, n_blocks, plan_n + pr, plan_blk + pr * n_blocks,
+                   plan_msk + pr * n_blocks);
+    }
 
     // S^T and dP^T of one 32-key half kt of the tile in buffer buf, P in place
     // of S^T. Masks: key 32*kt + 8*(j/4) + 4*half + j%4 is dropped when
@@ -411,12 +510,14 @@ constexpr int kBufBytes = kDlOff + kC * 4;
 static_assert(kBufBytes % 16 == 0, "buffer alignment");
 static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits");
 
-// A chunk's query tiles go to one workgroup, or to kSplit of them when there
-// are more than kMinTiles (more workgroups per chunk measured slower: each
-// one, even one with nothing dealt, pays the scan and the set-up, and the
-// dkdv workgroup holds a whole CU).
-constexpr int kSplit = 2;
-constexpr int kMinTiles = 8;
+// A chunk's query tiles go to up to kSplit workgroups, at least kMinTiles
+// tiles each. Routing concentrates on a few high-scoring chunks (at the 16K
+// backward workload one chunk has 52 (block, head) tiles, the mean is 7.4),
+// and the longest chain sets the kernel's time. A workgroup with nothing
+// dealt still pays the scan while holding a CU (the dkdv workgroup takes most
+// of a CU's LDS), which is why the split stops at kSplit.
+constexpr int kSplit = 4;
+constexpr int kMinTiles = 6;
 
 // kUnit = kGroup: a later block may have chosen only some of the chunk's 8
 // groups; the scan records them as an 8-bit mask per listed block, and the
@@ -426,364 +527,352 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
     const float *__restrict__ lse, const float *__restrict__ delta, int64_t n_q,
-    int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, const int32_t *__restrict__ ids, int k,
-    int sink, float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV,
-    float *__restrict__ part, int *__restrict__ counters)
+    int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, const int *__restrict__ plan_n,
+    const uint16_t *__restrict__ plan_blk, const uint8_t *__restrict__ plan_msk,
+    float scale_log2, float scale, float *__restrict__ dK, float *__restrict__ dV,
+    float *__restrict__ part, int *__restrict__ counters, int *__restrict__ next_item)
 {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];
     __shared__ int blist[kMaxBlocksDkdv];
     __shared__ uint8_t bmask[kMaxBlocksDkdv];
-    __shared__ uint8_t rmask[kMaxBlocksDkdv];   // by block: the scan's result
-    __shared__ int blist_n;
     __shared__ int is_last;
+    __shared__ int item_s;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    // grid (Hkv, kv_div, blocks * kSplit)
-    const int64_t gkv = blockIdx.x;                         // kv head
-    const int64_t g = gkv * kv_div + blockIdx.y;            // routing unit: its id rows
-    const int split = (int)(blockIdx.z % kSplit);
-    const int64_t a = blockIdx.z / kSplit;       // active chunk = its own query block
     const int64_t n_blocks = n_q / kC;
-    const int64_t ca = p0 / kC + a;               // absolute chunk index
+    // Persistent: one workgroup per CU takes (chunk, unit, part) items from a
+    // counter in item order until none is left; earlier chunks come first,
+    // as more later blocks can choose them (their lists are the longest).
+    // (A grid of one workgroup per item left CUs idle: dispatch is in order
+    // and stalls behind the busiest XCD, so the CUs freed by items with
+    // nothing dealt were not refilled for tens of microseconds.)
+    const int64_t n_items = Hkv * kv_div * n_blocks * kSplit;
+    for (;;) {
+        __syncthreads();                          // the last item is done with LDS
+        if (tid == 0) item_s = atomicAdd(next_item, 1);
+        __syncthreads();
+        const int64_t item = item_s;
+        if (item >= n_items) break;
+        const int64_t n_units = Hkv * kv_div;
+        const int split = (int)(item % kSplit);
+        const int64_t g = (item / kSplit) % n_units;    // routing unit: its id rows
+        const int64_t a = item / (kSplit * n_units);    // active chunk = its own query block
+        const int64_t gkv = g / kv_div;                 // kv head
+        const int64_t ca = p0 / kC + a;                 // absolute chunk index
 
-    // Query blocks that attend chunk a: its own (causal) and every later block
-    // whose routed ids list it (or, for group ids, any of its groups) -- every
-    // later block if the chunk lies in the sink window -- in ascending block
-    // order, each with the mask of the chunk's groups it attends. The four waves scan the later blocks' id rows (wave w: blocks
-    // a+1+w, a+5+w, ...), each row spread over the 64 lanes and kScanRows rows
-    // loaded before any is used; the masks land in LDS by block and wave 0
-    // then lists the blocks in order.
-    {
-        constexpr int kScanRows = 4;
-        const int32_t ca32 = (int32_t)ca;
-        for (int64_t base = a + 1 + wave; base < n_blocks; base += 4 * kScanRows) {
-            uint32_t msk[kScanRows];
-#pragma unroll
-            for (int rr = 0; rr < kScanRows; ++rr) msk[rr] = 0u;
-            for (int c0 = 0; c0 < k; c0 += 64) {
-                int32_t u[kScanRows];
-#pragma unroll
-                for (int rr = 0; rr < kScanRows; ++rr) {
-                    const int64_t bb = base + 4 * rr;
-                    u[rr] = (bb < n_blocks && c0 + lane < k)
-                                ? ids[(g * n_blocks + bb) * k + c0 + lane] : -1;
+        // The chunk's query tiles -- (listed block, query head) pairs, block-major
+        // -- are dealt round-robin to n_parts workgroups: this one takes tiles
+        // split, split + n_parts, ... (tile T: block blist[T / G], head T % G).
+        // The list is the plan the dq kernel stored; a workgroup with nothing
+        // dealt leaves after reading its length.
+        const int64_t pr = g * n_blocks + a;
+        const int n_list = plan_n[pr];
+        const int n_all = n_list * G;
+        const int n_parts = min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
+        if (split >= n_parts) continue;               // nothing dealt to this workgroup
+        const int n_tiles = (n_all - split + n_parts - 1) / n_parts;
+        for (int i = tid; i < n_list; i += kThreads) {
+            blist[i] = plan_blk[pr * n_blocks + i];
+            bmask[i] = plan_msk[pr * n_blocks + i];
+        }
+
+        const int col = lane & 31;
+        const int half = lane >> 5;
+        const int kh = wave & 1;         // keys 32*kh .. +32 of the chunk
+        const int qh = wave >> 1;        // queries 32*qh .. +32 of each tile
+        const int64_t key_row = ca * kC + 32 * kh + col;
+        bf16x8 kb[8], vb[8];
+    #pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            kb[ks] = *(const bf16x8 *)(K + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
+            vb[ks] = *(const bf16x8 *)(V + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
+        }
+        __syncthreads();                              // blist and bmask are in LDS
+
+        auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
+            const int T = split + n_parts * min(t, n_tiles - 1);
+            const int64_t bb = blist[T / G];
+            const int64_t hh = g * G + T % G;
+            return hh * n_q + bb * kC;
+        };
+        // Tile loader (all 256 threads): lane takes rows 4*kg .. 4*kg+3 of the
+        // 8-wide d slice dp of the Q and dO tiles (kg = lane%16, dp = 4*wave +
+        // lane/16), lse and Delta of the tile's queries on threads 0..63.
+        struct TileIn { u32x4 q[4], d[4]; float l, dl; };
+        const int lkg = lane & 15, ldp = 4 * wave + (lane >> 4);
+        auto load = [&](TileIn &r, int t) __attribute__((always_inline)) {
+            const int64_t row0 = tile_row0(t);
+            const uint16_t *qs = Q + (row0 + 4 * lkg) * kD + ldp * 8;
+            const uint16_t *ds = dO + (row0 + 4 * lkg) * kD + ldp * 8;
+    #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                r.q[j] = *(const u32x4 *)(qs + j * kD);
+                r.d[j] = *(const u32x4 *)(ds + j * kD);
+            }
+            const int qi = tid & (kC - 1);
+            r.l = lse[row0 + qi];
+            r.dl = delta[row0 + qi];
+        };
+        // Q and dO to LDS row-major (S and dP operands) and transposed under the
+        // accumulator's query permutation (dK and dV operands); with kg = lane%16
+        // the 8-byte transposed writes of the 64 lanes fall on distinct banks.
+        auto store = [&](const TileIn &r, int buf) __attribute__((always_inline)) {
+            uint8_t *B = smem + buf * kBufBytes;
+            uint16_t *Qs = (uint16_t *)(B + kQOff), *dOs = (uint16_t *)(B + kDOOff);
+            uint16_t *Qts = (uint16_t *)(B + kQtOff), *dOts = (uint16_t *)(B + kDOtOff);
+    #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *(u32x4 *)(Qs + (4 * lkg + j) * kRowStride + ldp * 8) = r.q[j];
+                *(u32x4 *)(dOs + (4 * lkg + j) * kRowStride + ldp * 8) = r.d[j];
+            }
+            const int pos = t_pos(4 * lkg);
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                u32x2 wq, wd;
+                wq[0] = __builtin_amdgcn_perm(r.q[1][e >> 1], r.q[0][e >> 1], sel);
+                wq[1] = __builtin_amdgcn_perm(r.q[3][e >> 1], r.q[2][e >> 1], sel);
+                wd[0] = __builtin_amdgcn_perm(r.d[1][e >> 1], r.d[0][e >> 1], sel);
+                wd[1] = __builtin_amdgcn_perm(r.d[3][e >> 1], r.d[2][e >> 1], sel);
+                *(u32x2 *)(Qts + (8 * ldp + e) * kTStride + pos) = wq;
+                *(u32x2 *)(dOts + (8 * ldp + e) * kTStride + pos) = wd;
+            }
+            if (tid < kC) {
+                ((float *)(B + kLseOff))[tid] = r.l * 1.44269504088896340736f;
+                ((float *)(B + kDlOff))[tid] = r.dl;
+            }
+        };
+        // Tiles run in pairs (register sets r0, r1 in a fixed order, loaded two
+        // tiles ahead); an odd count gets one padding step that computes nothing.
+        const int n_steps = n_tiles + (n_tiles & 1);
+        TileIn r0, r1;
+        load(r0, 0);
+        load(r1, 1);
+        store(r0, 0);
+        __syncthreads();
+
+        f32x16 dk[4], dv[4];
+    #pragma unroll
+        for (int dt = 0; dt < 4; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
+
+        auto step = [&](int it, TileIn &pre, const TileIn &nxt) __attribute__((always_inline)) {
+            const int buf = it & 1;
+            load(pre, it + 2);
+            if (it < n_tiles) {
+            const uint8_t *B = smem + buf * kBufBytes;
+            const uint16_t *Qb = (const uint16_t *)(B + kQOff);
+            const uint16_t *dOb = (const uint16_t *)(B + kDOOff);
+            const uint16_t *Qtb = (const uint16_t *)(B + kQtOff);
+            const uint16_t *dOtb = (const uint16_t *)(B + kDOtOff);
+            const float *lse2s = (const float *)(B + kLseOff);
+            const float *dls = (const float *)(B + kDlOff);
+
+            // S[q][key] = Q K^T, dP[q][key] = dO V^T for this wave's 32 x 32 block
+            // (A operands read from LDS two k-steps ahead of their MFMAs).
+            f32x16 s = zero16(), dp = zero16();
+            {
+                bf16x8 qa[8], da[8];
+                auto rd = [&](int ks) __attribute__((always_inline)) {
+                    const int off = (32 * qh + col) * kRowStride + 16 * ks + 8 * half;
+                    qa[ks] = *(const bf16x8 *)(Qb + off);
+                    da[ks] = *(const bf16x8 *)(dOb + off);
+                };
+                rd(0);
+                rd(1);
+    #pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    if (ks + 2 < 8) rd(ks + 2);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vb[ks], dp, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int rr = 0; rr < kScanRows; ++rr) {
-                    if constexpr (kUnit == kC) {
-                        msk[rr] |= __ballot(u[rr] == ca32) != 0 ? 0xFFu : 0u;
-                    } else {
-                        const bool in = (u[rr] >> 3) == ca32;
-#pragma unroll
-                        for (int bit = 0; bit < 8; ++bit)
-                            msk[rr] |= __ballot(in && (u[rr] & 7) == bit) != 0 ? 1u << bit : 0u;
-                    }
+            }
+            // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
+            // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
+            const int entry = (split + n_parts * it) / G;    // list entry of this tile
+            const bool diag = entry == 0;                    // entry 0 is the own block
+            // (group ids: this lane's key is dropped unless its group was chosen)
+            const bool kept = kUnit == kC ||
+                              ((bmask[entry] >> ((32 * kh + col) >> 3)) & 1);
+            bf16x8 pb[2], dsb[2];
+            bool big = false;
+    #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int q0 = 32 * qh + 8 * u + 4 * half;
+                const f32x4 l4 = *(const f32x4 *)(lse2s + q0);
+                const f32x4 d4 = *(const f32x4 *)(dls + q0);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * u + e;
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -l4[e]));
+                    if ((diag && 32 * kh + col > q0 + e) || !kept) p = 0.f;
+                    big |= p > kPairAbove;
+                    s[j] = p;
+                    dp[j] = p * (dp[j] - d4[e]);
+                    pb[j >> 3][j & 7] = (__bf16)s[j];
+                    dsb[j >> 3][j & 7] = (__bf16)dp[j];
                 }
             }
-#pragma unroll
-            for (int rr = 0; rr < kScanRows; ++rr) {
-                const int64_t bb = base + 4 * rr;
-                if (ca < sink) msk[rr] = 0xFFu;
-                if (lane == 0 && bb < n_blocks) rmask[bb] = (uint8_t)msk[rr];
-            }
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        if (lane == 0) {
-            blist[0] = (int)a;
-            bmask[0] = 0xFF;
-        }
-        int cnt = 1;
-        for (int64_t base = a + 1; base < n_blocks; base += 64) {
-            const int64_t bb = base + lane;
-            const uint32_t msk = bb < n_blocks ? rmask[bb] : 0u;
-            const bool hit = msk != 0;
-            const uint64_t m = __ballot(hit);
-            if (hit) {
-                blist[cnt + lanes_below(m)] = (int)bb;
-                bmask[cnt + lanes_below(m)] = (uint8_t)msk;
-            }
-            cnt += __popcll(m);
-        }
-        if (lane == 0) blist_n = cnt;
-    }
-    __syncthreads();
-    // The chunk's query tiles -- (listed block, query head) pairs, block-major
-    // -- are dealt round-robin to n_parts workgroups: this one takes tiles
-    // split, split + n_parts, ... (tile T: block blist[T / G], head T % G).
-    const int n_list = blist_n;
-    const int n_all = n_list * G;
-    const int n_parts = min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
-    if (split >= n_parts) return;                 // nothing dealt to this workgroup
-    const int n_tiles = (n_all - split + n_parts - 1) / n_parts;
-
-    const int col = lane & 31;
-    const int half = lane >> 5;
-    const int kh = wave & 1;         // keys 32*kh .. +32 of the chunk
-    const int qh = wave >> 1;        // queries 32*qh .. +32 of each tile
-    const int64_t key_row = ca * kC + 32 * kh + col;
-    bf16x8 kb[8], vb[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        kb[ks] = *(const bf16x8 *)(K + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
-        vb[ks] = *(const bf16x8 *)(V + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
-    }
-
-    auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
-        const int T = split + n_parts * min(t, n_tiles - 1);
-        const int64_t bb = blist[T / G];
-        const int64_t hh = g * G + T % G;
-        return hh * n_q + bb * kC;
-    };
-    // Tile loader (all 256 threads): lane takes rows 4*kg .. 4*kg+3 of the
-    // 8-wide d slice dp of the Q and dO tiles (kg = lane%16, dp = 4*wave +
-    // lane/16), lse and Delta of the tile's queries on threads 0..63.
-    struct TileIn { u32x4 q[4], d[4]; float l, dl; };
-    const int lkg = lane & 15, ldp = 4 * wave + (lane >> 4);
-    auto load = [&](TileIn &r, int t) __attribute__((always_inline)) {
-        const int64_t row0 = tile_row0(t);
-        const uint16_t *qs = Q + (row0 + 4 * lkg) * kD + ldp * 8;
-        const uint16_t *ds = dO + (row0 + 4 * lkg) * kD + ldp * 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            r.q[j] = *(const u32x4 *)(qs + j * kD);
-            r.d[j] = *(const u32x4 *)(ds + j * kD);
-        }
-        const int qi = tid & (kC - 1);
-        r.l = lse[row0 + qi];
-        r.dl = delta[row0 + qi];
-    };
-    // Q and dO to LDS row-major (S and dP operands) and transposed under the
-    // accumulator's query permutation (dK and dV operands); with kg = lane%16
-    // the 8-byte transposed writes of the 64 lanes fall on distinct banks.
-    auto store = [&](const TileIn &r, int buf) __attribute__((always_inline)) {
-        uint8_t *B = smem + buf * kBufBytes;
-        uint16_t *Qs = (uint16_t *)(B + kQOff), *dOs = (uint16_t *)(B + kDOOff);
-        uint16_t *Qts = (uint16_t *)(B + kQtOff), *dOts = (uint16_t *)(B + kDOtOff);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *(u32x4 *)(Qs + (4 * lkg + j) * kRowStride + ldp * 8) = r.q[j];
-            *(u32x4 *)(dOs + (4 * lkg + j) * kRowStride + ldp * 8) = r.d[j];
-        }
-        const int pos = t_pos(4 * lkg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 wq, wd;
-            wq[0] = __builtin_amdgcn_perm(r.q[1][e >> 1], r.q[0][e >> 1], sel);
-            wq[1] = __builtin_amdgcn_perm(r.q[3][e >> 1], r.q[2][e >> 1], sel);
-            wd[0] = __builtin_amdgcn_perm(r.d[1][e >> 1], r.d[0][e >> 1], sel);
-            wd[1] = __builtin_amdgcn_perm(r.d[3][e >> 1], r.d[2][e >> 1], sel);
-            *(u32x2 *)(Qts + (8 * ldp + e) * kTStride + pos) = wq;
-            *(u32x2 *)(dOts + (8 * ldp + e) * kTStride + pos) = wd;
-        }
-        if (tid < kC) {
-            ((float *)(B + kLseOff))[tid] = r.l * 1.44269504088896340736f;
-            ((float *)(B + kDlOff))[tid] = r.dl;
-        }
-    };
-    // Tiles run in pairs (register sets r0, r1 in a fixed order, loaded two
-    // tiles ahead); an odd count gets one padding step that computes nothing.
-    const int n_steps = n_tiles + (n_tiles & 1);
-    TileIn r0, r1;
-    load(r0, 0);
-    load(r1, 1);
-    store(r0, 0);
-    __syncthreads();
-
-    f32x16 dk[4], dv[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
-
-    auto step = [&](int it, TileIn &pre, const TileIn &nxt) __attribute__((always_inline)) {
-        const int buf = it & 1;
-        load(pre, it + 2);
-        if (it < n_tiles) {
-        const uint8_t *B = smem + buf * kBufBytes;
-        const uint16_t *Qb = (const uint16_t *)(B + kQOff);
-        const uint16_t *dOb = (const uint16_t *)(B + kDOOff);
-        const uint16_t *Qtb = (const uint16_t *)(B + kQtOff);
-        const uint16_t *dOtb = (const uint16_t *)(B + kDOtOff);
-        const float *lse2s = (const float *)(B + kLseOff);
-        const float *dls = (const float *)(B + kDlOff);
-
-        // S[q][key] = Q K^T, dP[q][key] = dO V^T for this wave's 32 x 32 block
-        // (A operands read from LDS two k-steps ahead of their MFMAs).
-        f32x16 s = zero16(), dp = zero16();
-        {
-            bf16x8 qa[8], da[8];
-            auto rd = [&](int ks) __attribute__((always_inline)) {
-                const int off = (32 * qh + col) * kRowStride + 16 * ks + 8 * half;
-                qa[ks] = *(const bf16x8 *)(Qb + off);
-                da[ks] = *(const bf16x8 *)(dOb + off);
-            };
-            rd(0);
-            rd(1);
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                if (ks + 2 < 8) rd(ks + 2);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vb[ks], dp, 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // lane: key 32*kh + col; queries 32*qh + 8u + 4*half + e (j = 4u + e).
-        // P and dS stay fp32 in s and dp; their bf16 hi halves feed the MFMAs.
-        const int entry = (split + n_parts * it) / G;    // list entry of this tile
-        const bool diag = entry == 0;                    // entry 0 is the own block
-        // (group ids: this lane's key is dropped unless its group was chosen)
-        const bool kept = kUnit == kC ||
-                          ((bmask[entry] >> ((32 * kh + col) >> 3)) & 1);
-        bf16x8 pb[2], dsb[2];
-        bool big = false;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q0 = 32 * qh + 8 * u + 4 * half;
-            const f32x4 l4 = *(const f32x4 *)(lse2s + q0);
-            const f32x4 d4 = *(const f32x4 *)(dls + q0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 4 * u + e;
-                float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -l4[e]));
-                if ((diag && 32 * kh + col > q0 + e) || !kept) p = 0.f;
-                big |= p > kPairAbove;
-                s[j] = p;
-                dp[j] = p * (dp[j] - d4[e]);
-                pb[j >> 3][j & 7] = (__bf16)s[j];
-                dsb[j >> 3][j & 7] = (__bf16)dp[j];
-            }
-        }
-        // dV^T += dO^T P, dK^T += Q^T dS (k runs over this wave's 32 queries);
-        // the 16 transposed operands are read before the MFMAs that use them
-        // and serve the low-half round too.
-        bf16x8 ta[8], tq[8];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int off = (32 * dt + col) * kTStride + 32 * qh + 16 * ks + 8 * half;
-                ta[2 * dt + ks] = *(const bf16x8 *)(dOtb + off);
-                tq[2 * dt + ks] = *(const bf16x8 *)(Qtb + off);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
-                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
-            }
-        if (__ballot(big) != 0) {              // wave-uniform: add the low halves
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                pb[j >> 3][j & 7] = (__bf16)(s[j] - (float)pb[j >> 3][j & 7]);
-                dsb[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsb[j >> 3][j & 7]);
-            }
-#pragma unroll
+            // dV^T += dO^T P, dK^T += Q^T dS (k runs over this wave's 32 queries);
+            // the 16 transposed operands are read before the MFMAs that use them
+            // and serve the low-half round too.
+            bf16x8 ta[8], tq[8];
+    #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
+    #pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int off = (32 * dt + col) * kTStride + 32 * qh + 16 * ks + 8 * half;
+                    ta[2 * dt + ks] = *(const bf16x8 *)(dOtb + off);
+                    tq[2 * dt + ks] = *(const bf16x8 *)(Qtb + off);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
                     dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
                 }
+            if (__ballot(big) != 0) {              // wave-uniform: add the low halves
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    pb[j >> 3][j & 7] = (__bf16)(s[j] - (float)pb[j >> 3][j & 7]);
+                    dsb[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsb[j >> 3][j & 7]);
+                }
+    #pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
+                        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
+                    }
+            }
+            }
+            if (it + 1 < n_steps) store(nxt, buf ^ 1);
+            __syncthreads();
+        };
+        for (int it = 0; it < n_steps; it += 2) {
+            step(it, r0, r1);
+            step(it + 1, r1, r0);
         }
-        }
-        if (it + 1 < n_steps) store(nxt, buf ^ 1);
-        __syncthreads();
-    };
-    for (int it = 0; it < n_steps; it += 2) {
-        step(it, r0, r1);
-        step(it + 1, r1, r0);
-    }
 
-    // Sum the two query halves: waves 2, 3 hand their partials to waves 0, 1.
-    float *red = (float *)smem;       // [2 waves][2 tensors][4 dt][16 j][64 lanes]
-    if (qh == 1) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane] = dk[dt][j];
-                red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane] = dv[dt][j];
-            }
-    }
-    __syncthreads();
-    // lane holds key 32*kh + col, d = 32*dt + 8u + 4*half + e
-    const int64_t out_row = g * n_q + a * kC + 32 * kh + col;
-    if (qh == 0) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                dk[dt][j] += red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane];
-                dv[dt][j] += red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane];
-            }
-    }
-    if (n_parts == 1) {
-        if (qh == 0) {
-#pragma unroll
+        // Sum the two query halves: waves 2, 3 hand their partials to waves 0, 1.
+        float *red = (float *)smem;       // [2 waves][2 tensors][4 dt][16 j][64 lanes]
+        if (qh == 1) {
+    #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane] = dk[dt][j];
+                    red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane] = dv[dt][j];
+                }
+        }
+        __syncthreads();
+        // lane holds key 32*kh + col, d = 32*dt + 8u + 4*half + e
+        const int64_t out_row = g * n_q + a * kC + 32 * kh + col;
+        if (qh == 0) {
+    #pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    dk[dt][j] += red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane];
+                    dv[dt][j] += red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane];
+                }
+        }
+        if (n_parts == 1) {
+            if (qh == 0) {
+    #pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        f32x4 vk, vv;
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            vk[e] = dk[dt][4 * u + e] * scale;
+                            vv[e] = dv[dt][4 * u + e];
+                        }
+                        *(f32x4 *)(dK + out_row * kD + 32 * dt + 8 * u + 4 * half) = vk;
+                        *(f32x4 *)(dV + out_row * kD + 32 * dt + 8 * u + 4 * half) = vv;
+                    }
+            }
+            continue;
+        }
+
+        // Several workgroups share this chunk: store the partial (the first
+        // workgroup into the chunk's own dK / dV rows, unscaled; workgroup s > 0
+        // into slot s - 1), count, and let the last one add the partials in
+        // workgroup order 0, 1, ... . The partials are stored at device scope
+        // (written through to where every XCD reads them), 8 bytes a lane with
+        // consecutive lanes on consecutive addresses (staged row-major through
+        // LDS first), and the count waits for those stores to complete; only the
+        // last workgroup then invalidates its L2's stale lines (an acquire)
+        // before reading them. (A device-scope release fence instead writes back
+        // the XCD's whole L2 in every workgroup: 7-21 us per split workgroup,
+        // measured.)
+        const int64_t part_stride = Hkv * kv_div * n_q * kD;   // floats per (slot, tensor)
+        constexpr int kStageStride = kD + 4;                   // floats per staged row
+        float *stage = (float *)smem;                          // [dK, dV][64 rows][kStageStride]
+        __syncthreads();                                        // red has been read
+        if (qh == 0) {
+            const int row = 32 * kh + col;
+    #pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+    #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     f32x4 vk, vv;
-#pragma unroll
+    #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        vk[e] = dk[dt][4 * u + e] * scale;
+                        vk[e] = dk[dt][4 * u + e];
                         vv[e] = dv[dt][4 * u + e];
                     }
-                    *(f32x4 *)(dK + out_row * kD + 32 * dt + 8 * u + 4 * half) = vk;
-                    *(f32x4 *)(dV + out_row * kD + 32 * dt + 8 * u + 4 * half) = vv;
+                    *(f32x4 *)(stage + row * kStageStride + 32 * dt + 8 * u + 4 * half) = vk;
+                    *(f32x4 *)(stage + (kC + row) * kStageStride + 32 * dt + 8 * u + 4 * half) = vv;
                 }
         }
-        return;
-    }
-
-    // Several workgroups share this chunk: store the partial, count, and let
-    // the last one add the partials in workgroup order 0, 1, ... .
-    const int64_t part_stride = Hkv * kv_div * n_q * kD;   // floats per (split, tensor)
-    if (qh == 0) {
-        float *pk = part + (int64_t)(2 * split) * part_stride + out_row * kD;
-        float *pv = part + (int64_t)(2 * split + 1) * part_stride + out_row * kD;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                f32x4 vk, vv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vk[e] = dk[dt][4 * u + e];
-                    vv[e] = dv[dt][4 * u + e];
-                }
-                *(f32x4 *)(pk + 32 * dt + 8 * u + 4 * half) = vk;
-                *(f32x4 *)(pv + 32 * dt + 8 * u + 4 * half) = vv;
+        __syncthreads();
+        {
+            const int64_t row_base = g * n_q + a * kC;
+            float *pk = split == 0 ? dK : part + (int64_t)(2 * (split - 1)) * part_stride;
+            float *pv = split == 0 ? dV : part + (int64_t)(2 * (split - 1) + 1) * part_stride;
+            // pair i of tensor t: row (i / 64), dims 2 (i % 64) .. +2
+            for (int i = tid; i < 2 * kC * (kD / 2); i += kThreads) {
+                const int t = i / (kC * (kD / 2)), w = i % (kC * (kD / 2));
+                const int row = w / (kD / 2), d2 = 2 * (w % (kD / 2));
+                const float *src = stage + (t * kC + row) * kStageStride + d2;
+                const uint64_t bits = (uint64_t)__float_as_uint(src[0]) |
+                                      ((uint64_t)__float_as_uint(src[1]) << 32);
+                uint64_t *dst = (uint64_t *)((t ? pv : pk) + (row_base + row) * kD + d2);
+                __hip_atomic_store(dst, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) is_last = atomicAdd(&counters[g * n_blocks + a], 1) == n_parts - 1;
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    // 64 keys x 128 d per tensor; thread t sums float4 column (t % 32) of rows
-    // t/32, t/32 + 8, ...
-    const int64_t row_base = g * n_q + a * kC;
-    for (int r = tid >> 5; r < kC; r += kThreads / 32) {
-        const int64_t off = (row_base + r) * kD + 4 * (tid & 31);
-        f32x4 sk = *(const f32x4 *)(part + off);
-        f32x4 sv = *(const f32x4 *)(part + part_stride + off);
-        for (int sp = 1; sp < n_parts; ++sp) {
-            const f32x4 xk = *(const f32x4 *)(part + (int64_t)(2 * sp) * part_stride + off);
-            const f32x4 xv = *(const f32x4 *)(part + (int64_t)(2 * sp + 1) * part_stride + off);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { sk[e] += xk[e]; sv[e] += xv[e]; }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sk[e] *= scale;
-        *(f32x4 *)(dK + off) = sk;
-        *(f32x4 *)(dV + off) = sv;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            is_last = __hip_atomic_fetch_add(&counters[g * n_blocks + a], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == n_parts - 1;
+        __syncthreads();
+        if (!is_last) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // 64 keys x 128 d per tensor; thread t sums float4 column (t % 32) of rows
+        // t/32, t/32 + 8, ...
+        const int64_t row_base = g * n_q + a * kC;
+        for (int r = tid >> 5; r < kC; r += kThreads / 32) {
+            const int64_t off = (row_base + r) * kD + 4 * (tid & 31);
+            f32x4 sk = *(const f32x4 *)(dK + off);
+            f32x4 sv = *(const f32x4 *)(dV + off);
+            for (int sp = 1; sp < n_parts; ++sp) {
+                const f32x4 xk = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1)) * part_stride + off);
+                const f32x4 xv = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1) + 1) * part_stride + off);
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) { sk[e] += xk[e]; sv[e] += xv[e]; }
+            }
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) sk[e] *= scale;
+            *(f32x4 *)(dK + off) = sk;
+            *(f32x4 *)(dV + off) = sv;
+        }
     }
 }
 
@@ -811,38 +900,61 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(
 
 // G: query heads per routing unit (1 with per-query-head routing, where
 // kv_div = query heads per kv head and dK/dV are then the per-head buffers).
+// Compute units of the current device (the persistent dkdv grid's size),
+// asked once per device.
+int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int G, int kUnit>
 hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                         int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, int64_t n_q,
                         const int32_t *ids, int32_t k, int32_t sink, float scale, const float *lse,
                         const uint16_t *dO, float *dQ, float *dK, float *dV,
-                        float *delta, int *counters, float *part, hipStream_t stream)
+                        float *delta, int *counters, int *plan_n, uint16_t *plan_blk,
+                        uint8_t *plan_msk, float *part, hipStream_t stream)
 {
+    int *next_item = counters + Hkv * kv_div * (n_q / kC);
     constexpr int NHG = G < 4 ? 1 : G / 4;
     const int64_t n_blocks = n_q / kC;
     const float scale_log2 = scale * 1.44269504088896340736f;
-    if (n_blocks * kSplit > 65535) return hipErrorInvalidConfiguration;     // grid z limit
+    if (n_blocks > 65535) return hipErrorInvalidConfiguration;     // grid z limit
     hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>),
                        dim3((unsigned)Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
                        dim3(kDqThreads), 0,
-                       stream, Q, K, V, dO, lse, delta, counters, n_q, kv_div, T_cap, p0,
-                       ids, k, (int)sink, scale_log2, scale, dQ);
+                       stream, Q, K, V, dO, lse, delta, counters, next_item, plan_n, plan_blk,
+                       plan_msk, n_q, kv_div, T_cap, p0, ids, k, (int)sink, scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int64_t n_items = Hkv * kv_div * n_blocks * kSplit;
     hipLaunchKernelGGL((bwd_dkdv_kernel<G, kUnit>),
-                       dim3((unsigned)Hkv, (unsigned)kv_div, (unsigned)(n_blocks * kSplit)),
-                       dim3(kThreads), 0,
-                       stream, Q, K, V, dO, lse, delta, n_q, Hkv, kv_div, T_cap, p0, ids, k,
-                       (int)sink, scale_log2, scale, dK, dV, part, counters);
+                       dim3((unsigned)std::min<int64_t>(n_items, device_cus())), dim3(kThreads),
+                       0, stream, Q, K, V, dO, lse, delta, n_q, Hkv, kv_div, T_cap, p0, plan_n,
+                       plan_blk, plan_msk, scale_log2, scale, dK, dV, part, counters, next_item);
     return hipGetLastError();
 }
 
-// Workspace layout (U routing units: Hkv, or Hq with per-query-head routing):
-// Delta [Hq][n_q] f32 | counters [U][n_q/C] int32 | partial sums
-// [kSplit][dK, dV][U][n_q][D] f32 | per-query-head routing only: each head's
-// dK and dV, [2][Hq][n_q][D] f32. Every part starts on a 256-byte boundary.
+// Workspace layout (U routing units: Hkv, or Hq with per-query-head routing;
+// nb = n_q/C blocks): Delta [Hq][n_q] f32 | counters [U][nb] int32 and the
+// dkdv work-queue counter | the dkdv
+// plan: plan_n [U][nb] int32, plan_blk [U][nb][nb] uint16, plan_msk
+// [U][nb][nb] uint8 | partial sums [kSplit - 1][dK, dV][U][n_q][D] f32 |
+// per-query-head routing only: each head's dK and dV, [2][Hq][n_q][D] f32.
+// Every part starts on a 256-byte boundary.
 struct BwdWorkspace {
-    size_t delta_off, counter_off, part_off, head_off, total;
+    size_t delta_off, counter_off, plan_n_off, plan_blk_off, plan_msk_off, part_off, head_off,
+        total;
 };
 
 BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
@@ -852,8 +964,12 @@ BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
     BwdWorkspace w;
     w.delta_off = 0;
     w.counter_off = up((size_t)(Hq * n_q) * sizeof(float));
-    w.part_off = w.counter_off + up((size_t)(U * (n_q / kC)) * sizeof(int));
-    w.head_off = w.part_off + (size_t)kSplit * 2 * (size_t)(U * n_q * kD) * sizeof(float);
+    const size_t nb = (size_t)(n_q / kC);
+    w.plan_n_off = w.counter_off + up(((size_t)U * nb + 1) * sizeof(int));
+    w.plan_blk_off = w.plan_n_off + up((size_t)U * nb * sizeof(int));
+    w.plan_msk_off = w.plan_blk_off + up((size_t)U * nb * nb * sizeof(uint16_t));
+    w.part_off = w.plan_msk_off + up((size_t)U * nb * nb);
+    w.head_off = w.part_off + (size_t)(kSplit - 1) * 2 * (size_t)(U * n_q * kD) * sizeof(float);
     w.total = w.head_off + (per_q_head ? 2 * (size_t)(Hq * n_q * kD) * sizeof(float) : 0);
     return w;
 }
@@ -881,6 +997,9 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
     uint8_t *ws = (uint8_t *)workspace;
     float *delta = (float *)(ws + w.delta_off);
     int *counters = (int *)(ws + w.counter_off);
+    int *plan_n = (int *)(ws + w.plan_n_off);
+    uint16_t *plan_blk = (uint16_t *)(ws + w.plan_blk_off);
+    uint8_t *plan_msk = ws + w.plan_msk_off;
     float *part = (float *)(ws + w.part_off);
     const int G = (int)(Hq / Hkv);
     if (per_q_head) {
@@ -888,7 +1007,7 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
         float *dVu = dKu + Hq * n_q * kD;
         hipError_t e = launch_bwd_g<1, kUnit>(Q, K, V, Hkv, G, T_cap, p0, n_q, ids, k, sink,
                                               scale, lse, dO, dQ, dKu, dVu, delta, counters,
-                                              part, stream);
+                                              plan_n, plan_blk, plan_msk, part, stream);
         if (e != hipSuccess) return e;
         const int64_t per_head = n_q * kD / 4, n_vec = Hkv * per_head;
         hipLaunchKernelGGL(sum_heads_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256),
@@ -896,10 +1015,10 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
         return hipGetLastError();
     }
     switch (G) {
-    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
-    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, part, stream);
+    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
+    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
+    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
+    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
     default: return hipErrorInvalidValue;
     }
 }

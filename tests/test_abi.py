@@ -341,15 +341,21 @@ def test_routing_variant_checks():
     assert L.hga_route_decode(ctypes.byref(per_head), FAKE, 100, 1, FAKE, 1, 1, FAKE, None,
                               FAKE, 1 << 20, None) == hga.HGA_ERR_UNSUPPORTED
     # the backward workspace grows by the per-head dK and dV and the per-head
-    # counters and partial sums
+    # counters, block lists and partial sums
     n_q = 2048
     a = hga.hga_attend_bwd_workspace_bytes(_cfg(), n_q)
     b = hga.hga_attend_bwd_workspace_bytes(per_head, n_q)
     up = lambda v: (v + 255) // 256 * 256
     delta = up(32 * n_q * 4)
-    split = 2                  # workgroups that may share one active chunk
-    assert a == delta + up(8 * 32 * 4) + split * 2 * 8 * n_q * 128 * 4
-    assert b == delta + up(32 * 32 * 4) + split * 2 * 32 * n_q * 128 * 4 + 2 * 32 * n_q * 128 * 4
+    nb = n_q // 64
+
+    def plan(U):               # per (unit, chunk): list length, block ids, group masks
+        return up(U * nb * 4) + up(U * nb * nb * 2) + up(U * nb * nb)
+
+    slots = 3                  # workgroups past the first that may share one active chunk
+    assert a == delta + up((8 * nb + 1) * 4) + plan(8) + slots * 2 * 8 * n_q * 128 * 4
+    assert b == delta + up((32 * nb + 1) * 4) + plan(32) + slots * 2 * 32 * n_q * 128 * 4 \
+        + 2 * 32 * n_q * 128 * 4
     # strictly causal routing needs the queries before p0 once p0 > 0
     args = lambda p0, qp: (ctypes.byref(_cfg()), FAKE, qp, p0, 2048, FAKE, 256, 256, FAKE,
                            None, None)
