@@ -77,14 +77,15 @@ __device__ __forceinline__ f32x16 zero16() {
 // plan_msk[g][a][.] (group masks).
 //
 // Scan, by four waves (wave w of them: blocks a+1+w, a+5+w, ...; each id row
-// spread over the 64 lanes, kScanRows rows loaded before any is used): the
-// mask by block into rmask (LDS, n_blocks entries).
+// spread over the 64 lanes, kScanRows rows loaded before any is used, so up
+// to 32 later blocks take one memory round trip): the mask by block into
+// rmask (LDS, n_blocks entries).
 template <int kUnit>
 __device__ __forceinline__ void plan_scan(const int32_t *__restrict__ ids, int64_t g, int64_t a,
                                           int64_t n_blocks, int k, int64_t ca, int sink,
                                           int wave4, uint8_t *rmask)
 {
-    constexpr int kScanRows = 4;
+    constexpr int kScanRows = 8;
     const int lane = threadIdx.x & 63;
     const int32_t ca32 = (int32_t)ca;
     for (int64_t base = a + 1 + wave4; base < n_blocks; base += 4 * kScanRows) {
@@ -299,8 +300,8 @@ void bwd_dq_kernel(
     // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
     if (g == 0 && b == 0 && hg == 0 && tid == 0) *next_item = 0;
-    // waves 4..7 scan for the dkdv plan of chunk b (stored after the first
-    // barrier below)
+    // waves 4..7 scan for the dkdv plan of chunk b (stored after the second
+    // barrier below) while wave 0 lists the block's own tiles
     if (hg == 0 && wave >= 4)
         plan_scan<kUnit>(ids, g, b, n_blocks, k, p0 / kC + b, sink, wave - 4, rmask);
     __syncthreads();
@@ -573,23 +574,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int n_parts = min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
         if (split >= n_parts) continue;               // nothing dealt to this workgroup
         const int n_tiles = (n_all - split + n_parts - 1) / n_parts;
-        for (int i = tid; i < n_list; i += kThreads) {
-            blist[i] = plan_blk[pr * n_blocks + i];
-            bmask[i] = plan_msk[pr * n_blocks + i];
-        }
-
         const int col = lane & 31;
         const int half = lane >> 5;
         const int kh = wave & 1;         // keys 32*kh .. +32 of the chunk
         const int qh = wave >> 1;        // queries 32*qh .. +32 of each tile
-        const int64_t key_row = ca * kC + 32 * kh + col;
-        bf16x8 kb[8], vb[8];
-    #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            kb[ks] = *(const bf16x8 *)(K + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
-            vb[ks] = *(const bf16x8 *)(V + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
-        }
-        __syncthreads();                              // blist and bmask are in LDS
 
         auto tile_row0 = [&](int t) __attribute__((always_inline)) -> int64_t {
             const int T = split + n_parts * min(t, n_tiles - 1);
@@ -602,11 +590,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // lane/16), lse and Delta of the tile's queries on threads 0..63.
         struct TileIn { u32x4 q[4], d[4]; float l, dl; };
         const int lkg = lane & 15, ldp = 4 * wave + (lane >> 4);
-        auto load = [&](TileIn &r, int t) __attribute__((always_inline)) {
-            const int64_t row0 = tile_row0(t);
+        auto load_at = [&](TileIn &r, int64_t row0) __attribute__((always_inline)) {
             const uint16_t *qs = Q + (row0 + 4 * lkg) * kD + ldp * 8;
             const uint16_t *ds = dO + (row0 + 4 * lkg) * kD + ldp * 8;
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
                 r.q[j] = *(const u32x4 *)(qs + j * kD);
                 r.d[j] = *(const u32x4 *)(ds + j * kD);
@@ -615,6 +602,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             r.l = lse[row0 + qi];
             r.dl = delta[row0 + qi];
         };
+        auto load = [&](TileIn &r, int t) __attribute__((always_inline)) {
+            load_at(r, tile_row0(t));
+        };
+
+        // The part's first tile is its head's tile of the chunk's own block
+        // (list entry 0) whenever split < G: those loads, and the chunk's
+        // keys and values (MFMA operands for the whole item), go out before
+        // the list is read.
+        TileIn r0, r1;
+        const bool first_own = split < G;
+        if (first_own) load_at(r0, (g * G + split) * n_q + a * kC);
+        const int64_t key_row = ca * kC + 32 * kh + col;
+        bf16x8 kb[8], vb[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            kb[ks] = *(const bf16x8 *)(K + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
+            vb[ks] = *(const bf16x8 *)(V + (gkv * T_cap + key_row) * kD + 16 * ks + 8 * half);
+        }
+        for (int i = tid; i < n_list; i += kThreads) {
+            blist[i] = plan_blk[pr * n_blocks + i];
+            bmask[i] = plan_msk[pr * n_blocks + i];
+        }
+        __syncthreads();                              // blist and bmask are in LDS
+
         // Q and dO to LDS row-major (S and dP operands) and transposed under the
         // accumulator's query permutation (dK and dV operands); with kg = lane%16
         // the 8-byte transposed writes of the 64 lanes fall on distinct banks.
@@ -622,13 +633,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             uint8_t *B = smem + buf * kBufBytes;
             uint16_t *Qs = (uint16_t *)(B + kQOff), *dOs = (uint16_t *)(B + kDOOff);
             uint16_t *Qts = (uint16_t *)(B + kQtOff), *dOts = (uint16_t *)(B + kDOtOff);
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
                 *(u32x4 *)(Qs + (4 * lkg + j) * kRowStride + ldp * 8) = r.q[j];
                 *(u32x4 *)(dOs + (4 * lkg + j) * kRowStride + ldp * 8) = r.d[j];
             }
             const int pos = t_pos(4 * lkg);
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
                 u32x2 wq, wd;
@@ -647,14 +658,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // Tiles run in pairs (register sets r0, r1 in a fixed order, loaded two
         // tiles ahead); an odd count gets one padding step that computes nothing.
         const int n_steps = n_tiles + (n_tiles & 1);
-        TileIn r0, r1;
-        load(r0, 0);
+        if (!first_own) load(r0, 0);
         load(r1, 1);
         store(r0, 0);
         __syncthreads();
 
         f32x16 dk[4], dv[4];
-    #pragma unroll
+#pragma unroll
         for (int dt = 0; dt < 4; ++dt) { dk[dt] = zero16(); dv[dt] = zero16(); }
 
         auto step = [&](int it, TileIn &pre, const TileIn &nxt) __attribute__((always_inline)) {
@@ -681,7 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                 };
                 rd(0);
                 rd(1);
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
                     if (ks + 2 < 8) rd(ks + 2);
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kb[ks], s, 0, 0, 0);
@@ -698,12 +708,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                               ((bmask[entry] >> ((32 * kh + col) >> 3)) & 1);
             bf16x8 pb[2], dsb[2];
             bool big = false;
-    #pragma unroll
+#pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int q0 = 32 * qh + 8 * u + 4 * half;
                 const f32x4 l4 = *(const f32x4 *)(lse2s + q0);
                 const f32x4 d4 = *(const f32x4 *)(dls + q0);
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * u + e;
                     float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -l4[e]));
@@ -719,31 +729,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             // the 16 transposed operands are read before the MFMAs that use them
             // and serve the low-half round too.
             bf16x8 ta[8], tq[8];
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const int off = (32 * dt + col) * kTStride + 32 * qh + 16 * ks + 8 * half;
                     ta[2 * dt + ks] = *(const bf16x8 *)(dOtb + off);
                     tq[2 * dt + ks] = *(const bf16x8 *)(Qtb + off);
                 }
             __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
                     dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
                 }
             if (__ballot(big) != 0) {              // wave-uniform: add the low halves
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     pb[j >> 3][j & 7] = (__bf16)(s[j] - (float)pb[j >> 3][j & 7]);
                     dsb[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsb[j >> 3][j & 7]);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[2 * dt + ks], pb[ks], dv[dt], 0, 0, 0);
                         dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[2 * dt + ks], dsb[ks], dk[dt], 0, 0, 0);
@@ -761,9 +771,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // Sum the two query halves: waves 2, 3 hand their partials to waves 0, 1.
         float *red = (float *)smem;       // [2 waves][2 tensors][4 dt][16 j][64 lanes]
         if (qh == 1) {
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane] = dk[dt][j];
                     red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane] = dv[dt][j];
@@ -773,9 +783,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // lane holds key 32*kh + col, d = 32*dt + 8u + 4*half + e
         const int64_t out_row = g * n_q + a * kC + 32 * kh + col;
         if (qh == 0) {
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     dk[dt][j] += red[(((kh * 2 + 0) * 4 + dt) * 16 + j) * 64 + lane];
                     dv[dt][j] += red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane];
@@ -783,12 +793,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         }
         if (n_parts == 1) {
             if (qh == 0) {
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         f32x4 vk, vv;
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             vk[e] = dk[dt][4 * u + e] * scale;
                             vv[e] = dv[dt][4 * u + e];
@@ -817,12 +827,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         __syncthreads();                                        // red has been read
         if (qh == 0) {
             const int row = 32 * kh + col;
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < 4; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     f32x4 vk, vv;
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         vk[e] = dk[dt][4 * u + e];
                         vv[e] = dv[dt][4 * u + e];
@@ -865,10 +875,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             for (int sp = 1; sp < n_parts; ++sp) {
                 const f32x4 xk = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1)) * part_stride + off);
                 const f32x4 xv = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1) + 1) * part_stride + off);
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) { sk[e] += xk[e]; sv[e] += xv[e]; }
             }
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) sk[e] *= scale;
             *(f32x4 *)(dK + off) = sk;
             *(f32x4 *)(dV + off) = sv;
