@@ -518,7 +518,7 @@ static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits"
 // dealt still pays the scan while holding a CU (the dkdv workgroup takes most
 // of a CU's LDS), which is why the split stops at kSplit.
 constexpr int kSplit = 4;
-constexpr int kMinTiles = 6;
+constexpr int kMinTiles = 10;
 
 // kUnit = kGroup: a later block may have chosen only some of the chunk's 8
 // groups; the scan records them as an 8-bit mask per listed block, and the
