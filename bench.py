@@ -167,20 +167,34 @@ def attend_bytes(ids: np.ndarray, n_q: int, Hq: int, D: int, p0: int, unit: int 
     return float(gathered + Hq * n_q * D * 2 * 2 + Hq * n_q * 4)
 
 
-def _median_ms(torch, fn, pre=None, n=10):
-    """Median HIP-event time of fn (after 3 untimed launches); pre runs before
-    each launch, outside the events."""
-    ts = []
-    for i in range(n + 3):
+_TIMER = None
+
+
+def _median_ms(torch, fn, pre=None, n=20):
+    """Median time of fn over n launches after 300 untimed ones (the first few
+    hundred launches after a host wait run at lower clocks), each between a
+    pair of fence-free HIP events on the launch stream (a default event's
+    system-scope release adds a few microseconds to the interval it
+    brackets); pre runs before each launch, outside the events."""
+    global _TIMER
+    if _TIMER is None:
+        _TIMER = HipTimer()
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(300):
         if pre is not None:
             pre()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
         fn()
-        b.record()
+    ts = []
+    for _ in range(n):
+        if pre is not None:
+            pre()
+        a, b = _TIMER.event(), _TIMER.event()
+        _TIMER.record(a, stream)
+        fn()
+        _TIMER.record(b, stream)
         ts.append((a, b))
     torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in ts[3:])
+    t = sorted(_TIMER.elapsed_ms(a, b) for a, b in ts)
     return t[len(t) // 2]
 
 
@@ -467,16 +481,8 @@ def extra_timings(torch, hga, inputs, dev):
     res.update(variant_timings(torch, hga, inputs, dev))
     res.update(attend_timings(torch, hga, inputs, dev))
     try:
-        times = []
-        for i in range(25):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            hga.hga_attend_bwd(cfg, Q, K, V, w.p0, ids, O, lse, dO, dQ, dK, dV, ws)
-            b.record()
-            times.append((a, b))
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in times[5:])
-        res["bwd16k_ms"] = t[len(t) // 2]
+        bwd = hga.prepare("hga_attend_bwd", cfg, Q, K, V, w.p0, ids, O, lse, dO, dQ, dK, dV, ws)
+        res["bwd16k_ms"] = _median_ms(torch, bwd)
         fl = bwd_flops(ids.cpu().numpy(), w.n_q, w.G, w.D, w.p0)
         res["bwd16k_algorithmic_gflop"] = fl / 1e9
         res["bwd16k_tflops"] = fl / (res["bwd16k_ms"] * 1e-3) / 1e12
@@ -487,7 +493,7 @@ def extra_timings(torch, hga, inputs, dev):
 
 
 def attend_timings(torch, hga, inputs, dev):
-    """hga_attend_fwd alone, HIP-event timed (median of 10 after 3 warm-up
+    """hga_attend_fwd alone, HIP-event timed (median of 20 after 300 warm-up
     launches): at the 128K-history workload (k = 32), and at the 16K layer
     with L2 and the Infinity Cache flushed before every launch (a 512 MiB
     write) beside the same launches warm."""
@@ -496,7 +502,7 @@ def attend_timings(torch, hga, inputs, dev):
     def up(a):
         return torch.from_numpy(a).to(torch.bfloat16).to(dev)
 
-    def med(fn, pre=None, n=10):
+    def med(fn, pre=None, n=20):
         return _median_ms(torch, fn, pre, n)
 
     for w, tag in ((inputs.LAYER128K, "layer128k"), (inputs.LAYER16K, "layer16k")):
@@ -635,7 +641,7 @@ def group_timings(torch, hga, inputs, dev):
 
 def variant_timings(torch, hga, inputs, dev):
     """The routing variants at the 16K layer, each call HIP-event timed alone
-    (median of 10): per-query-head routing (one id row per query head, so the
+    (median of 20): per-query-head routing (one id row per query head, so the
     G heads of a kv head gather their chunks separately) through the fused
     route + attention, the routing alone, the attention alone and the
     backward; strictly causal routing (hga_route_causal) beside the default
@@ -700,7 +706,7 @@ def variant_timings(torch, hga, inputs, dev):
 def decode_timings(torch, hga, inputs, dev):
     """Routed decode at batch 1: one token after the 128K-history workload's
     last position (k = 32) and 8 tokens after the 16K layer's (k = 16), each
-    call HIP-event timed (median of 10): the routing and the attention calls,
+    call HIP-event timed (median of 20): the routing and the attention calls,
     the two in turn, and the step as one hga_route_attend_decode call.
     Algorithmic bytes: the summaries each token scores, its routed and open
     chunks' K and V (bf16), Q read and O written."""
