@@ -486,16 +486,34 @@ void bwd_dq_kernel(
     }
 
     if (!computes) return;
-    float *drow = dQ + qrow * kD;
+    // dQ leaves through the wave's own LDS area (the tiles are free after the
+    // last barrier; waves 0-3 use Ks, 4-7 Vs), half a row at a time, so that
+    // every store instruction writes four whole 256-byte row halves, as
+    // non-temporal stores (nothing reads dQ again here, and no dirty lines
+    // are left for the end-of-kernel write-back).
+    constexpr int kStage = kD / 2 + 4;          // floats per staged half row
+    float *st = (float *)(wave < 4 ? &Ks[0][0] : &Vs[0][0]) + (wave & 3) * 32 * kStage;
+    const int64_t row0 = h * n_q + b * kC + 32 * qt;
+    const int piece = lane & 15;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int hd = 0; hd < 2; ++hd) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            f32x4 v;
+        for (int dt = 2 * hd; dt < 2 * hd + 2; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * u + e] * scale;
-            *(f32x4 *)(drow + 32 * dt + 8 * u + 4 * half) = v;
+            for (int u = 0; u < 4; ++u) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * u + e] * scale;
+                *(f32x4 *)(st + col * kStage + 32 * (dt - 2 * hd) + 8 * u + 4 * half) = v;
+            }
+        // (a wave's LDS accesses complete in order: its reads see its writes)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            __builtin_nontemporal_store(*(const f32x4 *)(st + r * kStage + 4 * piece),
+                                        (f32x4 *)(dQ + (row0 + r) * kD + 64 * hd + 4 * piece));
         }
+    }
 }
 
 // ------------------------------------------------------------------- dkdv
@@ -791,21 +809,40 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                     dv[dt][j] += red[(((kh * 2 + 1) * 4 + dt) * 16 + j) * 64 + lane];
                 }
         }
-        if (n_parts == 1) {
-            if (qh == 0) {
+        // Both paths below stage the chunk's 64 rows of dK and dV row-major in
+        // LDS (the tiles are free once red has been read), so that the stores
+        // write whole rows.
+        const int64_t part_stride = Hkv * kv_div * n_q * kD;   // floats per (slot, tensor)
+        constexpr int kStageStride = kD + 4;                   // floats per staged row
+        float *stage = (float *)smem;                          // [dK, dV][64 rows][kStageStride]
+        const float kscale = n_parts == 1 ? scale : 1.0f;      // partials stay unscaled
+        __syncthreads();                                        // red has been read
+        if (qh == 0) {
+            const int row = 32 * kh + col;
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        f32x4 vk, vv;
+                for (int u = 0; u < 4; ++u) {
+                    f32x4 vk, vv;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            vk[e] = dk[dt][4 * u + e] * scale;
-                            vv[e] = dv[dt][4 * u + e];
-                        }
-                        *(f32x4 *)(dK + out_row * kD + 32 * dt + 8 * u + 4 * half) = vk;
-                        *(f32x4 *)(dV + out_row * kD + 32 * dt + 8 * u + 4 * half) = vv;
+                    for (int e = 0; e < 4; ++e) {
+                        vk[e] = dk[dt][4 * u + e] * kscale;
+                        vv[e] = dv[dt][4 * u + e];
                     }
+                    *(f32x4 *)(stage + row * kStageStride + 32 * dt + 8 * u + 4 * half) = vk;
+                    *(f32x4 *)(stage + (kC + row) * kStageStride + 32 * dt + 8 * u + 4 * half) = vv;
+                }
+        }
+        __syncthreads();
+        const int64_t row_base = g * n_q + a * kC;
+        if (n_parts == 1) {
+            // the result: non-temporal row stores (nothing here reads it again)
+            for (int i = tid; i < 2 * kC * (kD / 4); i += kThreads) {
+                const int t = i / (kC * (kD / 4)), w = i % (kC * (kD / 4));
+                const int row = w / (kD / 4), d4 = 4 * (w % (kD / 4));
+                __builtin_nontemporal_store(
+                    *(const f32x4 *)(stage + (t * kC + row) * kStageStride + d4),
+                    (f32x4 *)((t ? dV : dK) + (row_base + row) * kD + d4));
             }
             continue;
         }
@@ -821,29 +858,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         // before reading them. (A device-scope release fence instead writes back
         // the XCD's whole L2 in every workgroup: 7-21 us per split workgroup,
         // measured.)
-        const int64_t part_stride = Hkv * kv_div * n_q * kD;   // floats per (slot, tensor)
-        constexpr int kStageStride = kD + 4;                   // floats per staged row
-        float *stage = (float *)smem;                          // [dK, dV][64 rows][kStageStride]
-        __syncthreads();                                        // red has been read
-        if (qh == 0) {
-            const int row = 32 * kh + col;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    f32x4 vk, vv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        vk[e] = dk[dt][4 * u + e];
-                        vv[e] = dv[dt][4 * u + e];
-                    }
-                    *(f32x4 *)(stage + row * kStageStride + 32 * dt + 8 * u + 4 * half) = vk;
-                    *(f32x4 *)(stage + (kC + row) * kStageStride + 32 * dt + 8 * u + 4 * half) = vv;
-                }
-        }
-        __syncthreads();
         {
-            const int64_t row_base = g * n_q + a * kC;
             float *pk = split == 0 ? dK : part + (int64_t)(2 * (split - 1)) * part_stride;
             float *pv = split == 0 ? dV : part + (int64_t)(2 * (split - 1) + 1) * part_stride;
             // pair i of tensor t: row (i / 64), dims 2 (i % 64) .. +2
@@ -866,8 +881,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         if (!is_last) continue;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // 64 keys x 128 d per tensor; thread t sums float4 column (t % 32) of rows
-        // t/32, t/32 + 8, ...
-        const int64_t row_base = g * n_q + a * kC;
+        // t/32, t/32 + 8, ... (whole rows per 32 threads: non-temporal stores)
         for (int r = tid >> 5; r < kC; r += kThreads / 32) {
             const int64_t off = (row_base + r) * kD + 4 * (tid & 31);
             f32x4 sk = *(const f32x4 *)(dK + off);
@@ -880,8 +894,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) sk[e] *= scale;
-            *(f32x4 *)(dK + off) = sk;
-            *(f32x4 *)(dV + off) = sv;
+            __builtin_nontemporal_store(sk, (f32x4 *)(dK + off));
+            __builtin_nontemporal_store(sv, (f32x4 *)(dV + off));
         }
     }
 }

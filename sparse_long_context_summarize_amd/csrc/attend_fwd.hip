@@ -565,13 +565,16 @@ void attend_fwd_kernel(
     if (half == 0)
         lse[row0 + col] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
     // (a wave's LDS accesses complete in order: its reads see its writes)
+    // O goes out with non-temporal stores: nothing in this kernel reads it
+    // again, and written-back lines would otherwise sit dirty in L2 for the
+    // end-of-kernel write-back (measured: 39.7 -> 38.4 us at the 16K layer).
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     const int piece = lane & 15;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + (lane >> 4);
-        *(u32x4 *)(O + (row0 + r) * kD + 8 * piece) =
-            *(const u32x4 *)(st + r * kOStride + 8 * piece);
+        __builtin_nontemporal_store(*(const u32x4 *)(st + r * kOStride + 8 * piece),
+                                    (u32x4 *)(O + (row0 + r) * kD + 8 * piece));
     }
 }
 
