@@ -253,13 +253,13 @@ hga_status hga_attend_bwd(const hga_config *cfg, const void *Q, const void *K,
  * address is looked up once per device, on the first call there. A call whose
  * hga_attend_bwd_workspace_bytes exceeds that size returns HGA_ERR_CAPACITY
  * (the 16K-history Qwen3-8B layer's backward, 32 query heads over 8 kv heads
- * and 2048 active queries, needs 48.3 MiB). The call allocates nothing (no
+ * and 2048 active queries, needs 112.3 MiB). The call allocates nothing (no
  * hipMalloc, no hipFree, no allocating library routine). Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one GPU (two
  * streams, two host threads) race and must be serialized by the caller.
  * The stream must belong to the current device (else HGA_ERR_INVALID_ARG).
  */
-#define HGA_BWD_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+#define HGA_BWD_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
 hga_status hga_attend_bwd_noalloc(const hga_config *cfg, const void *Q, const void *K,
                                   const void *V, int64_t T_cap, int64_t p0, int64_t n_q,
                                   const int32_t *ids, const void *O, const float *lse,

@@ -531,12 +531,25 @@ static_assert(2 * kBufBytes >= 2 * 2 * 4 * 16 * 64 * 4, "reduction scratch fits"
 
 // A chunk's query tiles go to up to kSplit workgroups, at least kMinTiles
 // tiles each. Routing concentrates on a few high-scoring chunks (at the 16K
-// backward workload one chunk has 52 (block, head) tiles, the mean is 7.4),
-// and the longest chain sets the kernel's time. A workgroup with nothing
-// dealt still pays the scan while holding a CU (the dkdv workgroup takes most
-// of a CU's LDS), which is why the split stops at kSplit.
-constexpr int kSplit = 4;
-constexpr int kMinTiles = 10;
+// backward workload one chunk has 52 (block, head) tiles, the mean is 7.4,
+// and 171 of the 256 (chunk, unit) pairs have only their own block's 4), so
+// the kernel's time is set by how the parts are packed onto the CUs: an item
+// costs about 5 us of set-up and epilogue plus 2-2.7 us per tile (measured).
+constexpr int kSplit = 8;
+constexpr int kMinTiles = 8;
+// Work order: the items go in four size levels, largest first (parts of at
+// least 9 tiles, 7-8, 5-6, then the rest), earlier chunks first within a
+// level, so that small items fill in at the end instead of long ones starting
+// late (a simulation of the measured item costs put this within 0.1 us of a
+// full largest-first sort at the 16K backward workload). Every workgroup
+// computes the same order from the plan lengths: a stable counting sort, its
+// four counts packed in 16-bit fields of one 64-bit prefix sum. Up to
+// kOrderUnits (chunk, unit) pairs; past that the items run in chunk order.
+constexpr int kOrderUnits = 512;
+constexpr int kOrderLevels = 4;
+__device__ __forceinline__ int order_level(int tiles) {
+    return tiles >= 9 ? 0 : tiles >= 7 ? 1 : tiles >= 5 ? 2 : 3;
+}
 
 // kUnit = kGroup: a later block may have chosen only some of the chunk's 8
 // groups; the scan records them as an 8-bit mask per listed block, and the
@@ -556,6 +569,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __shared__ uint8_t bmask[kMaxBlocksDkdv];
     __shared__ int is_last;
     __shared__ int item_s;
+    __shared__ uint16_t order[kOrderUnits * kSplit];   // plan index << 4 | part
+    __shared__ uint64_t o_wave[kThreads / 64];
+    __shared__ int o_total;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -567,17 +583,106 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // (A grid of one workgroup per item left CUs idle: dispatch is in order
     // and stalls behind the busiest XCD, so the CUs freed by items with
     // nothing dealt were not refilled for tens of microseconds.)
-    const int64_t n_items = Hkv * kv_div * n_blocks * kSplit;
+    const int64_t n_units = Hkv * kv_div;
+    const int64_t n_pairs = n_units * n_blocks;        // (unit, chunk) pairs: plan entries
+    const int64_t n_items = n_pairs * kSplit;
+    auto parts_of = [&](int n_all) __attribute__((always_inline)) {
+        return min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
+    };
+    // (the first item is taken before the order is built: its round trip
+    // overlaps the plan loads)
+    if (tid == 0) item_s = atomicAdd(next_item, 1);
+    const bool sorted = n_pairs <= kOrderUnits;
+    if (sorted) {
+        // thread t takes pairs q = 2t, 2t + 1 in chunk-major order (q = a *
+        // n_units + g: plan index g * n_blocks + a); the parts of a pair with
+        // n_all tiles hold ceil(n_all / np) tiles (the first n_hi) or floor
+        static_assert(2 * kThreads >= kOrderUnits, "two pairs per thread");
+        int na[2], pr2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 2 * tid + i;
+            pr2[i] = q < n_pairs ? (int)((q % n_units) * n_blocks + q / n_units) : 0;
+            na[i] = q < n_pairs ? plan_n[pr2[i]] * G : 0;
+        }
+        auto split_of = [&](int n_all, int &np, int &n_hi, int &t_hi) __attribute__((always_inline)) {
+            np = parts_of(n_all);
+            t_hi = (n_all + np - 1) / np;
+            n_hi = n_all % np == 0 ? np : n_all % np;
+        };
+        uint64_t mine = 0;                  // this thread's item counts by level
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (na[i] == 0) continue;
+            int np, n_hi, t_hi;
+            split_of(na[i], np, n_hi, t_hi);
+            mine += (uint64_t)n_hi << (16 * order_level(t_hi));
+            if (np > n_hi) mine += (uint64_t)(np - n_hi) << (16 * order_level(t_hi - 1));
+        }
+        // exclusive prefix over threads: within the wave, then across waves
+        uint64_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t lo = __shfl_up((uint32_t)incl, o), hi = __shfl_up((uint32_t)(incl >> 32), o);
+            if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+        }
+        if (lane == 63) o_wave[wave] = incl;
+        __syncthreads();
+        uint64_t excl = incl - mine, total = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            const uint64_t v = o_wave[w];
+            if (w < wave) excl += v;
+            total += v;
+        }
+        int base[kOrderLevels];
+        int start = 0;
+#pragma unroll
+        for (int l = 0; l < kOrderLevels; ++l) {
+            base[l] = start + (int)((excl >> (16 * l)) & 0xFFFF);
+            start += (int)((total >> (16 * l)) & 0xFFFF);
+        }
+        if (tid == 0) o_total = start;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (na[i] == 0) continue;
+            int np, n_hi, t_hi;
+            split_of(na[i], np, n_hi, t_hi);
+            for (int sp = 0; sp < np; ++sp) {
+                const int l = order_level(sp < n_hi ? t_hi : t_hi - 1);
+                int pos = 0;
+#pragma unroll
+                for (int m = 0; m < kOrderLevels; ++m)
+                    if (m == l) pos = base[m]++;
+                order[pos] = (uint16_t)((pr2[i] << 4) | sp);
+            }
+        }
+    }
+    static_assert(kOrderLevels * 16 <= 64 && kOrderUnits * kSplit < 65536, "level counts fit 16 bits");
+    static_assert(kOrderUnits * 16 <= 65536 && kSplit <= 16, "order entries fit 16 bits");
+    bool first = true;
     for (;;) {
-        __syncthreads();                          // the last item is done with LDS
-        if (tid == 0) item_s = atomicAdd(next_item, 1);
+        if (!first) {
+            __syncthreads();                      // the last item is done with LDS
+            if (tid == 0) item_s = atomicAdd(next_item, 1);
+        }
+        first = false;
         __syncthreads();
         const int64_t item = item_s;
-        if (item >= n_items) break;
-        const int64_t n_units = Hkv * kv_div;
-        const int split = (int)(item % kSplit);
-        const int64_t g = (item / kSplit) % n_units;    // routing unit: its id rows
-        const int64_t a = item / (kSplit * n_units);    // active chunk = its own query block
+        int split;
+        int64_t g, a;
+        if (sorted) {
+            if (item >= o_total) break;
+            const int e = order[item];
+            split = e & 15;
+            g = (e >> 4) / n_blocks;                    // routing unit: its id rows
+            a = (e >> 4) % n_blocks;                    // active chunk = its own query block
+        } else {
+            if (item >= n_items) break;
+            split = (int)(item % kSplit);
+            g = (item / kSplit) % n_units;
+            a = item / (kSplit * n_units);
+        }
         const int64_t gkv = g / kv_div;                 // kv head
         const int64_t ca = p0 / kC + a;                 // absolute chunk index
 
@@ -589,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int64_t pr = g * n_blocks + a;
         const int n_list = plan_n[pr];
         const int n_all = n_list * G;
-        const int n_parts = min(kSplit, max(1, (n_all + kMinTiles - 1) / kMinTiles));
+        const int n_parts = parts_of(n_all);
         if (split >= n_parts) continue;               // nothing dealt to this workgroup
         const int n_tiles = (n_all - split + n_parts - 1) / n_parts;
         const int col = lane & 31;
@@ -881,21 +986,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         if (!is_last) continue;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // 64 keys x 128 d per tensor; thread t sums float4 column (t % 32) of rows
-        // t/32, t/32 + 8, ... (whole rows per 32 threads: non-temporal stores)
-        for (int r = tid >> 5; r < kC; r += kThreads / 32) {
-            const int64_t off = (row_base + r) * kD + 4 * (tid & 31);
-            f32x4 sk = *(const f32x4 *)(dK + off);
-            f32x4 sv = *(const f32x4 *)(dV + off);
-            for (int sp = 1; sp < n_parts; ++sp) {
-                const f32x4 xk = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1)) * part_stride + off);
-                const f32x4 xv = *(const f32x4 *)(part + (int64_t)(2 * (sp - 1) + 1) * part_stride + off);
+        // t/32, t/32 + 8, ... (whole rows per 32 threads: non-temporal stores).
+        // This workgroup's own partial is still staged in LDS; the other
+        // parts' are loaded for two rows at a time, every load issued before
+        // the first add (a load-then-add chain per part would cost one memory
+        // round trip each, at the end of the chunk's chain). The sum still
+        // runs in part order 0, 1, ... .
+        constexpr int kRowsPer = kC / (kThreads / 32);          // rows per thread
+        constexpr int kRowBatch = 2;
+        const int c4 = 4 * (tid & 31);
+        for (int rb = 0; rb < kRowsPer; rb += kRowBatch) {
+            f32x4 xk[kRowBatch][kSplit], xv[kRowBatch][kSplit];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { sk[e] += xk[e]; sv[e] += xv[e]; }
+            for (int i = 0; i < kRowBatch; ++i) {
+                const int r = (tid >> 5) + (kThreads / 32) * (rb + i);
+                const int64_t off = (row_base + r) * kD + c4;
+#pragma unroll
+                for (int sp = 0; sp < kSplit; ++sp) {
+                    xk[i][sp] = xv[i][sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (sp >= n_parts) continue;
+                    if (sp == split) {
+                        xk[i][sp] = *(const f32x4 *)(stage + r * kStageStride + c4);
+                        xv[i][sp] = *(const f32x4 *)(stage + (kC + r) * kStageStride + c4);
+                    } else {
+                        const float *pk = sp == 0 ? dK : part + (int64_t)(2 * (sp - 1)) * part_stride;
+                        const float *pv = sp == 0 ? dV : part + (int64_t)(2 * (sp - 1) + 1) * part_stride;
+                        xk[i][sp] = *(const f32x4 *)(pk + off);
+                        xv[i][sp] = *(const f32x4 *)(pv + off);
+                    }
+                }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sk[e] *= scale;
-            __builtin_nontemporal_store(sk, (f32x4 *)(dK + off));
-            __builtin_nontemporal_store(sv, (f32x4 *)(dV + off));
+            for (int i = 0; i < kRowBatch; ++i) {
+                const int r = (tid >> 5) + (kThreads / 32) * (rb + i);
+                const int64_t off = (row_base + r) * kD + c4;
+                f32x4 sk = xk[i][0], sv = xv[i][0];
+#pragma unroll
+                for (int sp = 1; sp < kSplit; ++sp) {
+                    if (sp >= n_parts) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { sk[e] += xk[i][sp][e]; sv[e] += xv[i][sp][e]; }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sk[e] *= scale;
+                __builtin_nontemporal_store(sk, (f32x4 *)(dK + off));
+                __builtin_nontemporal_store(sv, (f32x4 *)(dV + off));
+            }
         }
     }
 }

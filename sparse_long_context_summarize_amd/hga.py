@@ -34,7 +34,7 @@ HGA_GROUP = 8
 HGA_MAX_SINK_CHUNKS = 64
 HGA_ROUTE_PER_KV_HEAD = 0
 HGA_ROUTE_PER_Q_HEAD = 1
-HGA_BWD_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+HGA_BWD_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class hga_config(ctypes.Structure):

@@ -352,7 +352,7 @@ def test_routing_variant_checks():
     def plan(U):               # per (unit, chunk): list length, block ids, group masks
         return up(U * nb * 4) + up(U * nb * nb * 2) + up(U * nb * nb)
 
-    slots = 3                  # workgroups past the first that may share one active chunk
+    slots = 7                  # workgroups past the first that may share one active chunk
     assert a == delta + up((8 * nb + 1) * 4) + plan(8) + slots * 2 * 8 * n_q * 128 * 4
     assert b == delta + up((32 * nb + 1) * 4) + plan(32) + slots * 2 * 32 * n_q * 128 * 4 \
         + 2 * 32 * n_q * 128 * 4
