@@ -544,8 +544,10 @@ constexpr int kMinTiles = 8;
 // full largest-first sort at the 16K backward workload). Every workgroup
 // computes the same order from the plan lengths: a stable counting sort, its
 // four counts packed in 16-bit fields of one 64-bit prefix sum. Up to
-// kOrderUnits (chunk, unit) pairs; past that the items run in chunk order.
-constexpr int kOrderUnits = 512;
+// kOrderUnits (chunk, unit) pairs and kOrderCap items; past that the items
+// run in chunk order.
+constexpr int kOrderUnits = 1024;
+constexpr int kOrderCap = 4096;
 constexpr int kOrderLevels = 4;
 __device__ __forceinline__ int order_level(int tiles) {
     return tiles >= 9 ? 0 : tiles >= 7 ? 1 : tiles >= 5 ? 2 : 3;
@@ -569,8 +571,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __shared__ uint8_t bmask[kMaxBlocksDkdv];
     __shared__ int is_last;
     __shared__ int item_s;
-    __shared__ uint16_t order[kOrderUnits * kSplit];   // plan index << 4 | part
+    __shared__ uint16_t order[kOrderCap];              // plan index << 4 | part
     __shared__ uint64_t o_wave[kThreads / 64];
+    __shared__ uint16_t o_na[kOrderUnits];             // tiles of each (chunk, unit) pair
     __shared__ int o_total;
 
     const int tid = threadIdx.x;
@@ -592,18 +595,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // (the first item is taken before the order is built: its round trip
     // overlaps the plan loads)
     if (tid == 0) item_s = atomicAdd(next_item, 1);
-    const bool sorted = n_pairs <= kOrderUnits;
+    bool sorted = n_pairs <= kOrderUnits;
     if (sorted) {
-        // thread t takes pairs q = 2t, 2t + 1 in chunk-major order (q = a *
-        // n_units + g: plan index g * n_blocks + a); the parts of a pair with
-        // n_all tiles hold ceil(n_all / np) tiles (the first n_hi) or floor
-        static_assert(2 * kThreads >= kOrderUnits, "two pairs per thread");
-        int na[2], pr2[2];
+        // thread t takes pairs q = kPer t .. kPer t + kPer - 1 in chunk-major
+        // order (q = a * n_units + g: plan index g * n_blocks + a); their tile
+        // counts n_all wait in LDS. The parts of a pair hold ceil(n_all / np)
+        // tiles (the first n_hi) or floor.
+        constexpr int kPer = kOrderUnits / kThreads;
+        auto plan_of = [&](int q) __attribute__((always_inline)) {
+            return (int)((q % n_units) * n_blocks + q / n_units);
+        };
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * tid + i;
-            pr2[i] = q < n_pairs ? (int)((q % n_units) * n_blocks + q / n_units) : 0;
-            na[i] = q < n_pairs ? plan_n[pr2[i]] * G : 0;
+        for (int i = 0; i < kPer; ++i) {
+            const int q = kPer * tid + i;
+            o_na[q] = q < n_pairs ? (uint16_t)(plan_n[plan_of(q)] * G) : (uint16_t)0;
         }
         auto split_of = [&](int n_all, int &np, int &n_hi, int &t_hi) __attribute__((always_inline)) {
             np = parts_of(n_all);
@@ -611,11 +616,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             n_hi = n_all % np == 0 ? np : n_all % np;
         };
         uint64_t mine = 0;                  // this thread's item counts by level
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (na[i] == 0) continue;
+        for (int i = 0; i < kPer; ++i) {
+            const int n_all = o_na[kPer * tid + i];
+            if (n_all == 0) continue;
             int np, n_hi, t_hi;
-            split_of(na[i], np, n_hi, t_hi);
+            split_of(n_all, np, n_hi, t_hi);
             mine += (uint64_t)n_hi << (16 * order_level(t_hi));
             if (np > n_hi) mine += (uint64_t)(np - n_hi) << (16 * order_level(t_hi - 1));
         }
@@ -643,23 +648,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
             start += (int)((total >> (16 * l)) & 0xFFFF);
         }
         if (tid == 0) o_total = start;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (na[i] == 0) continue;
+        sorted = start <= kOrderCap;        // (the same in every thread)
+        for (int i = 0; i < kPer && sorted; ++i) {
+            const int q = kPer * tid + i;
+            const int n_all = o_na[q];
+            if (n_all == 0) continue;
             int np, n_hi, t_hi;
-            split_of(na[i], np, n_hi, t_hi);
+            split_of(n_all, np, n_hi, t_hi);
             for (int sp = 0; sp < np; ++sp) {
                 const int l = order_level(sp < n_hi ? t_hi : t_hi - 1);
                 int pos = 0;
 #pragma unroll
                 for (int m = 0; m < kOrderLevels; ++m)
                     if (m == l) pos = base[m]++;
-                order[pos] = (uint16_t)((pr2[i] << 4) | sp);
+                order[pos] = (uint16_t)((plan_of(q) << 4) | sp);
             }
         }
     }
     static_assert(kOrderLevels * 16 <= 64 && kOrderUnits * kSplit < 65536, "level counts fit 16 bits");
     static_assert(kOrderUnits * 16 <= 65536 && kSplit <= 16, "order entries fit 16 bits");
+    static_assert(kOrderUnits % kThreads == 0, "whole pairs per thread");
     bool first = true;
     for (;;) {
         if (!first) {
