@@ -285,37 +285,6 @@ void bwd_dq_kernel(
     const uint16_t *Kg = K + gkv * T_cap * kD;
     const uint16_t *Vg = V + gkv * T_cap * kD;
 
-    // the sink window's units, the routed units (past the sink, before P,
-    // repeats dropped), then the local chunk
-    if (wave == 0) {
-        const int ns = sink_units(sink, P, kUnit);
-        write_sink_units(list, ns);
-        const int n = build_unit_list(ids + (g * n_blocks + b) * k, k,
-                                      (int64_t)sink * (kC / kUnit), P / kUnit, list + ns);
-        if (lane == 0) {
-            list[ns + n] = (int)local_chunk;
-            list_n = ns + n + 1;
-        }
-    }
-    // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
-    if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
-    if (g == 0 && b == 0 && hg == 0 && tid == 0) *next_item = 0;
-    // waves 4..7 scan for the dkdv plan of chunk b (stored after the second
-    // barrier below) while wave 0 lists the block's own tiles
-    if (hg == 0 && wave >= 4)
-        plan_scan<kUnit>(ids, g, b, n_blocks, k, p0 / kC + b, sink, wave - 4, rmask);
-    __syncthreads();
-    const int n_units = list_n - 1;
-    const int n_tiles = (kUnit == kC ? n_units : (n_units + 7) / 8) + 1;
-    // keys of the last routed tile (groups: 8 per group present; else 64)
-    const int pad_keys = (kUnit != kC && (n_units & 7) != 0) ? kGroup * (n_units & 7) : kC;
-    // Each pass walks the tile list once, padded to an even number of steps
-    // (a padding step moves data but computes nothing), so both pass loops
-    // run whole pairs with the register sets in one fixed order.
-    const int n_pass = n_tiles + (n_tiles & 1);
-    const int n_steps = 2 * n_pass;
-    const bool kgrp = tid >= kDqThreads / 2;
-
     // (as in the forward: with HW < 4 the two query halves' waves sit on
     // different SIMDs)
     const int qt = wave >> 2;
@@ -328,14 +297,56 @@ void bwd_dq_kernel(
     const int64_t qrow = h * n_q + b * kC + 32 * qt + col;
     bf16x8 qf[8], df[8];
     float lse2 = 0.f, dl = 0.f;
-    if (computes) {
+    // Q^T and dO^T (MFMA operands for the whole kernel) go out first, ahead
+    // of the list barrier: the plan-scan waves issue theirs after their scan
+    // loads, wave 0 after its id row (loads complete in order).
+    auto load_qdo = [&]() __attribute__((always_inline)) {
+        if (!computes) return;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             qf[ks] = *(const bf16x8 *)(Q + qrow * kD + 16 * ks + 8 * half);
             df[ks] = *(const bf16x8 *)(dO + qrow * kD + 16 * ks + 8 * half);
         }
         lse2 = lse[qrow] * 1.44269504088896340736f;
+    };
+    // the sink window's units, the routed units (past the sink, before P,
+    // repeats dropped), then the local chunk
+    if (wave == 0) {
+        const int32_t *id_row = ids + (g * n_blocks + b) * k;
+        const int id_first = lane < k ? id_row[lane] : -1;
+        load_qdo();
+        const int ns = sink_units(sink, P, kUnit);
+        write_sink_units(list, ns);
+        const int n = build_unit_list(id_row, k, (int64_t)sink * (kC / kUnit), P / kUnit,
+                                      list + ns, id_first);
+        if (lane == 0) {
+            list[ns + n] = (int)local_chunk;
+            list_n = ns + n + 1;
+        }
+    } else if (!(hg == 0 && wave >= 4)) {
+        load_qdo();
     }
+    // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
+    if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
+    if (g == 0 && b == 0 && hg == 0 && tid == 0) *next_item = 0;
+    // waves 4..7 scan for the dkdv plan of chunk b (stored after the second
+    // barrier below) while wave 0 lists the block's own tiles
+    if (hg == 0 && wave >= 4) {
+        plan_scan<kUnit>(ids, g, b, n_blocks, k, p0 / kC + b, sink, wave - 4, rmask);
+        load_qdo();
+    }
+    __syncthreads();
+    const int n_units = list_n - 1;
+    const int n_tiles = (kUnit == kC ? n_units : (n_units + 7) / 8) + 1;
+    // keys of the last routed tile (groups: 8 per group present; else 64)
+    const int pad_keys = (kUnit != kC && (n_units & 7) != 0) ? kGroup * (n_units & 7) : kC;
+    // Each pass walks the tile list once, padded to an even number of steps
+    // (a padding step moves data but computes nothing), so both pass loops
+    // run whole pairs with the register sets in one fixed order.
+    const int n_pass = n_tiles + (n_tiles & 1);
+    const int n_steps = 2 * n_pass;
+    const bool kgrp = tid >= kDqThreads / 2;
+
     const int *lst = list;
     // first token of a chunk tile, or the token of row r of a group tile
     // (the local tile is last; padding rows repeat the tile's last group)

@@ -82,15 +82,24 @@ __device__ __forceinline__ float row16_sum(float x) {
 // keys are taken). When every key is equal, T is that key. The chosen set is
 // then every key > T plus the lowest-positioned keys == T, k in all. Host and
 // device code: the CPU tests run this very function.
-template <typename CountGe>
+struct SameInt {
+    __host__ __device__ int operator()(int v) const { return v; }
+};
+// uniform(bit) marks the bit index as the same in every lane: the device
+// callers pass readfirstlane, which keeps the whole step -- candidate, ballot
+// counts, update -- on the scalar unit instead of crossing to vector
+// registers and back every step.
+template <typename CountGe, typename Uniform = SameInt>
 __host__ __device__ __forceinline__ uint32_t select_threshold(uint32_t mx, uint32_t mn, int k,
-                                                              CountGe count_ge)
+                                                              CountGe count_ge,
+                                                              Uniform uniform = Uniform{})
 {
     const uint32_t diff = mx ^ mn;
     if (diff == 0u) return mx;
     const int top = 31 - __builtin_clz(diff);
     uint32_t T = (top == 31) ? 0u : (mx & ~((2u << top) - 1u));
     for (int bit = top; bit >= 0; --bit) {
+        bit = uniform(bit);
         const uint32_t cand = T | (1u << bit);
         const int cnt = count_ge(cand);
         if (cnt >= k) T = cand;
@@ -124,7 +133,7 @@ __device__ __forceinline__ int wave_select(const uint32_t *keys, int n, int k, i
             cnt += __popcll(__ballot(p < n && keys[p] >= cand));
         }
         return cnt;
-    });
+    }, [](int v) { return __builtin_amdgcn_readfirstlane(v); });
     int n_gt = 0;
     for (int base = 0; base < n; base += 64) {
         const int p = base + lane;
@@ -215,7 +224,7 @@ __device__ __forceinline__ int select_top_k_reg(const uint32_t *keys, int nE, in
 #pragma unroll
             for (int it = 0; it < NI; ++it) cnt += __popcll(__ballot(key[it] >= cand));
             return cnt;
-        });
+        }, [](int v) { return __builtin_amdgcn_readfirstlane(v); });
         int n_gt = 0;
 #pragma unroll
         for (int it = 0; it < NI; ++it) n_gt += __popcll(__ballot(key[it] > T));
