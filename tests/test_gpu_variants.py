@@ -131,6 +131,16 @@ def test_per_head_backward(G, p0):
     check(x, p0, k, 1, res, f"per head bwd G={G} p0={p0}")
 
 
+def test_per_head_backward_beyond_the_sorted_queue():
+    """More (unit, chunk) pairs than the dK/dV kernel sorts by size (1024):
+    8 query-head units x 136 active blocks = 1088, so the items run in chunk
+    order."""
+    p0, n_q, k = 1024, 64 * 136, 3
+    x = inputs.small_random(740, 8, 1, 128, p0 + n_q, n_q, bf16=True, with_dO=True)
+    res = run(x, p0, k, bwd=True)
+    check(x, p0, k, 0, res, "per head bwd, 1088 pairs")
+
+
 def test_per_head_more_than_2048_candidates():
     T, n_q, k = 64 * 2100, 128, 9
     x = inputs.small_random(730, 4, 1, 128, T, n_q, bf16=True)
