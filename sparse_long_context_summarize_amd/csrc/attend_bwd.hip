@@ -20,7 +20,7 @@
 //          chunk a (the dkdv plan); the list's (block, query head) tiles, own
 //          block first, are dealt round-robin to up to kSplit parts, and a
 //          persistent grid (one workgroup per CU) takes (chunk, unit, part)
-//          items from a work queue:
+//          items from a work queue, largest parts first:
 //          S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
 //          Wave w owns keys 32*(w&1).. and queries 32*(w>>1).. of each query
 //          tile; the two query halves are summed through LDS. A chunk with
@@ -592,8 +592,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int wave = tid >> 6;
     const int64_t n_blocks = n_q / kC;
     // Persistent: one workgroup per CU takes (chunk, unit, part) items from a
-    // counter in item order until none is left; earlier chunks come first,
-    // as more later blocks can choose them (their lists are the longest).
+    // counter until none is left, in the size order built below (or, past
+    // kOrderUnits pairs, in chunk order, earlier chunks first: more later
+    // blocks can choose them, so their lists tend to be the longest).
     // (A grid of one workgroup per item left CUs idle: dispatch is in order
     // and stalls behind the busiest XCD, so the CUs freed by items with
     // nothing dealt were not refilled for tens of microseconds.)
