@@ -486,6 +486,8 @@ def extra_timings(torch, hga, inputs, dev):
         fl = bwd_flops(ids.cpu().numpy(), w.n_q, w.G, w.D, w.p0)
         res["bwd16k_algorithmic_gflop"] = fl / 1e9
         res["bwd16k_tflops"] = fl / (res["bwd16k_ms"] * 1e-3) / 1e12
+        n2, nw = hga.hga_diag_bwd_second_pass(cfg, w.n_q, ws)
+        res["bwd16k_dq_second_pass_workgroups"] = f"{n2} of {nw}"
     except hga.HGAError as e:
         res["bwd16k_ms"] = None
         res["bwd16k_error"] = str(e)
@@ -618,6 +620,8 @@ def group_timings(torch, hga, inputs, dev):
     ms = _median_ms(torch, layer)
     ms_fused = _median_ms(torch, layer_fused)
     ms_bwd = _median_ms(torch, bwd)
+    n2, nw = hga.hga_diag_bwd_second_pass(cfg, w.n_q, ws)
+    res["groups16k_bwd_dq_second_pass_workgroups"] = f"{n2} of {nw}"
     g = gids.cpu().numpy()
     fl_bwd = bwd_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
     fl = attend_flops(g, w.n_q, w.G, w.D, w.p0, unit=hga.HGA_GROUP)
@@ -685,6 +689,9 @@ def variant_timings(torch, hga, inputs, dev):
         fn()
         res[f"{name}_us"] = _median_ms(torch, fn) * 1e3
     calls["perhead16k_route_attend"]()
+    calls["perhead16k_bwd"]()
+    n2, nw = hga.hga_diag_bwd_second_pass(cfg_h, w.n_q, ws)
+    res["perhead16k_bwd_dq_second_pass_workgroups"] = f"{n2} of {nw}"
     torch.cuda.synchronize()
     g = ids_h.cpu().numpy()                    # one row per query head: G = 1 per unit
     fl = attend_flops(g, w.n_q, 1, w.D, w.p0)

@@ -223,10 +223,17 @@ size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
  * (sums over the G query heads that share kv head g, each head with its own
  * A(i); A(i) and the ids rule as for hga_attend_fwd, a set per row, id rows
  * per cfg->route_heads). lse is the output of
- * hga_attend_fwd for the same arguments. Delta is recomputed in fp32 from P
- * and dP rather than taken as dO . O, because the bf16 rounding of O would
- * reach dS undamped wherever attention concentrates on a few keys; O is
- * therefore accepted for interface symmetry but not read (it may be NULL).
+ * hga_attend_fwd for the same arguments, O (bf16, may be NULL) its output.
+ * Delta is summed exactly in fp32 from P and dP. The dQ kernel makes one pass
+ * over each block's tiles with the estimate D_i = dO_i . O_i in place of
+ * Delta_i and keeps it for the 32 query rows of a wave when each has
+ * |Delta_i - D_i| <= 2^-8 sum_j P_ij |dO_i . V_j - D_i| (the estimate then moves
+ * dQ_i by no more than the worst-case bound of rounding every dS term to bf16
+ * once, 2^-8 being bf16's unit roundoff); other waves -- attention concentrated
+ * on a few keys, where O's bf16 rounding would reach dS undamped, and every
+ * wave when O is NULL -- recompute dQ in a second pass with the exact Delta
+ * (hga_diag_bwd_second_pass counts the workgroups that ran one). O is read only
+ * for the estimate: any O gives gradients within that bound.
  * Every element of dQ, dK and dV is written; the caller does not clear them.
  * Deterministic: no output is accumulated with atomics, every sum has a fixed
  * order (a per-chunk counter in the workspace only decides which workgroup
@@ -360,8 +367,8 @@ hga_status hga_route_attend_fwd_groups(const hga_config *cfg, const void *Q, con
  * hga_attend_bwd_groups -- hga_attend_bwd for hga_attend_fwd_groups: the same
  * gradients (dQ of every active query; dK, dV of the active keys, summed over
  * the G heads; history detached) with A(i) built from group_ids as in
- * hga_attend_fwd_groups. lse is that call's output; O is not read (may be
- * NULL). The workspace is hga_attend_bwd_workspace_bytes(cfg, n_q) bytes, with
+ * hga_attend_fwd_groups. lse and O are that call's outputs (O may be NULL:
+ * it feeds only the dQ kernel's Delta estimate, as in hga_attend_bwd). The workspace is hga_attend_bwd_workspace_bytes(cfg, n_q) bytes, with
  * the same rules as for hga_attend_bwd; results are deterministic.
  */
 hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const void *K,
@@ -468,6 +475,18 @@ size_t hga_diag_gather_sink_words(const hga_config *cfg, int64_t n_q);
 hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, int64_t T_cap,
                            int64_t p0, int64_t n_q, const int32_t *ids, uint32_t *sink,
                            size_t sink_words, hipStream_t stream);
+
+/*
+ * hga_diag_bwd_second_pass -- how many dq workgroups of the last
+ * hga_attend_bwd or hga_attend_bwd_groups call on this workspace (same cfg and
+ * n_q) took the second pass over their tiles, which recomputes dQ with the
+ * exact Delta where the estimate from O was not close enough (or O was NULL).
+ * Waits for the stream; writes *n_second and *n_workgroups (the call's dq
+ * workgroups). Other arguments and errors as for hga_attend_bwd.
+ */
+hga_status hga_diag_bwd_second_pass(const hga_config *cfg, int64_t n_q, const void *workspace,
+                                    size_t ws_bytes, int64_t *n_second, int64_t *n_workgroups,
+                                    hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *hga_status_string(hga_status status);

@@ -7,14 +7,23 @@
 // runs in a fixed order, so results are bitwise reproducible:
 //   dq     query-major, the forward's work unit (query block x kv head) and
 //          wave layout (8 waves, two per SIMD, 32 queries of one head each),
-//          two passes over the routed chunks and the causal local block:
+//          one pass over the routed chunks and the causal local block, a
+//          second one only where the first cannot be trusted:
 //          pass 1: S^T = K Q^T, dP^T = V dO^T, P = exp(S - lse),
-//                  Delta_i = sum_j P_ij dP_ij (fp32; written for dkdv)
-//          pass 2: dS = P (dP - Delta), dQ^T += K^T dS^T.
-//          Delta is not taken as dO . O: O arrives rounded to bf16, and that
-//          rounding (2^-9 |O|) lands undamped on rows whose attention sits on a
-//          few keys. K^T sits in LDS under the accumulator's key permutation,
-//          as V^T does in the forward.
+//                  Delta_i = sum_j P_ij dP_ij exactly (fp32; written for dkdv)
+//                  and, against the estimate D_i = dO_i . O_i from the bf16 O,
+//                  dS = P (dP - D), dQ^T += K^T dS^T, M_i = sum_j P_ij |dP_ij - D_i|.
+//          The estimate's error e_i = Delta_i - D_i moves dQ_i by
+//          -scale e_i sum_j P_ij K_j, at most |e_i| max_j |K_j| elementwise;
+//          rounding every dS term to bf16 once (unit roundoff 2^-8) may move
+//          it by up to 2^-8 M_i max_j |K_j|. A wave whose rows all have
+//          |e_i| <= 2^-8 M_i keeps pass 1. The others -- attention sitting on
+//          a few keys, where O's rounding lands undamped on dS, or no O
+//          given -- recompute dQ in pass 2 with the exact Delta (the
+//          workgroup walks its tiles again; waves that kept pass 1 only load):
+//          dS = P (dP - Delta), dQ^T += K^T dS^T.
+//          K^T sits in LDS under the accumulator's key permutation, as V^T
+//          does in the forward.
 //   dkdv   key-major over the active chunks only (history is detached): the
 //          dq workgroup of block a also lists the later blocks whose ids chose
 //          chunk a (the dkdv plan); the list's (block, query head) tiles, own
@@ -37,6 +46,8 @@
 // permutes in a lane order whose 8-byte writes fall on distinct banks.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
+#include <vector>
 
 #include "hga_internal.h"
 
@@ -53,6 +64,11 @@ constexpr int kMaxBlocksDkdv = 1024;        // query blocks a dkdv workgroup can
 // damped by the weight: tiles holding one feed P and dS to the MFMAs as a bf16
 // pair hi + lo (hi = bf16(x), lo = bf16(x - hi)), keeping them to ~2^-17.
 constexpr float kPairAbove = 1.0f / 16.0f;
+// The dq kernel keeps its one-pass dQ for a row when the Delta estimate from
+// the bf16 O is off by at most this fraction of sum_j P_ij |dP_ij - D_i|:
+// bf16's unit roundoff, so the estimate moves dQ by no more than the
+// worst-case bound of rounding every dS term to bf16 once.
+constexpr float kDeltaEstTol = 1.0f / 256.0f;
 
 __device__ __forceinline__ int t_pos(int kk) {   // swap bits 2 and 3
     return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
@@ -242,9 +258,11 @@ __device__ __forceinline__ void dq_store_v_grp(const DqRegs &r, uint16_t *Vs)
 // SIMD: wave w computes head g*G + hg*HW + w%4 for queries 32*(w/4) .. +32,
 // with Q^T and dO^T in registers as MFMA B operands, in the transposed form
 // S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (each query's state in one
-// lane pair). Steps walk the tile list twice (pass 1, then pass 2); tiles are
-// loaded two steps ahead into registers and written to double-buffered LDS
-// one barrier before use. Each 64-key tile is processed as two 32-key halves.
+// lane pair). Steps walk the tile list once, or twice when pass 2 is needed
+// (a workgroup-wide vote after pass 1); tiles are loaded two steps ahead into
+// registers and written to double-buffered LDS one barrier before use. Each
+// 64-key tile is processed as two 32-key halves. O (bf16, may be NULL) only
+// feeds the Delta estimate of pass 1; without it pass 1 forms Delta alone.
 // kUnit = kC: ids are chunk ids. kUnit = kGroup: ids are 8-token group ids;
 // each routed tile is gathered from 8 groups, and a last routed tile with
 // fewer masks its missing groups' keys.
@@ -253,9 +271,10 @@ __global__ __launch_bounds__(kDqThreads, 1) __attribute__((amdgpu_waves_per_eu(2
 void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO,
+    const uint16_t *__restrict__ O,
     const float *__restrict__ lse, float *__restrict__ delta, int *__restrict__ counters,
     int *__restrict__ next_item, int *__restrict__ plan_n, uint16_t *__restrict__ plan_blk,
-    uint8_t *__restrict__ plan_msk,
+    uint8_t *__restrict__ plan_msk, uint8_t *__restrict__ redo_flags,
     int64_t n_q, int kv_div, int64_t T_cap, int64_t p0,
     const int32_t *__restrict__ ids, int k, int sink, float scale_log2, float scale,
     float *__restrict__ dQ)
@@ -267,6 +286,9 @@ void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t Kts[2][kTTile];
     __shared__ int list[(kUnit == kC ? kChunkListMax : kGroupListMax) + 1];
     __shared__ int list_n;
+    __shared__ int redo[kDqThreads / 64];       // pass 2 votes, by wave
+    __shared__ float dl_s[kDqThreads];          // Delta_i partial sums, one slot a thread
+    __shared__ float mabs_s[kDqThreads];        // M_i partial sums, one slot a thread
     __shared__ uint8_t rmask[kMaxBlocksDkdv];   // the dkdv plan's scan, by block
 
     const int tid = threadIdx.x;
@@ -295,17 +317,23 @@ void bwd_dq_kernel(
     const int col = lane & 31;
     const int half = lane >> 5;
     const int64_t qrow = h * n_q + b * kC + 32 * qt + col;
-    bf16x8 qf[8], df[8];
-    float lse2 = 0.f, dl = 0.f;
-    // Q^T and dO^T (MFMA operands for the whole kernel) go out first, ahead
-    // of the list barrier: the plan-scan waves issue theirs after their scan
-    // loads, wave 0 after its id row (loads complete in order).
+    bf16x8 qf[8], df[8], of[8];
+    float lse2 = 0.f;
+    const bool fast = O != nullptr;
+    // Q^T and dO^T (MFMA operands for the whole kernel) and the O row go out
+    // first, ahead of the list barrier: the plan-scan waves issue theirs after
+    // their scan loads, wave 0 after its id row (loads complete in order).
     auto load_qdo = [&]() __attribute__((always_inline)) {
         if (!computes) return;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             qf[ks] = *(const bf16x8 *)(Q + qrow * kD + 16 * ks + 8 * half);
             df[ks] = *(const bf16x8 *)(dO + qrow * kD + 16 * ks + 8 * half);
+        }
+        if (fast) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                of[ks] = *(const bf16x8 *)(O + qrow * kD + 16 * ks + 8 * half);
         }
         lse2 = lse[qrow] * 1.44269504088896340736f;
     };
@@ -326,6 +354,9 @@ void bwd_dq_kernel(
     } else if (!(hg == 0 && wave >= 4)) {
         load_qdo();
     }
+    if (lane == 0) redo[wave] = fast ? 0 : 1;
+    dl_s[tid] = 0.f;
+    mabs_s[tid] = 0.f;
     // the dkdv kernel that follows counts finished workgroups per (unit, chunk)
     if (hg == 0 && tid == 0) counters[g * n_blocks + b] = 0;
     if (g == 0 && b == 0 && hg == 0 && tid == 0) *next_item = 0;
@@ -384,6 +415,17 @@ void bwd_dq_kernel(
         plan_store(rmask, b, n_blocks, plan_n + pr, plan_blk + pr * n_blocks,
                    plan_msk + pr * n_blocks);
     }
+    // the Delta estimate D_i = dO_i . O_i (this lane's 64 dims, then its
+    // partner's), subtracted from dP in pass 1
+    float dsub = 0.f;
+    if (fast && computes) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dsub = fmaf((float)df[ks][e], (float)of[ks][e], dsub);
+        dsub += partner32(dsub);
+    }
 
     // S^T and dP^T of one 32-key half kt of the tile in buffer buf, P in place
     // of S^T. Masks: key 32*kt + 8*(j/4) + 4*half + j%4 is dropped when
@@ -431,69 +473,114 @@ void bwd_dq_kernel(
         __syncthreads();
     };
 
-    // pass 1: Delta_i = sum_j P_ij dP_ij
-    auto pass1 = [&](int buf, int mode) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x16 s, dp;
-            sdp(buf, kt, mode, s, dp);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) dl = fmaf(s[j], dp[j], dl);
-        }
-    };
-    for (int st = 0; st < n_pass; st += 2) {
-        step(st, r0, r1, pass1);
-        step(st + 1, r1, r0, pass1);
-    }
-    // Delta complete: join the two half-waves' key subsets, publish for dkdv
-    dl += partner32(dl);
-    if (computes && half == 0) delta[qrow] = dl;
-
-    // pass 2: dS = P (dP - Delta); dQ^T += K^T dS^T. dS enters the MFMAs as
-    // bf16 hi; halves holding a probability above kPairAbove add the rounding
+    // dQ^T += K^T dS^T with dS = P (dP - dsub): dS enters the MFMAs as bf16
+    // hi; halves holding a probability above kPairAbove add the rounding
     // remainder lo = bf16(dS - hi) in a second round (wave-uniform branch).
+    // Pass 1 (kFirst) also sums Delta_i = sum_j P_ij dP_ij and
+    // M_i = sum_j P_ij |dP_ij - dsub|; without O it forms Delta only.
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
-    auto pass2 = [&](int buf, int mode) __attribute__((always_inline)) {
+    // (the partial sums of Delta_i and M_i wait in LDS, one slot a thread,
+    // updated once a half: two more loop-carried registers made the register
+    // allocator spill, and LDS float atomics for the update took the whole
+    // pass from ~2.6 to ~4.7 us a tile)
+    auto pass = [&](int buf, int mode, auto first) __attribute__((always_inline)) {
+        constexpr bool kFirst = decltype(first)::value;
         const uint16_t *Ktb = Kts[buf];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x16 s, dp;
             sdp(buf, kt, mode, s, dp);
-            bf16x8 dsh[2];
             bool big = false;
 #pragma unroll
+            for (int j = 0; j < 16; ++j) big |= s[j] > kPairAbove;
+            const bool pair = __ballot(big) != 0;
+            if constexpr (kFirst) {
+                float d = 0.f, m = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    d = fmaf(s[j], dp[j], d);
+                    m = fmaf(s[j], fabsf(dp[j] - dsub), m);
+                }
+                dl_s[tid] += d;
+                mabs_s[tid] += m;
+                if (!fast) continue;
+            }
+            bf16x8 dsh[2];
+#pragma unroll
             for (int j = 0; j < 16; ++j) {
-                big |= s[j] > kPairAbove;
-                dp[j] = s[j] * (dp[j] - dl);
+                dp[j] = s[j] * (dp[j] - dsub);
                 dsh[j >> 3][j & 7] = (__bf16)dp[j];
             }
+            // K^T operands (dQ^T tile i&3, key step i>>2) read two MFMAs ahead,
+            // the order pinned by scheduling barriers (left free, the compiler
+            // placed each read behind the MFMA before it and waited on it)
+            auto kt_rd = [&](int i) __attribute__((always_inline)) {
+                return *(const bf16x8 *)(Ktb + (32 * (i & 3) + col) * kTStride +
+                                         16 * (2 * kt + (i >> 2)) + 8 * half);
+            };
+            auto dq_mfmas = [&](const bf16x8 (&ds)[2]) __attribute__((always_inline)) {
+                bf16x8 a[3];
+                a[0] = kt_rd(0);
+                a[1] = kt_rd(1);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)(Ktb + (32 * dt + col) * kTStride + 16 * (2 * kt + kk) + 8 * half);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsh[kk], acc[dt], 0, 0, 0);
+                for (int i = 0; i < 8; ++i) {
+                    if (i + 2 < 8) a[(i + 2) % 3] = kt_rd(i + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % 3], ds[i >> 2], acc[i & 3], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            if (__ballot(big) != 0) {
+            };
+            dq_mfmas(dsh);
+            if (pair) {
                 bf16x8 dsl[2];
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     dsl[j >> 3][j & 7] = (__bf16)(dp[j] - (float)dsh[j >> 3][j & 7]);
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const bf16x8 a = *(const bf16x8 *)(Ktb + (32 * dt + col) * kTStride + 16 * (2 * kt + kk) + 8 * half);
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsl[kk], acc[dt], 0, 0, 0);
-                    }
+                dq_mfmas(dsl);
             }
         }
     };
-    for (int st = n_pass; st < n_steps; st += 2) {
-        step(st, r0, r1, pass2);
-        step(st + 1, r1, r0, pass2);
+    auto pass1 = [&](int buf, int mode) __attribute__((always_inline)) {
+        pass(buf, mode, std::true_type{});
+    };
+    auto pass2 = [&](int buf, int mode) __attribute__((always_inline)) {
+        pass(buf, mode, std::false_type{});
+    };
+    for (int st = 0; st < n_pass; st += 2) {
+        step(st, r0, r1, pass1);
+        step(st + 1, r1, r0, pass1);
+    }
+    // Delta complete: join the two half-waves' key subsets, publish for dkdv;
+    // a row whose estimate missed by more than kDeltaEstTol M_i (or is not
+    // finite) sends its wave through pass 2
+    float dl = dl_s[tid];
+    dl += partner32(dl);
+    float mabs = mabs_s[tid];
+    mabs += partner32(mabs);
+    if (computes && half == 0) delta[qrow] = dl;
+    if (__ballot(computes && !(fabsf(dl - dsub) <= kDeltaEstTol * mabs)) != 0 && lane == 0)
+        redo[wave] = 1;
+    __syncthreads();
+    const bool my_redo = redo[wave] != 0;
+    int any_redo = 0;
+#pragma unroll
+    for (int w = 0; w < kDqThreads / 64; ++w) any_redo |= redo[w];
+    if (tid == 0) redo_flags[(g * NHG + hg) * n_blocks + b] = (uint8_t)(any_redo != 0);
+    if (any_redo) {
+        if (my_redo) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+            dsub = dl;
+        }
+        auto pass2w = [&](int buf, int mode) __attribute__((always_inline)) {
+            if (my_redo) pass2(buf, mode);
+        };
+        for (int st = n_pass; st < n_steps; st += 2) {
+            step(st, r0, r1, pass2w);
+            step(st + 1, r1, r0, pass2w);
+        }
     }
 
     if (!computes) return;
@@ -1100,10 +1187,11 @@ int device_cus()
 template <int G, int kUnit>
 hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                         int64_t Hkv, int kv_div, int64_t T_cap, int64_t p0, int64_t n_q,
-                        const int32_t *ids, int32_t k, int32_t sink, float scale, const float *lse,
+                        const int32_t *ids, int32_t k, int32_t sink, float scale,
+                        const uint16_t *O, const float *lse,
                         const uint16_t *dO, float *dQ, float *dK, float *dV,
                         float *delta, int *counters, int *plan_n, uint16_t *plan_blk,
-                        uint8_t *plan_msk, float *part, hipStream_t stream)
+                        uint8_t *plan_msk, uint8_t *redo_flags, float *part, hipStream_t stream)
 {
     int *next_item = counters + Hkv * kv_div * (n_q / kC);
     constexpr int NHG = G < 4 ? 1 : G / 4;
@@ -1113,8 +1201,9 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     hipLaunchKernelGGL((bwd_dq_kernel<G, kUnit>),
                        dim3((unsigned)Hkv, (unsigned)(kv_div * NHG), (unsigned)n_blocks),
                        dim3(kDqThreads), 0,
-                       stream, Q, K, V, dO, lse, delta, counters, next_item, plan_n, plan_blk,
-                       plan_msk, n_q, kv_div, T_cap, p0, ids, k, (int)sink, scale_log2, scale, dQ);
+                       stream, Q, K, V, dO, O, lse, delta, counters, next_item, plan_n,
+                       plan_blk, plan_msk, redo_flags, n_q, kv_div, T_cap, p0, ids, k, (int)sink,
+                       scale_log2, scale, dQ);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_items = Hkv * kv_div * n_blocks * kSplit;
@@ -1129,12 +1218,13 @@ hipError_t launch_bwd_g(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
 // nb = n_q/C blocks): Delta [Hq][n_q] f32 | counters [U][nb] int32 and the
 // dkdv work-queue counter | the dkdv
 // plan: plan_n [U][nb] int32, plan_blk [U][nb][nb] uint16, plan_msk
-// [U][nb][nb] uint8 | partial sums [kSplit - 1][dK, dV][U][n_q][D] f32 |
+// [U][nb][nb] uint8 | the dq workgroups' pass-2 flags [U][2][nb] uint8 (two
+// workgroups per unit when G = 8) | partial sums [kSplit - 1][dK, dV][U][n_q][D] f32 |
 // per-query-head routing only: each head's dK and dV, [2][Hq][n_q][D] f32.
 // Every part starts on a 256-byte boundary.
 struct BwdWorkspace {
-    size_t delta_off, counter_off, plan_n_off, plan_blk_off, plan_msk_off, part_off, head_off,
-        total;
+    size_t delta_off, counter_off, plan_n_off, plan_blk_off, plan_msk_off, redo_off, part_off,
+        head_off, total;
 };
 
 BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
@@ -1148,7 +1238,8 @@ BwdWorkspace bwd_layout(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head)
     w.plan_n_off = w.counter_off + up(((size_t)U * nb + 1) * sizeof(int));
     w.plan_blk_off = w.plan_n_off + up((size_t)U * nb * sizeof(int));
     w.plan_msk_off = w.plan_blk_off + up((size_t)U * nb * nb * sizeof(uint16_t));
-    w.part_off = w.plan_msk_off + up((size_t)U * nb * nb);
+    w.redo_off = w.plan_msk_off + up((size_t)U * nb * nb);
+    w.part_off = w.redo_off + up((size_t)U * 2 * nb);
     w.head_off = w.part_off + (size_t)(kSplit - 1) * 2 * (size_t)(U * n_q * kD) * sizeof(float);
     w.total = w.head_off + (per_q_head ? 2 * (size_t)(Hq * n_q * kD) * sizeof(float) : 0);
     return w;
@@ -1163,14 +1254,38 @@ size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head
 
 int64_t bwd_max_queries() { return (int64_t)kMaxBlocksDkdv * kC; }
 
+hipError_t bwd_second_pass_count(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head,
+                                 const void *workspace, int64_t *n_second, int64_t *n_wg,
+                                 hipStream_t stream)
+{
+    const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q, per_q_head);
+    const int64_t U = per_q_head ? Hq : Hkv;
+    const int64_t G = per_q_head ? 1 : Hq / Hkv;
+    const int64_t nhg = G < 4 ? 1 : G / 4;
+    const int64_t n = U * nhg * (n_q / kC);
+    std::vector<uint8_t> h((size_t)std::max<int64_t>(n, 1));
+    if (n > 0) {
+        hipError_t e = hipMemcpyAsync(h.data(), (const uint8_t *)workspace + w.redo_off,
+                                      (size_t)n, hipMemcpyDeviceToHost, stream);
+        if (e != hipSuccess) return e;
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return e;
+    }
+    int64_t c = 0;
+    for (int64_t i = 0; i < n; ++i) c += h[(size_t)i] != 0;
+    *n_second = c;
+    *n_wg = n;
+    return hipSuccess;
+}
+
 namespace {
 
 template <int kUnit>
 hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                            int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0, int64_t n_q,
                            const int32_t *ids, int32_t k, int32_t sink, bool per_q_head,
-                           float scale, const float *lse, const uint16_t *dO, float *dQ,
-                           float *dK, float *dV, void *workspace, hipStream_t stream)
+                           float scale, const uint16_t *O, const float *lse, const uint16_t *dO,
+                           float *dQ, float *dK, float *dV, void *workspace, hipStream_t stream)
 {
     if (n_q == 0) return hipSuccess;
     const BwdWorkspace w = bwd_layout(Hq, Hkv, n_q, per_q_head);
@@ -1180,14 +1295,15 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
     int *plan_n = (int *)(ws + w.plan_n_off);
     uint16_t *plan_blk = (uint16_t *)(ws + w.plan_blk_off);
     uint8_t *plan_msk = ws + w.plan_msk_off;
+    uint8_t *redo = ws + w.redo_off;
     float *part = (float *)(ws + w.part_off);
     const int G = (int)(Hq / Hkv);
     if (per_q_head) {
         float *dKu = (float *)(ws + w.head_off);
         float *dVu = dKu + Hq * n_q * kD;
         hipError_t e = launch_bwd_g<1, kUnit>(Q, K, V, Hkv, G, T_cap, p0, n_q, ids, k, sink,
-                                              scale, lse, dO, dQ, dKu, dVu, delta, counters,
-                                              plan_n, plan_blk, plan_msk, part, stream);
+                                              scale, O, lse, dO, dQ, dKu, dVu, delta, counters,
+                                              plan_n, plan_blk, plan_msk, redo, part, stream);
         if (e != hipSuccess) return e;
         const int64_t per_head = n_q * kD / 4, n_vec = Hkv * per_head;
         hipLaunchKernelGGL(sum_heads_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256),
@@ -1195,10 +1311,10 @@ hipError_t launch_bwd_unit(const uint16_t *Q, const uint16_t *K, const uint16_t 
         return hipGetLastError();
     }
     switch (G) {
-    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
-    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
-    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
-    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, part, stream);
+    case 1: return launch_bwd_g<1, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, O, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, redo, part, stream);
+    case 2: return launch_bwd_g<2, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, O, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, redo, part, stream);
+    case 4: return launch_bwd_g<4, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, O, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, redo, part, stream);
+    case 8: return launch_bwd_g<8, kUnit>(Q, K, V, Hkv, 1, T_cap, p0, n_q, ids, k, sink, scale, O, lse, dO, dQ, dK, dV, delta, counters, plan_n, plan_blk, plan_msk, redo, part, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1212,19 +1328,19 @@ hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K, const uint16_
                              const uint16_t *dO, float *dQ, float *dK, float *dV,
                              void *workspace, hipStream_t stream)
 {
-    (void)O;    // Delta is recomputed from P and dP (see the dq kernel)
     return launch_bwd_unit<kC>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, ids, k, sink, per_q_head,
-                               scale, lse, dO, dQ, dK, dV, workspace, stream);
+                               scale, O, lse, dO, dQ, dK, dV, workspace, stream);
 }
 
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                     int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                     int64_t n_q, const int32_t *gids, int32_t m, int32_t sink,
-                                    float scale, const float *lse, const uint16_t *dO, float *dQ,
-                                    float *dK, float *dV, void *workspace, hipStream_t stream)
+                                    float scale, const uint16_t *O, const float *lse,
+                                    const uint16_t *dO, float *dQ, float *dK, float *dV,
+                                    void *workspace, hipStream_t stream)
 {
     return launch_bwd_unit<kGroup>(Q, K, V, Hq, Hkv, T_cap, p0, n_q, gids, m, sink, false,
-                                   scale, lse, dO, dQ, dK, dV, workspace, stream);
+                                   scale, O, lse, dO, dQ, dK, dV, workspace, stream);
 }
 
 }  // namespace hga

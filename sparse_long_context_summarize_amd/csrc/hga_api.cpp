@@ -555,7 +555,7 @@ hga_status hga_attend_bwd_groups(const hga_config *cfg, const void *Q, const voi
                                                     (const uint16_t *)V, cfg->n_q_heads,
                                                     cfg->n_kv_heads, T_cap, p0, n_q, group_ids,
                                                     group_top_k, cfg->sink_chunks,
-                                                    effective_scale(cfg), lse,
+                                                    effective_scale(cfg), (const uint16_t *)O, lse,
                                                     (const uint16_t *)dO, dQ, dK_active,
                                                     dV_active, workspace, stream),
                       "hga_attend_bwd_groups launch");
@@ -726,6 +726,31 @@ hga_status hga_diag_gather(const hga_config *cfg, const void *K, const void *V, 
                                          cfg->n_kv_heads, T_cap, p0, n_q, ids, cfg->top_k,
                                          cfg->sink_chunks, sink, stream),
                       "hga_diag_gather launch");
+}
+
+hga_status hga_diag_bwd_second_pass(const hga_config *cfg, int64_t n_q, const void *workspace,
+                                    size_t ws_bytes, int64_t *n_second, int64_t *n_workgroups,
+                                    hipStream_t stream)
+{
+    g_last_error[0] = '\0';
+    hga_status st = check_config(cfg);
+    if (st != HGA_OK) return st;
+    if (n_q < 0 || n_q % hga::kC != 0)
+        return fail(HGA_ERR_INVALID_ARG, "n_q = %lld is not a multiple of %d", (long long)n_q,
+                    hga::kC);
+    if (!n_second || !n_workgroups) return fail(HGA_ERR_INVALID_ARG, "a required pointer is NULL");
+    *n_second = 0;
+    *n_workgroups = 0;
+    if (n_q == 0) return HGA_OK;
+    if (!workspace) return fail(HGA_ERR_INVALID_ARG, "workspace is NULL");
+    const size_t need = hga::bwd_workspace_bytes(cfg->n_q_heads, cfg->n_kv_heads, n_q,
+                                                 per_q_head(cfg));
+    if (ws_bytes < need)
+        return fail(HGA_ERR_CAPACITY, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
+    return hip_status(hga::bwd_second_pass_count(cfg->n_q_heads, cfg->n_kv_heads, n_q,
+                                                 per_q_head(cfg), workspace, n_second,
+                                                 n_workgroups, stream),
+                      "hga_diag_bwd_second_pass copy");
 }
 
 size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q)

@@ -212,13 +212,19 @@ size_t gather_sink_words(int64_t Hkv, int64_t n_q);
 hipError_t launch_attend_bwd_groups(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                     int64_t Hq, int64_t Hkv, int64_t T_cap, int64_t p0,
                                     int64_t n_q, const int32_t *gids, int32_t m, int32_t sink,
-                                    float scale, const float *lse, const uint16_t *dO, float *dQ,
-                                    float *dK, float *dV, void *workspace, hipStream_t stream);
+                                    float scale, const uint16_t *O, const float *lse,
+                                    const uint16_t *dO, float *dQ, float *dK, float *dV,
+                                    void *workspace, hipStream_t stream);
 
 size_t bwd_workspace_bytes(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head);
 
 // Largest active segment (queries) the backward's key-major pass can list.
 int64_t bwd_max_queries();
+// The dq workgroups' pass-2 flags left in a backward workspace: how many of
+// the n_wg workgroups of the last call on it ran the second pass (host wait).
+hipError_t bwd_second_pass_count(int64_t Hq, int64_t Hkv, int64_t n_q, bool per_q_head,
+                                 const void *workspace, int64_t *n_second, int64_t *n_wg,
+                                 hipStream_t stream);
 
 hipError_t launch_attend_bwd(const uint16_t *Q, const uint16_t *K,
                              const uint16_t *V, int64_t Hq, int64_t Hkv,

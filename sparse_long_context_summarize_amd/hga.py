@@ -29,7 +29,7 @@ EXPORTED = ("hga_summarize", "hga_route", "hga_route_causal", "hga_attend_fwd",
             "hga_attend_bwd_groups", "hga_route_decode", "hga_decode_workspace_bytes",
             "hga_attend_decode", "hga_route_attend_decode_workspace_bytes",
             "hga_route_attend_decode", "hga_diag_gather_sink_words", "hga_diag_gather",
-            "hga_status_string", "hga_last_error", "hga_version")
+            "hga_diag_bwd_second_pass", "hga_status_string", "hga_last_error", "hga_version")
 HGA_GROUP = 8
 HGA_MAX_SINK_CHUNKS = 64
 HGA_ROUTE_PER_KV_HEAD = 0
@@ -111,6 +111,10 @@ def lib() -> ctypes.CDLL:
     L.hga_diag_gather_sink_words.restype = ctypes.c_size_t
     L.hga_diag_gather.argtypes = [_cfgp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, ctypes.c_size_t,
                                   _vp]
+    L.hga_diag_bwd_second_pass.argtypes = [_cfgp, _i64, _vp, ctypes.c_size_t,
+                                           ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.POINTER(ctypes.c_int64), _vp]
+    L.hga_diag_bwd_second_pass.restype = ctypes.c_int
     L.hga_attend_bwd_groups.argtypes = [_cfgp, _vp, _vp, _vp, _i64, _i64, _i64, _vp,
                                         ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         ctypes.c_size_t, _vp]
@@ -628,6 +632,21 @@ def hga_diag_gather(cfg: hga_config, K: torch.Tensor, V: torch.Tensor, p0: int, 
     int32 scratch of hga_diag_gather_sink_words words)."""
     _check("hga_diag_gather", lib().hga_diag_gather(
         *_m_diag_gather(cfg, K, V, p0, n_q, ids, sink, stream)))
+
+
+def hga_diag_bwd_second_pass(cfg: hga_config, n_q: int, workspace: torch.Tensor,
+                             stream=None) -> tuple[int, int]:
+    """Diagnostic: (dq workgroups that ran the second pass, dq workgroups) of
+    the last backward call on `workspace`; waits for the stream."""
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous GPU memory")
+    n2, nw = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("hga_diag_bwd_second_pass", lib().hga_diag_bwd_second_pass(
+        ctypes.byref(cfg), n_q, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), ctypes.byref(n2), ctypes.byref(nw),
+        _stream(stream)))
+    return int(n2.value), int(nw.value)
 
 
 def prepare(name: str, *args, **kwargs):

@@ -123,6 +123,24 @@ def test_route_checks():
              None) == hga.HGA_OK
 
 
+def test_bwd_second_pass_diag_checks():
+    L = hga.lib()
+    cfg = _cfg()
+    need = hga.hga_attend_bwd_workspace_bytes(cfg, 2048)
+    n2, nw = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    d = L.hga_diag_bwd_second_pass
+    assert d(ctypes.byref(cfg), 2047, FAKE, need, ctypes.byref(n2), ctypes.byref(nw),
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert d(ctypes.byref(cfg), 2048, FAKE, need - 1, ctypes.byref(n2), ctypes.byref(nw),
+             None) == hga.HGA_ERR_CAPACITY
+    assert d(ctypes.byref(cfg), 2048, None, need, ctypes.byref(n2), ctypes.byref(nw),
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert d(ctypes.byref(cfg), 2048, FAKE, need, None, ctypes.byref(nw),
+             None) == hga.HGA_ERR_INVALID_ARG
+    assert d(ctypes.byref(cfg), 0, None, 0, ctypes.byref(n2), ctypes.byref(nw), None) == hga.HGA_OK
+    assert (n2.value, nw.value) == (0, 0)
+
+
 def test_bwd_checks():
     L = hga.lib()
     cfg = _cfg()
@@ -349,8 +367,9 @@ def test_routing_variant_checks():
     delta = up(32 * n_q * 4)
     nb = n_q // 64
 
-    def plan(U):               # per (unit, chunk): list length, block ids, group masks
-        return up(U * nb * 4) + up(U * nb * nb * 2) + up(U * nb * nb)
+    def plan(U):               # per (unit, chunk): list length, block ids, group masks,
+        # and the dq workgroups' second-pass flags (two workgroups per unit at G = 8)
+        return up(U * nb * 4) + up(U * nb * nb * 2) + up(U * nb * nb) + up(U * 2 * nb)
 
     slots = 7                  # workgroups past the first that may share one active chunk
     assert a == delta + up((8 * nb + 1) * 4) + plan(8) + slots * 2 * 8 * n_q * 128 * 4

@@ -165,3 +165,71 @@ def test_repeated_and_unsorted_ids_count_once():
     ids[0, 3] = np.arange(k) % 15
     res = gpu_fwd_bwd(x, p0, k, ids_override=ids)
     check_grads(x, p0, res, "repeated ids")
+
+
+def _bwd_again(d, n_q, O):
+    """hga_attend_bwd on the device tensors of gpu_fwd_bwd with another O;
+    returns the gradients and the dq workgroups that took the second pass."""
+    cfg = d["cfg"]
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    dQ = torch.full((Hq, n_q, D), float("nan"), device="cuda")
+    dK = torch.full((Hkv, n_q, D), float("nan"), device="cuda")
+    dV = torch.full((Hkv, n_q, D), float("nan"), device="cuda")
+    d["ws"].fill_(255)
+    hga.hga_attend_bwd(cfg, d["Q"], d["K"], d["V"], d["p0"], d["ids"], O, d["lse"], d["dO"],
+                       dQ, dK, dV, d["ws"])
+    second = hga.hga_diag_bwd_second_pass(cfg, n_q, d["ws"])
+    return dict(ids=d["ids"].cpu().numpy(), dQ=from_dev(dQ), dK=from_dev(dK),
+                dV=from_dev(dV)), second
+
+
+def test_bwd16k_one_pass():
+    # Attention at the 16K workload is spread over ~1100 keys a row, so the
+    # Delta estimate from the forward's O is close enough almost everywhere:
+    # nearly every dq workgroup keeps its first pass. Without O every
+    # workgroup takes the second pass; both give the oracle's gradients.
+    w = inputs.BWD16K
+    x = inputs.generate(w)
+    res = gpu_fwd_bwd(x, w.p0, w.k)
+    d = dict(res["dev"], p0=w.p0)
+    again, (n2, nw) = _bwd_again(d, w.n_q, d["O"])
+    log(f"bwd16k with O: {n2} of {nw} dq workgroups took the second pass")
+    assert nw == w.Hkv * w.n_blocks and n2 <= nw // 32
+    np.testing.assert_array_equal(again["dQ"], res["dQ"])
+    none, (n2, nw) = _bwd_again(d, w.n_q, None)
+    log(f"bwd16k without O: {n2} of {nw} dq workgroups took the second pass")
+    assert n2 == nw
+    check_grads(x, w.p0, none, "bwd16k without O")
+
+
+@pytest.mark.parametrize("O_kind", ["zeros", "noise"])
+def test_any_O_gives_the_gradients(O_kind):
+    # O only feeds the estimate: a wrong one sends the workgroups through the
+    # second pass, never into the gradients.
+    T, n_q = 1024, 256
+    x = inputs.small_random(35, 8, 2, 128, T, n_q, bf16=True, with_dO=True)
+    res = gpu_fwd_bwd(x, T - n_q, 3)
+    d = dict(res["dev"], p0=T - n_q)
+    O = torch.zeros_like(d["O"]) if O_kind == "zeros" else \
+        torch.randn(d["O"].shape, generator=torch.Generator().manual_seed(7)).to(
+            torch.bfloat16).cuda()
+    got, (n2, nw) = _bwd_again(d, n_q, O)
+    log(f"O = {O_kind}: {n2} of {nw} dq workgroups took the second pass")
+    assert n2 == nw
+    check_grads(x, T - n_q, got, f"O = {O_kind}")
+
+
+def test_peaked_rows_take_the_second_pass():
+    # Query rows scaled by 16 put most of each row's attention on one or two
+    # keys: O's bf16 rounding would reach dS undamped there, so those
+    # workgroups recompute dQ with the exact Delta. The first segment (p0 = 0)
+    # adds rows that see a single key.
+    T = n_q = 1024
+    x = inputs.small_random(36, 4, 1, 128, T, n_q, bf16=True, with_dO=True)
+    x["Q"] = x["Q"] * 16.0
+    res = gpu_fwd_bwd(x, 0, 5)
+    d = dict(res["dev"], p0=0)
+    n2, nw = hga.hga_diag_bwd_second_pass(d["cfg"], n_q, d["ws"])
+    log(f"peaked rows: {n2} of {nw} dq workgroups took the second pass")
+    assert n2 > 0
+    check_grads(x, 0, res, "peaked rows")
