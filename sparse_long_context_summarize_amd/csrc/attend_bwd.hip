@@ -450,12 +450,15 @@ void bwd_dq_kernel(
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        const int thr = mode == 1 ? 32 * (qt - kt) + col - 4 * half
-                      : mode == 2 ? pad_keys - 32 * kt - 4 * half - 1 : 1 << 20;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -lse2));
-            s[j] = (8 * (j >> 2) + (j & 3) > thr) ? 0.f : p;
+        for (int j = 0; j < 16; ++j)
+            s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], scale_log2, -lse2));
+        if (mode != 0) {             // (wave-uniform: one tile in 17 at the 16K layer)
+            const int thr = mode == 1 ? 32 * (qt - kt) + col - 4 * half
+                                      : pad_keys - 32 * kt - 4 * half - 1;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (8 * (j >> 2) + (j & 3) > thr) s[j] = 0.f;
         }
     };
 
@@ -476,8 +479,10 @@ void bwd_dq_kernel(
     // dQ^T += K^T dS^T with dS = P (dP - dsub): dS enters the MFMAs as bf16
     // hi; halves holding a probability above kPairAbove add the rounding
     // remainder lo = bf16(dS - hi) in a second round (wave-uniform branch).
-    // Pass 1 (kFirst) also sums Delta_i = sum_j P_ij dP_ij and
-    // M_i = sum_j P_ij |dP_ij - dsub|; without O it forms Delta only.
+    // Pass 1 (kFirst) also sums sum_j dS_ij = Delta_i - dsub (the row's
+    // probabilities sum to 1; up to fp32 rounding, Delta_i = sum_j P_ij dP_ij)
+    // and M_i = sum_j |dS_ij| = sum_j P_ij |dP_ij - dsub|; without O (dsub = 0)
+    // it forms Delta only.
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
@@ -492,26 +497,27 @@ void bwd_dq_kernel(
         for (int kt = 0; kt < 2; ++kt) {
             f32x16 s, dp;
             sdp(buf, kt, mode, s, dp);
-            bool big = false;
+            float pm = s[0];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) big |= s[j] > kPairAbove;
-            const bool pair = __ballot(big) != 0;
-            if constexpr (kFirst) {
-                float d = 0.f, m = 0.f;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    d = fmaf(s[j], dp[j], d);
-                    m = fmaf(s[j], fabsf(dp[j] - dsub), m);
-                }
-                dl_s[tid] += d;
-                mabs_s[tid] += m;
-                if (!fast) continue;
-            }
+            for (int j = 1; j < 16; ++j) pm = fmaxf(pm, s[j]);
+            const bool pair = __ballot(pm > kPairAbove) != 0;
             bf16x8 dsh[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 dp[j] = s[j] * (dp[j] - dsub);
                 dsh[j >> 3][j & 7] = (__bf16)dp[j];
+            }
+            if constexpr (kFirst) {
+                // sum_j dS_ij = Delta_i - dsub (the row's P sum to 1) and M_i
+                float d = 0.f, m = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    d += dp[j];
+                    m += fabsf(dp[j]);
+                }
+                dl_s[tid] += d;
+                mabs_s[tid] += m;
+                if (!fast) continue;
             }
             // K^T operands (dQ^T tile i&3, key step i>>2) read two MFMAs ahead,
             // the order pinned by scheduling barriers (left free, the compiler
@@ -555,12 +561,13 @@ void bwd_dq_kernel(
     // Delta complete: join the two half-waves' key subsets, publish for dkdv;
     // a row whose estimate missed by more than kDeltaEstTol M_i (or is not
     // finite) sends its wave through pass 2
-    float dl = dl_s[tid];
-    dl += partner32(dl);
+    float err = dl_s[tid];                       // Delta_i - dsub
+    err += partner32(err);
     float mabs = mabs_s[tid];
     mabs += partner32(mabs);
+    const float dl = dsub + err;
     if (computes && half == 0) delta[qrow] = dl;
-    if (__ballot(computes && !(fabsf(dl - dsub) <= kDeltaEstTol * mabs)) != 0 && lane == 0)
+    if (__ballot(computes && !(fabsf(err) <= kDeltaEstTol * mabs)) != 0 && lane == 0)
         redo[wave] = 1;
     __syncthreads();
     const bool my_redo = redo[wave] != 0;
