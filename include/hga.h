@@ -233,7 +233,8 @@ size_t hga_attend_bwd_workspace_bytes(const hga_config *cfg, int64_t n_q);
  * on a few keys, where O's bf16 rounding would reach dS undamped, and every
  * wave when O is NULL -- recompute dQ in a second pass with the exact Delta
  * (hga_diag_bwd_second_pass counts the workgroups that ran one). O is read only
- * for the estimate: any O gives gradients within that bound.
+ * for the estimate: any O, Inf or NaN included, gives gradients within that
+ * bound (an estimate that is not finite always takes the second pass).
  * Every element of dQ, dK and dV is written; the caller does not clear them.
  * Deterministic: no output is accumulated with atomics, every sum has a fixed
  * order (a per-chunk counter in the workspace only decides which workgroup

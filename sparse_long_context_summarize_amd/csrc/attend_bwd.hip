@@ -479,10 +479,9 @@ void bwd_dq_kernel(
     // dQ^T += K^T dS^T with dS = P (dP - dsub): dS enters the MFMAs as bf16
     // hi; halves holding a probability above kPairAbove add the rounding
     // remainder lo = bf16(dS - hi) in a second round (wave-uniform branch).
-    // Pass 1 (kFirst) also sums sum_j dS_ij = Delta_i - dsub (the row's
-    // probabilities sum to 1; up to fp32 rounding, Delta_i = sum_j P_ij dP_ij)
-    // and M_i = sum_j |dS_ij| = sum_j P_ij |dP_ij - dsub|; without O (dsub = 0)
-    // it forms Delta only.
+    // Pass 1 (kFirst) also sums Delta_i = sum_j P_ij dP_ij (exactly: it
+    // does not lean on the estimate) and M_i = sum_j |dS_ij| =
+    // sum_j P_ij |dP_ij - dsub|; without O it forms Delta only.
     f32x16 acc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
@@ -501,6 +500,11 @@ void bwd_dq_kernel(
 #pragma unroll
             for (int j = 1; j < 16; ++j) pm = fmaxf(pm, s[j]);
             const bool pair = __ballot(pm > kPairAbove) != 0;
+            float d = 0.f;
+            if constexpr (kFirst) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) d = fmaf(s[j], dp[j], d);
+            }
             bf16x8 dsh[2];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -508,13 +512,9 @@ void bwd_dq_kernel(
                 dsh[j >> 3][j & 7] = (__bf16)dp[j];
             }
             if constexpr (kFirst) {
-                // sum_j dS_ij = Delta_i - dsub (the row's P sum to 1) and M_i
-                float d = 0.f, m = 0.f;
+                float m = 0.f;                  // M_i: sum_j |dS_ij|
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    d += dp[j];
-                    m += fabsf(dp[j]);
-                }
+                for (int j = 0; j < 16; ++j) m += fabsf(dp[j]);
                 dl_s[tid] += d;
                 mabs_s[tid] += m;
                 if (!fast) continue;
@@ -561,14 +561,16 @@ void bwd_dq_kernel(
     // Delta complete: join the two half-waves' key subsets, publish for dkdv;
     // a row whose estimate missed by more than kDeltaEstTol M_i (or is not
     // finite) sends its wave through pass 2
-    float err = dl_s[tid];                       // Delta_i - dsub
-    err += partner32(err);
+    float dl = dl_s[tid];
+    dl += partner32(dl);
     float mabs = mabs_s[tid];
     mabs += partner32(mabs);
-    const float dl = dsub + err;
     if (computes && half == 0) delta[qrow] = dl;
-    if (__ballot(computes && !(fabsf(err) <= kDeltaEstTol * mabs)) != 0 && lane == 0)
-        redo[wave] = 1;
+    // (an estimate or M that is not finite -- O holding Inf or NaN -- never
+    // passes: inf <= inf would)
+    const bool keep = __builtin_isfinite(dsub) && __builtin_isfinite(mabs) &&
+                      fabsf(dl - dsub) <= kDeltaEstTol * mabs;
+    if (__ballot(computes && !keep) != 0 && lane == 0) redo[wave] = 1;
     __syncthreads();
     const bool my_redo = redo[wave] != 0;
     int any_redo = 0;

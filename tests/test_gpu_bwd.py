@@ -202,16 +202,20 @@ def test_bwd16k_one_pass():
     check_grads(x, w.p0, none, "bwd16k without O")
 
 
-@pytest.mark.parametrize("O_kind", ["zeros", "noise"])
+@pytest.mark.parametrize("O_kind", ["zeros", "noise", "inf", "nan", "huge"])
 def test_any_O_gives_the_gradients(O_kind):
-    # O only feeds the estimate: a wrong one sends the workgroups through the
-    # second pass, never into the gradients.
+    # O only feeds the estimate: a wrong one -- zero, noise, infinite, NaN or
+    # huge -- sends the workgroups through the second pass, never into the
+    # gradients (Delta, which dK/dV use, is summed from P and dP alone).
     T, n_q = 1024, 256
     x = inputs.small_random(35, 8, 2, 128, T, n_q, bf16=True, with_dO=True)
     res = gpu_fwd_bwd(x, T - n_q, 3)
     d = dict(res["dev"], p0=T - n_q)
-    O = torch.zeros_like(d["O"]) if O_kind == "zeros" else \
-        torch.randn(d["O"].shape, generator=torch.Generator().manual_seed(7)).to(
+    fill = {"zeros": 0.0, "inf": float("inf"), "nan": float("nan"), "huge": 3.0e38}
+    if O_kind in fill:
+        O = torch.full_like(d["O"], fill[O_kind])
+    else:
+        O = torch.randn(d["O"].shape, generator=torch.Generator().manual_seed(7)).to(
             torch.bfloat16).cuda()
     got, (n2, nw) = _bwd_again(d, n_q, O)
     log(f"O = {O_kind}: {n2} of {nw} dq workgroups took the second pass")
