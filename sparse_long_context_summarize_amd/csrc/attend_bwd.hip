@@ -258,8 +258,9 @@ __device__ __forceinline__ void dq_store_v_grp(const DqRegs &r, uint16_t *Vs)
 // SIMD: wave w computes head g*G + hg*HW + w%4 for queries 32*(w/4) .. +32,
 // with Q^T and dO^T in registers as MFMA B operands, in the transposed form
 // S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (each query's state in one
-// lane pair). Steps walk the tile list once, or twice when pass 2 is needed
-// (a workgroup-wide vote after pass 1); tiles are loaded two steps ahead into
+// lane pair). Steps walk the tile list once, or twice when a wave needs pass
+// 2 (a vote by wave after pass 1; only the waves that voted compute in the
+// second walk, the others load and wait at its barriers); tiles are loaded two steps ahead into
 // registers and written to double-buffered LDS one barrier before use. Each
 // 64-key tile is processed as two 32-key halves. O (bf16, may be NULL) only
 // feeds the Delta estimate of pass 1; without it pass 1 forms Delta alone.
