@@ -14,7 +14,7 @@
 //                  and, against the estimate D_i = dO_i . O_i from the bf16 O,
 //                  dS = P (dP - D), dQ^T += K^T dS^T, M_i = sum_j P_ij |dP_ij - D_i|.
 //          The estimate's error e_i = Delta_i - D_i moves dQ_i by
-//          -scale e_i sum_j P_ij K_j, at most |e_i| max_j |K_j| elementwise;
+//          +scale e_i sum_j P_ij K_j, at most |e_i| max_j |K_j| elementwise;
 //          rounding every dS term to bf16 once (unit roundoff 2^-8) may move
 //          it by up to 2^-8 M_i max_j |K_j|. A wave whose rows all have
 //          |e_i| <= 2^-8 M_i keeps pass 1. The others -- attention sitting on
