@@ -282,6 +282,11 @@ void bwd_dq_kernel(
 {
     constexpr int HW = G < 4 ? G : 4;
     constexpr int NHG = G / HW;
+    // One query head per workgroup (G = 1, or per-query-head routing): the
+    // two 32-key halves of each tile go to two waves on different SIMDs
+    // (four computing waves instead of two), whose dQ partials are added at
+    // the end.
+    constexpr int KSPLIT = HW == 1 ? 2 : 1;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kRowTile];
     __shared__ __attribute__((aligned(16))) uint16_t Kts[2][kTTile];
@@ -312,7 +317,10 @@ void bwd_dq_kernel(
     // different SIMDs)
     const int qt = wave >> 2;
     const int lane4 = wave & 3;
-    const bool computes = lane4 / HW == qt % (4 / HW);
+    // (KSPLIT = 2: waves 0, 2 take queries 0-31, waves 5, 7 queries 32-63,
+    // the key half kth = lane4 / 2 each)
+    const bool computes = KSPLIT == 2 ? (lane4 & 1) == qt : lane4 / HW == qt % (4 / HW);
+    const int kth = KSPLIT == 2 ? lane4 >> 1 : 0;
     const int hw = lane4 % HW;                   // head slot
     const int64_t h = g * G + hg * HW + hw;
     const int col = lane & 31;
@@ -495,7 +503,8 @@ void bwd_dq_kernel(
         constexpr bool kFirst = decltype(first)::value;
         const uint16_t *Ktb = Kts[buf];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kk = 0; kk < 2 / KSPLIT; ++kk) {
+            const int kt = KSPLIT == 2 ? kth : kk;
             f32x16 s, dp;
             sdp(buf, kt, mode, s, dp);
             float pm = s[0];
@@ -563,11 +572,18 @@ void bwd_dq_kernel(
     // Delta complete: join the two half-waves' key subsets, publish for dkdv;
     // a row whose estimate missed by more than kDeltaEstTol M_i (or is not
     // finite) sends its wave through pass 2
-    float dl = dl_s[tid];
+    float dl, mabs;
+    if constexpr (KSPLIT == 2) {     // the two key halves' waves: tid and tid ^ 128
+        const int t0 = tid & ~128;
+        dl = dl_s[t0] + dl_s[t0 | 128];
+        mabs = mabs_s[t0] + mabs_s[t0 | 128];
+    } else {
+        dl = dl_s[tid];
+        mabs = mabs_s[tid];
+    }
     dl += partner32(dl);
-    float mabs = mabs_s[tid];
     mabs += partner32(mabs);
-    if (computes && half == 0) delta[qrow] = dl;
+    if (computes && half == 0 && kth == 0) delta[qrow] = dl;
     // (an estimate or M that is not finite -- O holding Inf or NaN -- never
     // passes: inf <= inf would)
     const bool keep = __builtin_isfinite(dsub) && __builtin_isfinite(mabs) &&
@@ -594,7 +610,35 @@ void bwd_dq_kernel(
         }
     }
 
-    if (!computes) return;
+    if constexpr (KSPLIT == 2) {
+        // the key-half-1 waves hand their dQ partials to the key-half-0 waves
+        // through the K^T tiles (free after the last barrier), added in that order
+        float *xf = (float *)&Kts[0][0] + qt * (4 * 16 * 64);
+        static_assert(2 * 4 * 16 * 64 * sizeof(float) <= sizeof(Kts), "partials fit");
+        if (computes && kth == 1) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    f32x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[dt][4 * u + e];
+                    *(f32x4 *)(xf + ((dt * 4 + u) * 64 + lane) * 4) = v;
+                }
+        }
+        __syncthreads();
+        if (computes && kth == 0) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x4 v = *(const f32x4 *)(xf + ((dt * 4 + u) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[dt][4 * u + e] += v[e];
+                }
+        }
+    }
+    if (!computes || kth != 0) return;
     // dQ leaves through the wave's own LDS area (the tiles are free after the
     // last barrier; waves 0-3 use Ks, 4-7 Vs), half a row at a time, so that
     // every store instruction writes four whole 256-byte row halves, as
